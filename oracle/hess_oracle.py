@@ -1,0 +1,211 @@
+"""Plain float64 NumPy oracle for GPTQ/QQQ calibration-Hessian accumulation.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``; never by the library.
+
+What it computes, and where the pages define it
+-----------------------------------------------
+* Per-batch Gram accumulation ``S += X^T X`` with X laid out tokens x
+  features, and the token count ``N += n`` (GPTQModel PR 2979, "fix(qqq):
+  per-device Hessian partials ...", Summary and What Changed: the count is
+  of flattened token vectors, not batches; GPTQModel wiki "QQQ", Concepts >
+  Quadratic error compensation).  The pages write the same matrix as
+  ``X X^T`` for X laid out features x tokens.
+* In-place accumulation into one persistent buffer (GPTQModel PR 2981,
+  "fix(qqq): accumulate Hessian in-place per device", Changes).  Here the
+  buffer is float64 and exact to ~1e-16; the library keeps float32.
+* ``materialize``: scale the sum by 2 / total tokens (PR 2979, What Changed;
+  wiki "QQQ", Concepts), then the quantization pass's steps 2 and 3 (wiki
+  "QQQ", Concepts > Quadratic error compensation): neutralize dead input
+  columns, then add ``damp_percent * mean(diag(H))`` to the diagonal.  The
+  damping value returned is that absolute amount (wiki "QQQ", Implementation
+  internals > Quantizer API and results).
+* ``local_blocks``: per contiguous 16-feature block b, ``X_b^T X_b`` as a
+  batched product (NVIDIA Model-Optimizer PR 3002 page, "What does this PR
+  do?", the ``local_hessian`` bullet).
+* ``grouped_grams``: one independent (S_e, N_e) per routed expert over the
+  rows routed to it (Model-Optimizer PR 3002 page, "What does this PR do?":
+  the option applies to every GPTQ Hessian, fused MoE experts included).
+
+Readings where the pages leave a step open (each is also listed in the
+design notes):
+* dead column  <=>  its Hessian diagonal is exactly zero, i.e. the column
+  is all zero for any input whose nonzero squares do not underflow; the
+  neutralized diagonal entry becomes 1 (its row and column are already 0).
+* N = 0 gives a zero scaled H, so every column is dead.
+* neutralization happens before damping, so the mean diagonal includes the
+  1s written for dead columns (the order of steps 2 and 3 on the wiki).
+* the mean of the diagonal is taken in float64.
+* local blocks are unscaled and accumulate across calls.
+
+The input decoding is exact: bf16 values are given as their uint16 bit
+patterns and widened bit-for-bit; float32 values widen exactly to float64.
+Products of two such values are exact in float64 (<= 48 significant bits)
+and the sums carry only float64 rounding, about 1e-16 relative per add.
+"""
+
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+__all__ = [
+    "decode_bf16",
+    "exact_float64",
+    "GramAccumulator",
+    "materialize",
+    "local_blocks",
+    "grouped_grams",
+    "gram_entries",
+    "gram_exact_fraction",
+]
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 numbers given as uint16 bit patterns, as float64.
+
+    A bf16 number is the upper half of a float32 bit pattern, so shifting the
+    16 bits up by 16 and reading the result as float32 is exact.
+    """
+    bits = np.asarray(bits)
+    if bits.dtype != np.uint16:
+        raise TypeError("bf16 input must be given as uint16 bit patterns")
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def exact_float64(X: np.ndarray, in_dtype: str) -> np.ndarray:
+    """The stored input values as float64, exactly.
+
+    ``in_dtype`` is ``"bf16"`` (X holds uint16 bit patterns) or ``"f32"``.
+    """
+    if in_dtype == "bf16":
+        return decode_bf16(X)
+    if in_dtype == "f32":
+        X = np.asarray(X)
+        if X.dtype != np.float32:
+            raise TypeError("f32 input must be a float32 array")
+        return X.astype(np.float64)
+    raise ValueError(f"unknown input dtype {in_dtype!r}")
+
+
+class GramAccumulator:
+    """Running Gram sum S and token count N of one Hessian.
+
+    ``add_batch`` takes one calibration batch, tokens x features; an empty
+    batch changes nothing (GPTQModel PR 2981, Validation: empty batches).
+    """
+
+    def __init__(self, d: int):
+        if d < 1:
+            raise ValueError("d must be positive")
+        self.d = int(d)
+        self.S = np.zeros((self.d, self.d), dtype=np.float64)
+        self.N = 0
+
+    def add_batch(self, X: np.ndarray, in_dtype: str) -> None:
+        Xd = exact_float64(X, in_dtype)
+        if Xd.ndim != 2 or Xd.shape[1] != self.d:
+            raise ValueError(f"batch must be (tokens, {self.d})")
+        n = Xd.shape[0]
+        if n == 0:
+            return
+        self.S += Xd.T @ Xd
+        self.N += n
+
+    def materialize(self, damp_percent: float, neutralize: bool = True):
+        return materialize(self.S, self.N, damp_percent, neutralize)
+
+
+def materialize(S: np.ndarray, N: int, damp_percent: float, neutralize: bool = True):
+    """Final Hessian from the Gram sum: scale, neutralize, damp.
+
+    Returns ``(H, dead, damp)``: H float64 (d, d), ``dead`` a bool mask of
+    the neutralized columns (all False when ``neutralize`` is off), ``damp``
+    the absolute amount added to every diagonal entry.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    d = S.shape[0]
+    # Scale by 2 / total tokens, once, at the end; nothing accumulated -> 0.
+    H = (2.0 / N) * S if N > 0 else np.zeros((d, d), dtype=np.float64)
+    diag = np.diag(H).copy()
+    if neutralize:
+        dead = diag == 0.0
+        H[dead, :] = 0.0
+        H[:, dead] = 0.0
+        H[dead, dead] = 1.0
+    else:
+        dead = np.zeros(d, dtype=bool)
+    damp = float(damp_percent) * float(np.mean(np.diag(H)))
+    H[np.arange(d), np.arange(d)] += damp
+    return H, dead, damp
+
+
+def local_blocks(X: np.ndarray, in_dtype: str, block: int = 16) -> np.ndarray:
+    """Per-block Gram matrices of contiguous feature blocks, unscaled.
+
+    out[b] = X[:, block*b : block*(b+1)]^T  X[:, block*b : block*(b+1)]
+    """
+    Xd = exact_float64(X, in_dtype)
+    n, d = Xd.shape
+    if d % block != 0:
+        raise ValueError("feature count must be a multiple of the block size")
+    nb = d // block
+    out = np.empty((nb, block, block), dtype=np.float64)
+    for b in range(nb):
+        Xb = Xd[:, block * b: block * (b + 1)]
+        out[b] = Xb.T @ Xb
+    return out
+
+
+def grouped_grams(X: np.ndarray, in_dtype: str, row_idx: np.ndarray, offsets: np.ndarray):
+    """Independent Gram sums per group of rows (one group per routed expert).
+
+    Group e consists of rows ``row_idx[offsets[e]:offsets[e+1]]`` of X.
+    Returns a list of ``(S_e, N_e)``.  A group with no rows gets S = 0, N = 0.
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    row_idx = np.asarray(row_idx)
+    out = []
+    for e in range(len(offsets) - 1):
+        acc = GramAccumulator(np.asarray(X).shape[1])
+        rows = row_idx[offsets[e]:offsets[e + 1]]
+        acc.add_batch(np.asarray(X)[rows], in_dtype)
+        out.append((acc.S, acc.N))
+    return out
+
+
+def gram_entries(batches, in_dtype: str, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """Selected entries S[rows[k], cols[k]] of the Gram sum over ``batches``.
+
+    Each entry is the float64 dot product of two feature columns over every
+    token of every batch; used to check full-size results at sampled points.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    acc = np.zeros(rows.shape[0], dtype=np.float64)
+    for X in batches:
+        Xd = exact_float64(X, in_dtype)
+        if Xd.shape[0] == 0:
+            continue
+        acc += np.einsum("tk,tk->k", Xd[:, rows], Xd[:, cols])
+    return acc
+
+
+def gram_exact_fraction(rows_of_values) -> list:
+    """Exact rational Gram sum by a plain triple loop (tiny inputs only).
+
+    ``rows_of_values`` is a sequence of tokens, each a sequence of d Python
+    numbers (floats are converted exactly with ``Fraction``).  Returns a
+    d x d list of lists of ``Fraction``.
+    """
+    rows = [[Fraction(v) for v in r] for r in rows_of_values]
+    if not rows:
+        return []
+    d = len(rows[0])
+    S = [[Fraction(0) for _ in range(d)] for _ in range(d)]
+    for r in rows:
+        for i in range(d):
+            for j in range(d):
+                S[i][j] += r[i] * r[j]
+    return S

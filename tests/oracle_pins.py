@@ -1,0 +1,284 @@
+"""Pins for the float64 oracle: checks against facts that do not come from it.
+
+Each ``pin_*`` takes an oracle-like namespace ``O`` (the real ``oracle``
+package, or a deliberately broken variant built in the tests) and raises
+``AssertionError`` when ``O`` disagrees with:
+* exact rational arithmetic (``fractions.Fraction`` triple loops),
+* the pages' printed worked example,
+* hand-derived closed forms stored under ``tests/golden`` with citations,
+* library routines on special cases where they compute the same thing,
+* mathematical invariants (symmetry, positive semi-definiteness).
+"""
+
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _frac_gram(rows):
+    """Exact Gram by a triple loop written here, independent of the oracle."""
+    d = len(rows[0])
+    S = [[Fraction(0)] * d for _ in range(d)]
+    for r in rows:
+        fr = [Fraction(float(v)) for v in r]
+        for i in range(d):
+            for j in range(d):
+                S[i][j] += fr[i] * fr[j]
+    return S
+
+
+def pin_bruteforce_fraction(O, seed=11):
+    """Accumulated S over several tiny batches equals the exact rational sum."""
+    rng = np.random.default_rng(seed)
+    d = 5
+    sizes = [3, 0, 4, 1]
+    batches = [rng.standard_normal((n, d)).astype(np.float32) for n in sizes]
+    acc = O.GramAccumulator(d)
+    for b in batches:
+        acc.add_batch(b, "f32")
+    rows = [r for b in batches for r in b.tolist()]
+    S_exact = _frac_gram(rows)
+    assert acc.N == sum(sizes), f"token count {acc.N} != {sum(sizes)}"
+    for i in range(d):
+        for j in range(d):
+            ref = float(S_exact[i][j])
+            assert abs(acc.S[i, j] - ref) <= 1e-14 * max(1.0, abs(ref)), (i, j, acc.S[i, j], ref)
+    # the scaled Hessian, exactly: H = 2/N S
+    H, dead, damp = acc.materialize(0.0, neutralize=False)
+    for i in range(d):
+        for j in range(d):
+            ref = float(Fraction(2, acc.N) * S_exact[i][j])
+            assert abs(H[i, j] - ref) <= 1e-14 * max(1.0, abs(ref))
+    assert damp == 0.0 and not dead.any()
+
+
+def pin_orientation_hand(O):
+    g = _load("orientation_hand.json")
+    X = np.asarray(g["X"], dtype=np.float32)
+    acc = O.GramAccumulator(X.shape[1])
+    acc.add_batch(X, "f32")
+    assert acc.S.shape == (2, 2)
+    assert np.array_equal(acc.S, np.asarray(g["expected_S"], dtype=np.float64))
+    assert acc.N == g["expected_N"]
+    H, _, _ = acc.materialize(0.0, neutralize=False)
+    assert np.allclose(3.0 * H, np.asarray(g["expected_H_times_3"], dtype=np.float64), rtol=0, atol=1e-13)
+
+
+def pin_worked_example(O):
+    """The pages' printed fp32-vs-bf16 staging example, to the last bit."""
+    g = _load("worked_example_staging.json")
+    x = np.asarray(g["tokens"], dtype=np.float32)
+    acc = O.GramAccumulator(1)
+    acc.add_batch(x, "f32")
+    H, _, _ = acc.materialize(0.0, neutralize=False)
+    assert float(np.float32(H[0, 0])) == g["expected_diag_f32_input"]
+    assert H[0, 0] == g["expected_diag_f32_input"]  # exact in float32 and float64
+    acc = O.GramAccumulator(1)
+    acc.add_batch(W.to_bf16_bits(x), "bf16")
+    H, _, _ = acc.materialize(0.0, neutralize=False)
+    assert H[0, 0] == g["expected_diag_bf16_input"]
+
+
+def pin_neutralize_damp_hand(O):
+    g = _load("neutralize_damp_hand.json")
+    X = np.asarray(g["X"], dtype=np.float32)
+    acc = O.GramAccumulator(X.shape[1])
+    acc.add_batch(X, "f32")
+    H, dead, damp = acc.materialize(g["damp_percent"])
+    assert np.allclose(np.diag(H), g["expected_diag"], rtol=0, atol=1e-15)
+    assert np.array_equal(dead, np.asarray(g["expected_dead"]))
+    assert abs(damp - g["expected_damp"]) <= 1e-17
+    off = H - np.diag(np.diag(H))
+    assert not off.any()
+    e = g["empty_accumulator"]
+    acc = O.GramAccumulator(e["d"])
+    acc.add_batch(np.zeros((0, e["d"]), dtype=np.float32), "f32")
+    H, dead, damp = acc.materialize(e["damp_percent"])
+    assert acc.N == 0
+    assert np.allclose(np.diag(H), e["expected_diag"], rtol=0, atol=1e-15)
+    assert dead.all() and abs(damp - e["expected_damp"]) <= 1e-17
+    assert not (H - np.diag(np.diag(H))).any()
+
+
+def pin_multi_batch_is_concatenation(O, seed=3):
+    """Batches accumulate like one concatenated batch; N counts tokens."""
+    rng = np.random.default_rng(seed)
+    d = 7
+    sizes = [5, 1, 0, 9, 2]
+    batches = [rng.standard_normal((n, d)).astype(np.float32) for n in sizes]
+    a = O.GramAccumulator(d)
+    for b in batches:
+        a.add_batch(b, "f32")
+    c = O.GramAccumulator(d)
+    c.add_batch(np.concatenate(batches, axis=0), "f32")
+    assert a.N == c.N == sum(sizes)
+    assert np.allclose(a.S, c.S, rtol=1e-14, atol=1e-14)
+    Ha, _, _ = a.materialize(0.01)
+    Hc, _, _ = c.materialize(0.01)
+    assert np.allclose(Ha, Hc, rtol=1e-14, atol=1e-14)
+
+
+def pin_empty_batch_noop(O, seed=4):
+    rng = np.random.default_rng(seed)
+    d = 6
+    a = O.GramAccumulator(d)
+    a.add_batch(rng.standard_normal((4, d)).astype(np.float32), "f32")
+    S0, N0 = a.S.copy(), a.N
+    a.add_batch(np.zeros((0, d), dtype=np.float32), "f32")
+    a.add_batch(np.zeros((0, d), dtype=np.uint16), "bf16")
+    assert a.N == N0 and np.array_equal(a.S, S0)
+
+
+def pin_covariance_special_case(O, seed=5):
+    """For zero-mean columns, 2/N X^T X is twice numpy's biased covariance."""
+    rng = np.random.default_rng(seed)
+    Y = rng.standard_normal((50, 6)).astype(np.float32)
+    X = np.concatenate([Y, -Y], axis=0)  # every column sums to exactly zero
+    a = O.GramAccumulator(6)
+    a.add_batch(X, "f32")
+    H, _, _ = a.materialize(0.0, neutralize=False)
+    ref = 2.0 * np.cov(X.astype(np.float64), rowvar=False, bias=True)
+    assert np.allclose(H, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_symmetric_psd_cholesky(O, seed=6):
+    rng = np.random.default_rng(seed)
+    d = 24
+    a = O.GramAccumulator(d)
+    for n in (3, 8, 5):  # N = 16 < d: rank-deficient before damping
+        a.add_batch(rng.standard_normal((n, d)).astype(np.float32), "f32")
+    H, _, damp = a.materialize(0.0, neutralize=False)
+    assert np.array_equal(H, H.T)
+    w = np.linalg.eigvalsh(H)
+    assert w.min() >= -1e-12 * np.trace(H)
+    Hd, _, damp = a.materialize(0.01)
+    assert damp > 0
+    np.linalg.cholesky(Hd)  # raises if the damped Hessian is not positive definite
+
+
+def pin_unit_variance_diagonal(O, seed=7):
+    """N(0,1) inputs give a diagonal close to 2 (E[2/N sum x^2] = 2)."""
+    rng = np.random.default_rng(seed)
+    d, n = 8, 100_000
+    a = O.GramAccumulator(d)
+    a.add_batch(rng.standard_normal((n, d)).astype(np.float32), "f32")
+    H, _, _ = a.materialize(0.0, neutralize=False)
+    # std of each diagonal entry is 2*sqrt(2/n) ~ 0.009; allow 6 sigma
+    assert np.all(np.abs(np.diag(H) - 2.0) < 0.054)
+
+
+def pin_dead_mask_matches_zeroed_columns(O, seed=8):
+    rng = np.random.default_rng(seed)
+    d = 40
+    dead = np.array([0, 7, 13, 39])
+    X = rng.standard_normal((30, d)).astype(np.float32)
+    X[:, dead] = 0.0
+    a = O.GramAccumulator(d)
+    a.add_batch(W.to_bf16_bits(X), "bf16")
+    H, mask, damp = a.materialize(0.05)
+    assert np.array_equal(np.flatnonzero(mask), dead)
+    H0, _, _ = a.materialize(0.0)
+    assert np.allclose(H - H0, damp * np.eye(d), rtol=0, atol=1e-13)
+    assert np.all(np.diag(H0)[dead] == 1.0)
+
+
+def pin_bf16_decode(O):
+    import torch
+    known = {0x3F80: 1.0, 0xC000: -2.0, 0x3F81: 1.0078125, 0x0000: 0.0, 0x8000: -0.0,
+             0x7F7F: 3.3895313892515355e38, 0x0001: 9.183549615799121e-41}
+    for bits, val in known.items():
+        got = O.decode_bf16(np.array([bits], dtype=np.uint16))[0]
+        assert got == val, (hex(bits), got, val)
+    rng = np.random.default_rng(9)
+    bits = rng.integers(0, 1 << 16, size=4096, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]  # finite values only
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(O.decode_bf16(bits), ref)
+
+
+def pin_local_blocks(O, seed=10):
+    """Per-block Grams: exact rational check, and equal to the full Gram's diagonal blocks."""
+    rng = np.random.default_rng(seed)
+    n, d = 6, 48
+    X = rng.standard_normal((n, d)).astype(np.float32)
+    Xb = W.to_bf16_bits(X)
+    B = O.local_blocks(Xb, "bf16")
+    assert B.shape == (3, 16, 16)
+    vals = W.bf16_bits_to_float32(Xb).astype(np.float64)
+    for b in range(3):
+        cols = vals[:, 16 * b: 16 * b + 16]
+        S_exact = _frac_gram(cols.tolist())
+        for i in range(16):
+            for j in range(16):
+                assert abs(B[b, i, j] - float(S_exact[i][j])) <= 1e-14 * max(1.0, abs(float(S_exact[i][j])))
+    a = O.GramAccumulator(d)
+    a.add_batch(Xb, "bf16")
+    for b in range(3):
+        sl = slice(16 * b, 16 * b + 16)
+        assert np.allclose(B[b], a.S[sl, sl], rtol=1e-14, atol=1e-14)
+
+
+def pin_grouped(O, seed=12):
+    rng = np.random.default_rng(seed)
+    T, d, E, k = 200, 16, 12, 3
+    X = rng.standard_normal((T, d)).astype(np.float32)
+    row_idx, offsets = W.moe_routing(rng, T, experts=E, topk=k)
+    assert offsets[-1] == T * k
+    out = O.grouped_grams(X, "f32", row_idx, offsets)
+    assert len(out) == E
+    assert sum(N for _, N in out) == T * k
+    for e, (S, N) in enumerate(out):
+        rows = row_idx[offsets[e]:offsets[e + 1]]
+        sub = X[rows].astype(np.float64).tolist()
+        assert N == len(rows)
+        if N == 0:
+            assert not S.any()
+            continue
+        S_exact = _frac_gram(sub)
+        for i in range(0, d, 5):
+            for j in range(0, d, 3):
+                assert abs(S[i, j] - float(S_exact[i][j])) <= 1e-13 * max(1.0, abs(float(S_exact[i][j])))
+
+
+def pin_gram_entries(O, seed=13):
+    rng = np.random.default_rng(seed)
+    d = 9
+    batches = [rng.standard_normal((n, d)).astype(np.float32) for n in (4, 0, 3)]
+    rows = np.array([0, 3, 8, 8])
+    cols = np.array([0, 5, 2, 8])
+    got = O.gram_entries(batches, "f32", rows, cols)
+    allrows = [r for b in batches for r in b.tolist()]
+    S_exact = _frac_gram(allrows)
+    for k in range(4):
+        assert abs(got[k] - float(S_exact[rows[k]][cols[k]])) <= 1e-14 * max(1, abs(float(S_exact[rows[k]][cols[k]])))
+
+
+ALL_PINS = [
+    pin_bruteforce_fraction,
+    pin_orientation_hand,
+    pin_worked_example,
+    pin_neutralize_damp_hand,
+    pin_multi_batch_is_concatenation,
+    pin_empty_batch_noop,
+    pin_covariance_special_case,
+    pin_symmetric_psd_cholesky,
+    pin_unit_variance_diagonal,
+    pin_dead_mask_matches_zeroed_columns,
+    pin_bf16_decode,
+    pin_local_blocks,
+    pin_grouped,
+    pin_gram_entries,
+]
