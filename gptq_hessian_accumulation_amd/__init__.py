@@ -1,0 +1,273 @@
+"""Calibration-Hessian accumulation on AMD Instinct MI355X (gfx950).
+
+Python binding of ``libhess.so`` (C ABI in ``include/hess.h``).  The binding
+only marshals arguments: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current HIP stream.
+
+    H = (2/N) * sum_t x_t x_t^T         (GPTQModel PR 2979, What Changed)
+
+``Hessian.add_batch`` accumulates one calibration batch in place,
+``Hessian.materialize`` scales by 2/N, neutralizes dead columns and adds
+``damp_percent * mean(diag)`` to the diagonal (GPTQModel wiki "QQQ",
+Concepts > Quadratic error compensation), ``local_blocks`` builds the 16 x 16
+per-block Gram matrices and ``add_batch_grouped`` updates many routed-expert
+Hessians in one launch (Model-Optimizer PR 3002 page, "What does this PR do?").
+
+There is no CPU fallback: without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+__all__ = [
+    "Hessian",
+    "HessError",
+    "local_blocks",
+    "add_batch_grouped",
+    "set_tile_override",
+    "library_path",
+    "exported_symbols",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libhess.so")
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "hess.h")
+
+HESS_BF16 = 0
+HESS_F32 = 1
+HESS_NO_NEUTRALIZE = 1
+
+_STATUS = {0: "HESS_OK", -1: "HESS_EINVAL", -2: "HESS_ENOMEM", -3: "HESS_EHIP", -4: "HESS_ESTATE",
+           -5: "HESS_EALIGN"}
+
+
+class HessError(RuntimeError):
+    """A libhess call returned an error status."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{_STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"libhess.so is not built ({_LIB_PATH}); run `python gptq_hessian_accumulation_amd/build.py` "
+            "(or __graft_entry__.build()).  There is no CPU fallback.")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sig = {
+        "hess_abi_version": (c_int, []),
+        "hess_strerror": (ctypes.c_char_p, [c_int]),
+        "hess_last_error": (ctypes.c_char_p, []),
+        "hess_create": (vp, [i64, c_int]),
+        "hess_destroy": (c_int, [vp]),
+        "hess_add_batch": (c_int, [vp, vp, i64, i64, vp]),
+        "hess_materialize": (c_int, [vp, ctypes.c_float, vp]),
+        "hess_materialize_ex": (c_int, [vp, ctypes.c_float, ctypes.c_uint, vp, vp, vp, vp]),
+        "hess_reset": (c_int, [vp, vp]),
+        "hess_token_count": (c_int, [vp, ctypes.POINTER(i64)]),
+        "hess_set_tile_override": (c_int, [c_int]),
+        "hess_info": (c_int, [vp, ctypes.POINTER(i64), ctypes.POINTER(c_int)]),
+        "hess_state_buffer": (c_int, [vp, ctypes.POINTER(vp)]),
+        "hess_local_blocks": (c_int, [vp, i64, i64, c_int, vp]),
+        "hess_local_blocks_ex": (c_int, [vp, c_int, i64, i64, i64, c_int, vp, c_int, vp]),
+        "hess_add_batch_grouped": (c_int, [ctypes.POINTER(vp), c_int, vp, i64, vp, ctypes.POINTER(i64), vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        lib = _load()
+        raise HessError(code, lib.hess_last_error().decode(errors="replace"))
+
+
+def exported_symbols() -> list:
+    """Names of the functions declared in include/hess.h."""
+    with open(_HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hess_[a-z0-9_]+)\s*\(", text)))
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dtype_code(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return HESS_BF16
+    if dtype == torch.float32:
+        return HESS_F32
+    raise TypeError(f"unsupported activation dtype {dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _as_rows(x: torch.Tensor, d: int):
+    """(tokens, d) view of x with unit feature stride; returns (tensor, n, ld)."""
+    if x.shape[-1] != d:
+        raise ValueError(f"last dimension {x.shape[-1]} != d = {d}")
+    x2 = x.reshape(-1, d) if x.dim() != 2 else x
+    if x2.shape[0] > 0 and d > 1 and x2.stride(1) != 1:
+        x2 = x2.contiguous()
+    ld = x2.stride(0) if x2.shape[0] > 1 else d
+    return x2, x2.shape[0], max(ld, d)
+
+
+def set_tile_override(edge: int) -> None:
+    """Force the SYRK tile edge (0 = automatic, 128 or 192); process-wide."""
+    _check(_load().hess_set_tile_override(int(edge)))
+
+
+class Hessian:
+    """One calibration-Hessian accumulator of width ``d`` on the current GPU.
+
+    ``dtype`` is the activation element type every batch will have
+    (``torch.bfloat16`` or ``torch.float32``); the Hessian is always float32.
+    """
+
+    def __init__(self, d: int, dtype=torch.bfloat16):
+        lib = _load()
+        self.d = int(d)
+        self.dtype = dtype
+        self._code = _dtype_code(dtype)
+        h = lib.hess_create(self.d, self._code)
+        if not h:
+            raise HessError(-1, lib.hess_last_error().decode(errors="replace"))
+        self._h = ctypes.c_void_p(h)
+        self._device = torch.cuda.current_device()
+
+    # -- accumulation ----------------------------------------------------
+    def add_batch(self, x: torch.Tensor, stream=None) -> None:
+        """S += X^T X, N += tokens; leading dimensions of x are flattened to tokens."""
+        if not x.is_cuda:
+            raise ValueError("activations must be on the GPU")
+        if x.dtype != self.dtype:
+            raise TypeError(f"activations are {x.dtype}, this Hessian takes {self.dtype}")
+        x2, n, ld = _as_rows(x, self.d)
+        ptr = x2.data_ptr() if n > 0 else None
+        _check(_load().hess_add_batch(self._h, ptr, n, ld, _stream(stream)))
+
+    def materialize(self, damp_percent: float = 0.01, out: torch.Tensor | None = None, neutralize: bool = True,
+                    stream=None):
+        """Return ``(H, dead, damp)``: H float32 (d, d), dead bool (d,), damp float32 (1,), all on the GPU."""
+        dev = torch.device("cuda", self._device)
+        if out is None:
+            out = torch.empty((self.d, self.d), dtype=torch.float32, device=dev)
+        elif out.dtype != torch.float32 or tuple(out.shape) != (self.d, self.d) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 (d, d) GPU tensor")
+        dead = torch.empty(self.d, dtype=torch.uint8, device=dev)
+        damp = torch.empty(1, dtype=torch.float32, device=dev)
+        flags = 0 if neutralize else HESS_NO_NEUTRALIZE
+        _check(_load().hess_materialize_ex(self._h, float(damp_percent), flags, out.data_ptr(), dead.data_ptr(),
+                                           damp.data_ptr(), _stream(stream)))
+        return out, dead.bool(), damp
+
+    def materialize_in_place(self, damp_percent: float = 0.01, neutralize: bool = True, stream=None):
+        """Materialize into the accumulator's own buffer; the handle then needs reset()."""
+        dev = torch.device("cuda", self._device)
+        dead = torch.empty(self.d, dtype=torch.uint8, device=dev)
+        damp = torch.empty(1, dtype=torch.float32, device=dev)
+        flags = 0 if neutralize else HESS_NO_NEUTRALIZE
+        _check(_load().hess_materialize_ex(self._h, float(damp_percent), flags, None, dead.data_ptr(),
+                                           damp.data_ptr(), _stream(stream)))
+        return dead.bool(), damp
+
+    def state_buffer_ptr(self) -> int:
+        p = ctypes.c_void_p()
+        _check(_load().hess_state_buffer(self._h, ctypes.byref(p)))
+        return p.value
+
+    def state_tensor(self) -> torch.Tensor:
+        """A (d, d) float32 view of the accumulator's device buffer (S, or H after an in-place materialize)."""
+        ptr, d = self.state_buffer_ptr(), self.d
+
+        class _View:
+            __cuda_array_interface__ = {"shape": (d, d), "typestr": "<f4", "data": (ptr, False), "version": 2,
+                                        "strides": None}
+
+        return torch.as_tensor(_View(), device=torch.device("cuda", self._device))
+
+    def reset(self, stream=None) -> None:
+        _check(_load().hess_reset(self._h, _stream(stream)))
+
+    @property
+    def nsamples(self) -> int:
+        n = ctypes.c_int64()
+        _check(_load().hess_token_count(self._h, ctypes.byref(n)))
+        return n.value
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _check(_load().hess_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def local_blocks(x: torch.Tensor, out: torch.Tensor | None = None, accumulate: bool = True, block: int = 16,
+                 stream=None) -> torch.Tensor:
+    """out[b] (+)= X_b^T X_b for every 16-feature block b; float32 (d/16, 16, 16)."""
+    if not x.is_cuda:
+        raise ValueError("activations must be on the GPU")
+    d = x.shape[-1]
+    x2, n, ld = _as_rows(x, d)
+    if out is None:
+        out = torch.zeros((d // block, block, block), dtype=torch.float32, device=x.device)
+    elif out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != (d // block) * block * block:
+        raise ValueError("out must be a contiguous float32 (d/16, 16, 16) GPU tensor")
+    ptr = x2.data_ptr() if n > 0 else None
+    _check(_load().hess_local_blocks_ex(ptr, _dtype_code(x.dtype), n, d, ld, block, out.data_ptr(),
+                                        1 if accumulate else 0, _stream(stream)))
+    return out
+
+
+def add_batch_grouped(hessians, x: torch.Tensor, offsets, row_idx: torch.Tensor | None = None, stream=None) -> None:
+    """For each e: hessians[e] accumulates rows row_idx[offsets[e]:offsets[e+1]] of x, in one launch."""
+    if not hessians:
+        raise ValueError("need at least one Hessian")
+    d = hessians[0].d
+    for h in hessians:
+        if h.dtype != x.dtype:
+            raise TypeError("all Hessians must take the activation dtype")
+    x2, n, ld = _as_rows(x, d)
+    offs = [int(o) for o in (offsets.tolist() if hasattr(offsets, "tolist") else offsets)]
+    if len(offs) != len(hessians) + 1:
+        raise ValueError("offsets must have len(hessians) + 1 entries")
+    if row_idx is not None:
+        if row_idx.dtype != torch.int32 or not row_idx.is_cuda or not row_idx.is_contiguous():
+            raise ValueError("row_idx must be a contiguous int32 GPU tensor")
+        if row_idx.numel() < offs[-1]:
+            raise ValueError("row_idx shorter than offsets[-1]")
+    elif offs[-1] > n:
+        raise ValueError("offsets exceed the number of rows of x")
+    arr = (ctypes.c_void_p * len(hessians))(*[h._h.value for h in hessians])
+    oarr = (ctypes.c_int64 * len(offs))(*offs)
+    _check(_load().hess_add_batch_grouped(arr, len(hessians), x2.data_ptr() if n > 0 else None, ld,
+                                          row_idx.data_ptr() if row_idx is not None else None, oarr,
+                                          _stream(stream)))

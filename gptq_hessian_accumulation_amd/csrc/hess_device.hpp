@@ -1,0 +1,79 @@
+// Device-side building blocks shared by the gfx950 kernels of libhess.
+//
+// Matrix-core facts these kernels rely on (CDNA4, wave64), checked on the
+// hardware by an in-bounds lane-layout test:
+//  * v_mfma_f32_32x32x16_bf16: lane l supplies A[m = l%32][k = 8*(l/32)+s]
+//    and B[k = 8*(l/32)+s][n = l%32] for s = 0..7; accumulator register r of
+//    lane l holds C[8*(r/4) + 4*(l/32) + r%4][l%32].
+//  * v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][8*(l/16)+s] and
+//    B[8*(l/16)+s][l%16]; register r of lane l holds C[4*(l/16)+r][l%16].
+//  * A and B use the same k for the same (lane, slot), so a Gram X^T X only
+//    needs each lane to hold the same tokens for its A row and its B column.
+//  * The accumulation sums each group of 8 products exactly and rounds the
+//    sum into the fp32 accumulator to nearest.
+//  * ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+//    r (r = 0..3) from the address supplied by lane 4r + i/4, plus 2*(i%4)
+//    bytes: a 4 x 16 block of 16-bit values read transposed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hess {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#define HESS_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Split an fp32 value into hi + lo bf16 parts: hi = bf16(x), lo = bf16(x - hi).
+// x - hi is exact in fp32; x differs from hi + lo by at most 2^-17 |x|.
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_bits(x);
+  float r = x - bf16_bits_to_f32(hi);
+  lo = f32_to_bf16_bits(r);
+}
+
+// Pack two 16-bit values (low halves of a and b) into one dword: a | b << 16.
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+// Pack the high 16-bit halves of a and b: (a >> 16) | (b & 0xffff0000).
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// Transpose an 8 x 8 block of 16-bit values held as 8 rows of 4 dwords
+// (row t holds columns 2p, 2p+1 in dword p) into 8 columns of 4 dwords
+// (column f holds rows 2p, 2p+1 in dword p).
+__device__ __forceinline__ void transpose8x8_b16(const u32x4 (&row)[8], u32x4 (&col)[8]) {
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t a = row[2 * p][f >> 1];
+      const uint32_t b = row[2 * p + 1][f >> 1];
+      col[f][p] = (f & 1) ? pack_hi16(a, b) : pack_lo16(a, b);
+    }
+  }
+}
+
+}  // namespace hess

@@ -1,0 +1,210 @@
+/*
+ * hess.h -- calibration-Hessian accumulation on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libhess.so.  The library accumulates the GPTQ/QQQ calibration
+ * Hessian H = (2/N) * sum_t x_t x_t^T of a linear layer's input activations
+ * on one GPU, and builds the 16x16 per-block "local" Hessians.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Activations X are device memory, row-major tokens x features: element
+ *   (t, j) is at X[t*ld + j], with ld >= d elements.  bf16 or float32.
+ * - The Gram sum S, H_out, local blocks and dead masks are device memory.
+ *   Pointers marked (host) are host memory.
+ * - Every device operation is enqueued on the given HIP stream
+ *   (hipStream_t passed as hess_stream_t; NULL is the null stream).  No call
+ *   synchronizes with the host or allocates device memory after
+ *   hess_create(), so the calls may be captured into a HIP graph.  X must
+ *   stay valid and unchanged until the stream has executed the call.
+ * - A handle remembers the stream of its last call.  A call on a different
+ *   stream first makes that stream wait for the previous one (an event), so
+ *   updates of one Hessian never overlap.  Different handles are independent.
+ *   A handle must not be used from two host threads at the same time.
+ * - Errors are returned as negative codes; the library never aborts and has
+ *   no fallback paths.  hess_last_error() gives the calling thread's message
+ *   for its last failed call.
+ *
+ * Page citations below refer to: GPTQModel PR 2979 "fix(qqq): per-device
+ * Hessian partials for balanced multi-GPU calibration"; GPTQModel PR 2981
+ * "fix(qqq): accumulate Hessian in-place per device to reduce memory";
+ * NVIDIA Model-Optimizer PR 3002 page ("hessian_input_dtype"); GPTQModel
+ * wiki "QQQ".
+ */
+#ifndef HESS_H
+#define HESS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HESS_ABI_VERSION 1
+
+typedef struct hess_s* hess_t;
+typedef void* hess_stream_t; /* a hipStream_t */
+
+/* Input element types.  bf16 products are exact in float32 and summed in
+ * float32 (Model-Optimizer PR 3002 page, "What does this PR do?": bfloat16
+ * in, float32 out).  float32 inputs are multiplied to float32 accuracy. */
+enum hess_dtype { HESS_BF16 = 0, HESS_F32 = 1 };
+
+enum hess_status {
+  HESS_OK = 0,
+  HESS_EINVAL = -1, /* invalid argument */
+  HESS_ENOMEM = -2, /* device allocation failed (hess_create only) */
+  HESS_EHIP = -3,   /* a HIP runtime or launch error; see hess_last_error() */
+  HESS_ESTATE = -4, /* handle consumed by an in-place materialize */
+  HESS_EALIGN = -5  /* X not aligned to its element size */
+};
+
+/* hess_materialize_ex flags */
+#define HESS_NO_NEUTRALIZE 1u /* skip dead-column neutralization */
+
+/* Library ABI version (HESS_ABI_VERSION). */
+int hess_abi_version(void);
+
+/* Static description of a status code. */
+const char* hess_strerror(int code);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* hess_last_error(void);
+
+/*
+ * hess_create -- a new, empty Hessian accumulator of width d.
+ *
+ * Allocates and zeroes the persistent float32 d x d Gram buffer once (GPTQModel
+ * PR 2981, Changes: the per-device buffer is allocated once, as float32) plus
+ * fixed scratch for split reductions, on the current HIP device.  N = 0.
+ *   d         number of input features (Hessian width), 1 <= d <= 65536.
+ *   in_dtype  HESS_BF16 or HESS_F32: the element type of every X later given
+ *             to hess_add_batch (Model-Optimizer PR 3002, hessian_input_dtype).
+ * Returns NULL on error (EINVAL / ENOMEM / EHIP; see hess_last_error()).
+ * The handle owns its device memory until hess_destroy().
+ */
+hess_t hess_create(int64_t d, int in_dtype);
+
+/* Frees the handle and its device memory after draining its last stream. */
+int hess_destroy(hess_t h);
+
+/*
+ * hess_add_batch -- S += X^T X and N += n_tokens, in place.
+ *
+ * One calibration batch (GPTQModel PR 2979, What Changed: add_batch computes
+ * the Gram of the flattened activations and counts token vectors; PR 2981,
+ * Changes: accumulated directly into the persistent buffer with no transient
+ * d x d product).  Only the upper triangle of S (j >= i) is maintained.
+ *   X         device, n_tokens x d row-major with row stride ld elements, of
+ *             the handle's in_dtype, aligned to its element size.  When X is
+ *             16-byte aligned and ld*elem_size is a multiple of 16 bytes the
+ *             rows are read with 16-byte loads; otherwise a slower kernel
+ *             with element loads is used.
+ *   n_tokens  >= 0; 0 is a no-op (PR 2981, Validation: empty batches).
+ *   ld        row stride in elements, >= d.
+ *   stream    HIP stream the update is ordered on.
+ * Errors: EINVAL (h NULL, n_tokens < 0, ld < d, X NULL with n_tokens > 0),
+ * EALIGN (X not aligned to its element size), ESTATE, EHIP.  On error
+ * nothing is enqueued and N is unchanged.
+ */
+int hess_add_batch(hess_t h, const void* X, int64_t n_tokens, int64_t ld, hess_stream_t stream);
+
+/*
+ * hess_materialize -- H_out = neutralize_dead(S * 2/N) + damp * I, where
+ * damp = damp_percent * mean(diag) of the neutralized matrix.
+ *
+ * The final scale by 2 / total tokens (PR 2979, What Changed; wiki "QQQ",
+ * Concepts > Quadratic error compensation), then steps 2 and 3 of the
+ * quantization pass on that wiki page: neutralize dead input columns (a
+ * column whose diagonal is exactly zero: its row and column stay zero and
+ * its diagonal becomes 1), then add damp_percent * mean(diag(H)) to the
+ * diagonal.  N = 0 gives (1 + damp_percent) * I.
+ *   damp_percent  a fraction in [0, 1) (the pages' config validates (0, 1)).
+ *   H_out         device, d x d float32, full symmetric matrix, row-major;
+ *                 bitwise symmetric.  Must not alias S.
+ * Enqueued on the handle's last-used stream.  S and N are unchanged, so
+ * accumulation may continue and a later call sees the larger sum.
+ */
+int hess_materialize(hess_t h, float damp_percent, float* H_out);
+
+/*
+ * hess_materialize_ex -- hess_materialize with options.
+ *   flags     0 or HESS_NO_NEUTRALIZE.
+ *   H_out     device d x d float32, or NULL to materialize in place into the
+ *             handle's own buffer (saves a second d x d allocation); after
+ *             an in-place call the handle only accepts hess_reset,
+ *             hess_token_count, hess_state_buffer and hess_destroy (ESTATE).
+ *   dead_out  device, d bytes (1 = neutralized column), or NULL.
+ *   damp_out  device, one float: the absolute damping added to the diagonal
+ *             (wiki "QQQ", Implementation internals > Quantizer API and
+ *             results: the returned damp is that value), or NULL.
+ *   stream    HIP stream.
+ */
+int hess_materialize_ex(hess_t h, float damp_percent, unsigned flags, float* H_out,
+                        uint8_t* dead_out, float* damp_out, hess_stream_t stream);
+
+/* S = 0, N = 0 (enqueued on stream); also re-arms a consumed handle. */
+int hess_reset(hess_t h, hess_stream_t stream);
+
+/* Tokens accumulated so far (host int64; exact, counted on the host). */
+int hess_token_count(hess_t h, int64_t* n_out);
+
+/* Tuning and test hook, process-wide: force the edge of the upper-triangle
+ * tiles used by hess_add_batch (0 = automatic choice per call, 128 or 192).
+ * float32 inputs and unaligned X always use 128. */
+int hess_set_tile_override(int edge);
+
+/* Width and input type of a handle (host outputs). */
+int hess_info(hess_t h, int64_t* d_out, int* in_dtype_out);
+
+/*
+ * hess_state_buffer -- the device address of the handle's float32 d x d
+ * buffer: the Gram sum S (upper triangle valid) or, after an in-place
+ * materialize, H.  Read-only for callers except through this API.
+ */
+int hess_state_buffer(hess_t h, const float** S_out);
+
+/*
+ * hess_local_blocks -- out[b] += X_b^T X_b for every contiguous block of 16
+ * features (Model-Optimizer PR 3002 page, "What does this PR do?",
+ * local_hessian bullet: 16x16 per-block Hessians by a batched product that
+ * reads bfloat16 and writes float32).  Unscaled; accumulates into out.
+ *   X         device bf16, n_tokens x d row-major, ld = d.
+ *   n_tokens  >= 0.
+ *   d         multiple of block, >= block.
+ *   block     must be 16.
+ *   out       device float32 (d/16, 16, 16), row-major blocks.
+ * Runs on the null stream.
+ */
+int hess_local_blocks(const void* X, int64_t n_tokens, int64_t d, int block, float* out);
+
+/*
+ * hess_local_blocks_ex -- hess_local_blocks with dtype, stride, stream and
+ * accumulate (nonzero: out += ..., zero: out = ...).
+ */
+int hess_local_blocks_ex(const void* X, int in_dtype, int64_t n_tokens, int64_t d, int64_t ld,
+                         int block, float* out, int accumulate, hess_stream_t stream);
+
+/*
+ * hess_add_batch_grouped -- for each group e < n_groups:
+ *   S_e += X[rows_e]^T X[rows_e],  N_e += |rows_e|,
+ * in one launch.  One Hessian per routed expert over the tokens routed to it
+ * (Model-Optimizer PR 3002 page: the option applies to every GPTQ Hessian,
+ * fused MoE experts included; experts never share a Hessian).
+ *   hs        (host) n_groups distinct handles of equal d and in_dtype.
+ *   X         device, T x d row-major with row stride ld (all tokens).
+ *   row_idx   device int32, offsets[n_groups] entries: rows of X grouped by
+ *             expert; group e is row_idx[offsets[e] .. offsets[e+1]).  NULL
+ *             means X's rows are already grouped (row_idx[i] = i).
+ *   offsets   (host) int64, n_groups + 1 non-decreasing entries, offsets[0]=0.
+ * All row indices must be in [0, T) where T is the caller's row count; the
+ * library cannot check device contents.
+ */
+int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld,
+                           const int32_t* row_idx, const int64_t* offsets, hess_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HESS_H */

@@ -1,0 +1,61 @@
+"""The C-ABI library loads and exports every declared symbol; argument checks
+that return before touching the GPU behave as declared.  CPU only."""
+
+import ctypes
+import os
+
+import pytest
+
+import gptq_hessian_accumulation_amd as hs
+
+LIB = hs.library_path()
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libhess.so not built")
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIB)
+    names = hs.exported_symbols()
+    assert len(names) >= 14
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_required_entry_points_declared():
+    names = set(hs.exported_symbols())
+    for n in ("hess_create", "hess_add_batch", "hess_materialize", "hess_local_blocks",
+              "hess_materialize_ex", "hess_add_batch_grouped", "hess_local_blocks_ex", "hess_reset",
+              "hess_destroy", "hess_token_count"):
+        assert n in names
+
+
+def test_version_and_status_strings():
+    lib = hs._load()
+    assert lib.hess_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.hess_strerror(code)
+    assert lib.hess_strerror(-99) == b"unknown status"
+
+
+def test_invalid_arguments_rejected_without_gpu():
+    lib = hs._load()
+    assert not lib.hess_create(0, 0)
+    assert b"outside" in lib.hess_last_error()
+    assert not lib.hess_create(16, 7)
+    assert lib.hess_add_batch(None, None, 1, 16, None) == -1
+    assert lib.hess_materialize(None, 0.01, None) == -1
+    assert lib.hess_token_count(None, None) == -1
+    # local blocks: block must be 16, d a multiple of 16, ld >= d
+    assert lib.hess_local_blocks(None, 0, 32, 8, ctypes.c_void_p(16)) == -1
+    assert lib.hess_local_blocks(None, 0, 40, 16, ctypes.c_void_p(16)) == -1
+    assert lib.hess_local_blocks_ex(None, 0, 0, 32, 16, 16, ctypes.c_void_p(16), 1, None) == -1
+    assert lib.hess_local_blocks_ex(None, 0, 5, 32, 32, 16, ctypes.c_void_p(16), 1, None) == -1
+    assert lib.hess_set_tile_override(100) == -1
+    offs = (ctypes.c_int64 * 2)(0, 1)
+    assert lib.hess_add_batch_grouped(None, 1, None, 16, None, offs, None) == -1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(hs, "_lib", None)
+    monkeypatch.setattr(hs, "_LIB_PATH", "/nonexistent/libhess.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        hs._load()

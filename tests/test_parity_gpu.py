@@ -1,0 +1,343 @@
+"""HIP path vs the float64 oracle, element by element, through the C ABI.
+
+Small and medium shapes that span several tiles and ragged tails are compared
+in full; the edge cases of the method (empty batches, N = 0, dead columns,
+odd widths, unaligned rows) are covered; exactness cases (the pages' worked
+example, dyadic inputs whose every float32 sum is exact) are compared bitwise.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+import gptq_hessian_accumulation_amd as hs
+from tests.helpers import TOL, agreement, block_agreement, to_device, torch_dtype
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _tile_auto():
+    hs.set_tile_override(0)
+    yield
+    hs.set_tile_override(0)
+
+
+def run_lib(wl: W.Workload, damp=0.01, neutralize=True):
+    h = hs.Hessian(wl.d, torch_dtype(wl.dtype))
+    for b in wl.batches:
+        h.add_batch(to_device(b, wl.dtype))
+    H, dead, dmp = h.materialize(damp, neutralize=neutralize)
+    torch.cuda.synchronize()
+    out = H.cpu().numpy(), dead.cpu().numpy(), float(dmp.cpu()[0]), h.nsamples
+    h.close()
+    return out
+
+
+def run_oracle(wl: W.Workload, damp=0.01, neutralize=True):
+    acc = O.GramAccumulator(wl.d)
+    for b in wl.batches:
+        acc.add_batch(b, wl.dtype)
+    H, dead, dmp = acc.materialize(damp, neutralize)
+    return H, dead, dmp, acc.N
+
+
+def check_against_oracle(wl: W.Workload, tol=None):
+    tol = TOL[wl.dtype] if tol is None else tol
+    for damp, neut in ((0.0, False), (0.01, True)):
+        H, dead, dmp, N = run_lib(wl, damp, neut)
+        Hr, deadr, dmpr, Nr = run_oracle(wl, damp, neut)
+        assert N == Nr
+        assert np.array_equal(dead, deadr)
+        err = agreement(H, Hr)
+        assert err <= tol, f"agreement {err:.3e} > {tol:.1e} (damp={damp}, neutralize={neut})"
+        assert np.array_equal(H, H.T), "H must be bitwise symmetric"
+        assert abs(dmp - dmpr) <= 1e-6 * max(abs(dmpr), 1e-30) + 1e-30
+    return err
+
+
+# ------------------------------------------------------------ small cases --
+
+def test_tiny_case_fp32():
+    _say("tiny d=256 fp32 100/37/0")
+    wl = W.tiny_case()
+    check_against_oracle(wl)
+
+
+@pytest.mark.parametrize("d", [384, 520, 700])
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_ragged_batches(d, dtype):
+    _say(f"ragged d={d} {dtype}")
+    sizes = [1, 63, 64, 65, 777, 0, 1500]
+    wl = W.ragged_case(d, sizes, seed=100 + d, dtype=dtype, dead_frac=0.02)
+    check_against_oracle(wl)
+
+
+@pytest.mark.parametrize("d", [1, 17, 255, 257])
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_edge_widths(d, dtype):
+    _say(f"edge width d={d} {dtype}")
+    wl = W.ragged_case(d, [3, 129, 1], seed=7 + d, dtype=dtype)
+    check_against_oracle(wl)
+
+
+@pytest.mark.parametrize("edge", [128])
+def test_forced_tile_edges(edge):
+    _say(f"forced tile {edge}")
+    hs.set_tile_override(edge)
+    wl = W.ragged_case(1000, [300, 2000], seed=55, dtype=W.BF16)
+    check_against_oracle(wl)
+
+
+def test_worked_example_bitwise():
+    """One token with component 1 + 2^-10: fp32 input gives 2.003908157348633, bf16 input 2.0."""
+    _say("worked example")
+    x = np.zeros((1, 16), dtype=np.float32)
+    x[0, 0] = 1.0009765625
+    for dtype, expect in ((W.F32, 2.003908157348633), (W.BF16, 2.0)):
+        wl = W.Workload(d=16, dtype=dtype, batches=[W.encode(x, dtype)])
+        H, dead, dmp, N = run_lib(wl, damp=0.0, neutralize=False)
+        assert N == 1
+        assert H[0, 0] == np.float32(expect)
+        assert not H[1:, :].any() and not H[0, 1:].any()
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_dyadic_inputs_exact(dtype):
+    """Values in {-2..2}/4 keep every float32 partial sum exact, so S is unique; N = 256 makes 2/N exact."""
+    _say(f"dyadic exact {dtype}")
+    rng = np.random.default_rng(31)
+    d = 300
+    batches = [(rng.integers(-2, 3, size=(n, d)) / 4.0).astype(np.float32) for n in (100, 0, 156)]
+    wl = W.Workload(d=d, dtype=dtype, batches=[W.encode(b, dtype) for b in batches])
+    H, dead, dmp, N = run_lib(wl, damp=0.0, neutralize=False)
+    Hr, _, _, Nr = run_oracle(wl, damp=0.0, neutralize=False)
+    assert N == Nr == 256
+    assert np.array_equal(H.astype(np.float64), Hr)
+
+
+def test_empty_accumulator():
+    _say("N = 0")
+    for dtype in (W.BF16, W.F32):
+        wl = W.Workload(d=70, dtype=dtype, batches=[np.zeros((0, 70), dtype=np.uint16 if dtype == W.BF16
+                                                            else np.float32)])
+        H, dead, dmp, N = run_lib(wl, damp=0.01)
+        assert N == 0 and dead.all()
+        assert np.array_equal(H, np.float32(1.01) * np.eye(70, dtype=np.float32))
+        assert dmp == np.float32(0.01)
+
+
+def test_dead_columns_and_damping():
+    _say("dead columns and damping")
+    wl = W.ragged_case(600, [500, 300], seed=9, dtype=W.BF16, dead_frac=0.05)
+    H1, dead1, d1, _ = run_lib(wl, damp=0.05)
+    H0, dead0, d0, _ = run_lib(wl, damp=0.0)
+    assert np.array_equal(np.flatnonzero(dead1), wl.dead_cols)
+    assert np.array_equal(dead0, dead1)
+    assert d0 == 0.0
+    # H(p) - H(0) is the damping on the diagonal only
+    diff = H1.astype(np.float64) - H0.astype(np.float64)
+    assert np.array_equal(diff - np.diag(np.diag(diff)), np.zeros_like(diff))
+    # (h + damp) is rounded once in float32: within half an ulp of the largest diagonal
+    ulp = float(np.spacing(np.float32(np.max(np.diag(H1)))))
+    assert np.allclose(np.diag(diff), d1, rtol=0, atol=ulp)
+    assert np.all(np.diag(H0)[wl.dead_cols] == 1.0)
+    assert not H0[wl.dead_cols][:, np.setdiff1d(np.arange(600), wl.dead_cols)].any()
+    np.linalg.cholesky(H1.astype(np.float64))
+
+
+def test_materialize_repeatable_and_accumulation_continues():
+    _say("materialize twice, continue")
+    wl = W.ragged_case(256, [200, 100, 50], seed=12, dtype=W.BF16)
+    h = hs.Hessian(256, torch.bfloat16)
+    h.add_batch(to_device(wl.batches[0], W.BF16))
+    A, _, _ = h.materialize(0.01)
+    B, _, _ = h.materialize(0.01)
+    assert torch.equal(A, B)
+    for b in wl.batches[1:]:
+        h.add_batch(to_device(b, W.BF16))
+    C, _, _ = h.materialize(0.01)
+    Hr, _, _, _ = run_oracle(wl, 0.01)
+    assert agreement(C.cpu().numpy(), Hr) <= TOL[W.BF16]
+    assert h.nsamples == 350
+    h.close()
+
+
+def test_in_place_materialize_consumes_handle():
+    _say("in-place materialize")
+    wl = W.ragged_case(200, [150], seed=13, dtype=W.F32)
+    h = hs.Hessian(200, torch.float32)
+    h.add_batch(to_device(wl.batches[0], W.F32))
+    ref, _, _ = h.materialize(0.01)
+    dead, damp = h.materialize_in_place(0.01)
+    torch.cuda.synchronize()
+    with pytest.raises(hs.HessError) as e:
+        h.add_batch(to_device(wl.batches[0], W.F32))
+    assert e.value.code == -4
+    # the state buffer now holds H
+    buf = h.state_tensor().clone()
+    assert torch.equal(buf, ref)
+    h.reset()
+    h.add_batch(to_device(wl.batches[0], W.F32))
+    again, _, _ = h.materialize(0.01)
+    assert torch.equal(again, ref)
+    h.close()
+
+
+def test_two_streams_are_ordered():
+    _say("two streams")
+    wl = W.ragged_case(512, [800, 800, 800, 800], seed=14, dtype=W.BF16)
+    xs = [to_device(b, W.BF16) for b in wl.batches]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    h = hs.Hessian(512, torch.bfloat16)
+    for i, x in enumerate(xs):
+        h.add_batch(x, stream=s1 if i % 2 == 0 else s2)
+    H, _, _ = h.materialize(0.01, stream=s1)
+    s1.synchronize()
+    Hr, _, _, _ = run_oracle(wl, 0.01)
+    assert agreement(H.cpu().numpy(), Hr) <= TOL[W.BF16]
+    h.close()
+
+
+def test_add_batch_allocates_nothing():
+    _say("zero allocation")
+    h = hs.Hessian(1024, torch.bfloat16)
+    x = torch.randn(1500, 1024, device="cuda").to(torch.bfloat16)
+    h.add_batch(x)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    alloc0 = torch.cuda.memory_allocated()
+    for _ in range(30):
+        h.add_batch(x)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.memory_allocated() == alloc0
+    assert free1 == free0
+    h.close()
+
+
+def test_flattened_leading_dims_and_strided_rows():
+    _say("3-D input and strided rows")
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((4, 50, 96)).astype(np.float32)
+    big = np.zeros((200, 128), dtype=np.float32)
+    big[:, :96] = x.reshape(200, 96)
+    h = hs.Hessian(96, torch.float32)
+    h.add_batch(torch.from_numpy(x).cuda())                 # (4, 50, 96) -> 200 tokens
+    h.add_batch(torch.from_numpy(big).cuda()[:, :96])       # row stride 128
+    H, _, _ = h.materialize(0.0, neutralize=False)
+    acc = O.GramAccumulator(96)
+    acc.add_batch(x.reshape(200, 96), W.F32)
+    acc.add_batch(big[:, :96].copy(), W.F32)
+    Hr, _, _ = acc.materialize(0.0, neutralize=False)
+    assert h.nsamples == 400
+    assert agreement(H.cpu().numpy(), Hr) <= TOL[W.F32]
+    h.close()
+
+
+def test_nan_propagates():
+    _say("NaN input")
+    x = np.ones((4, 32), dtype=np.float32)
+    x[2, 5] = np.nan
+    h = hs.Hessian(32, torch.float32)
+    h.add_batch(torch.from_numpy(x).cuda())
+    H, dead, damp = h.materialize(0.01)
+    Hn = H.cpu().numpy()
+    assert np.isnan(Hn[5, 5]) and np.isnan(Hn[5, 0]) and not dead.cpu().numpy()[5]
+    h.close()
+
+
+# ----------------------------------------------------------- local blocks --
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+@pytest.mark.parametrize("n,d", [(1000, 512), (77, 48), (4096, 272)])
+def test_local_blocks(dtype, n, d):
+    _say(f"local blocks n={n} d={d} {dtype}")
+    rng = np.random.default_rng(40 + n)
+    x = W.encode(W.normal_rows(rng, n, d, W.column_scales(rng, d)), dtype)
+    x2 = W.encode(W.normal_rows(rng, n // 2 + 1, d), dtype)
+    xt = to_device(x, dtype)
+    out = hs.local_blocks(xt, accumulate=False)
+    hs.local_blocks(to_device(x2, dtype), out=out, accumulate=True)
+    torch.cuda.synchronize()
+    ref = O.local_blocks(x, dtype) + O.local_blocks(x2, dtype)
+    assert block_agreement(out.cpu().numpy(), ref) <= TOL[dtype]
+
+
+def test_local_blocks_match_full_path_diagonal_blocks():
+    _say("local vs full diagonal blocks")
+    rng = np.random.default_rng(41)
+    x = W.encode(W.normal_rows(rng, 3000, 256), W.BF16)
+    xt = to_device(x, W.BF16)
+    B = hs.local_blocks(xt, accumulate=False)
+    h = hs.Hessian(256, torch.bfloat16)
+    h.add_batch(xt)
+    H, _, _ = h.materialize(0.0, neutralize=False)
+    S = H.double() * (3000 / 2.0)
+    for b in range(16):
+        sl = slice(16 * b, 16 * b + 16)
+        ref = S[sl, sl]
+        assert torch.allclose(B[b].double(), ref, rtol=2e-5, atol=1e-3)
+    h.close()
+
+
+# ---------------------------------------------------------------- grouped --
+
+@pytest.mark.parametrize("gather", [True, False])
+def test_grouped_experts(gather):
+    _say(f"grouped experts gather={gather}")
+    rng = np.random.default_rng(50)
+    T, d, E, k = 1500, 384, 12, 3
+    x = W.encode(W.normal_rows(rng, T, d, W.column_scales(rng, d)), W.BF16)
+    row_idx, offsets = W.moe_routing(rng, T, experts=E, topk=k)
+    hsx = [hs.Hessian(d, torch.bfloat16) for _ in range(E)]
+    if gather:
+        hs.add_batch_grouped(hsx, to_device(x, W.BF16), offsets, torch.from_numpy(row_idx).cuda())
+        src, idx = x, row_idx
+    else:
+        xg = x[row_idx]
+        hs.add_batch_grouped(hsx, to_device(xg, W.BF16), offsets)
+        src, idx = xg, np.arange(xg.shape[0], dtype=np.int32)
+    ref = O.grouped_grams(src, W.BF16, idx, offsets)
+    for e in range(E):
+        S_e, N_e = ref[e]
+        assert hsx[e].nsamples == N_e
+        H, _, _ = hsx[e].materialize(0.0, neutralize=False)
+        Hr, _, _ = O.materialize(S_e, N_e, 0.0, neutralize=False)
+        if N_e == 0:
+            assert not H.cpu().numpy().any()
+        else:
+            assert agreement(H.cpu().numpy(), Hr) <= TOL[W.BF16]
+        hsx[e].close()
+
+
+def test_grouped_equals_single_handle_runs():
+    _say("grouped equals single")
+    rng = np.random.default_rng(51)
+    T, d, E = 900, 256, 5
+    x = W.encode(W.normal_rows(rng, T, d), W.BF16)
+    row_idx, offsets = W.moe_routing(rng, T, experts=E, topk=2)
+    xt = to_device(x, W.BF16)
+    ridx = torch.from_numpy(row_idx).cuda()
+    grouped = [hs.Hessian(d, torch.bfloat16) for _ in range(E)]
+    hs.add_batch_grouped(grouped, xt, offsets, ridx)
+    for e in range(E):
+        rows = ridx[offsets[e]:offsets[e + 1]].long()
+        single = hs.Hessian(d, torch.bfloat16)
+        single.add_batch(xt[rows])
+        A, _, _ = grouped[e].materialize(0.01)
+        B, _, _ = single.materialize(0.01)
+        assert agreement(A.cpu().numpy(), B.cpu().numpy().astype(np.float64)) <= 1e-6
+        single.close()
+        grouped[e].close()
