@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark: ms per calibration Hessian on one MI355X.
+
+A step is one whole Hessian: reset, every calibration batch through
+hess_add_batch, then hess_materialize (scale 2/N, neutralize, 1% damping).
+The headline workload is width 2,560 with 360 batches of 1..2,000 tokens,
+bf16 activations N(0,1) x lognormal(0, 0.5) column scales, pre-staged in one
+device buffer (inputs resident in HBM before the timed region starts).
+
+Other workloads (width 4,096 ragged and a single 32K-token batch in bf16 and
+fp32, 64 routed-expert Hessians in one grouped launch, 16x16 local blocks)
+are timed after the headline and reported under "extra".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+P_BF16 = 2.5e15        # MI355X dense bf16 matrix peak, FLOP/s
+P_F32_MFMA = 157.3e12  # MI355X fp32 matrix peak, FLOP/s
+HBM = 8.0e12           # MI355X HBM3E peak, bytes/s
+METRIC = "ms per Hessian & TFLOP/s (MFMA util %) at d=2560/4096, ragged batches"
+PAGES_MS = {2560: 11.0, 4096: 15.0}  # the pages' GB300 bf16-in numbers for ~360 ragged batches
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def ragged_setup(torch, W, d, seed, dtype="bf16", count=360, dead_frac=0.0, device="cuda"):
+    """Batches of U[1,2000] tokens, staged back to back in one device buffer."""
+    rng = np.random.default_rng(seed)
+    sizes = rng.integers(1, 2001, size=count)
+    dead = W.dead_columns(rng, d, dead_frac)
+    gen = W.torch_generator(seed, device)
+    scales = W.torch_column_scales(gen, d, device)
+    if dead.size:
+        scales[torch.from_numpy(dead).to(device)] = 0.0
+    total = int(sizes.sum())
+    buf = W.torch_rows(gen, total, d, scales, dtype, device)
+    views, off = [], 0
+    for n in sizes:
+        views.append(buf[off:off + int(n)])
+        off += int(n)
+    return buf, views, sizes
+
+
+def time_hessian(torch, hs, d, views, steps, warmup, dtype, kernel_events=False):
+    """Whole-Hessian timing; optionally per-add_batch HIP events (same stream)."""
+    h = hs.Hessian(d, dtype)
+    out = torch.empty((d, d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def one(evs=None):
+        h.reset()
+        for i, x in enumerate(views):
+            if evs is not None:
+                evs[i][0].record(stream)
+            h.add_batch(x)
+            if evs is not None:
+                evs[i][1].record(stream)
+        h.materialize(0.01, out=out)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(steps):
+        one()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - wall0) * 1e3 / steps
+    ms = t0.elapsed_time(t1) / steps
+    kern_ms = None
+    if kernel_events:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in views]
+        tot = np.zeros(len(views))
+        for _ in range(steps):
+            one(evs)
+            torch.cuda.synchronize()
+            tot += np.array([a.elapsed_time(b) for a, b in evs])
+        kern_ms = tot / steps
+    h.close()
+    return ms, wall, kern_ms
+
+
+def syrk_flops(d, n):
+    return float(n) * d * (d + 1)          # upper triangle incl. diagonal, 2 flops per MAC
+
+
+def syrk_bytes(d, n, esize):
+    return 4.0 * d * (d + 1) + float(n) * d * esize   # upper S read + write, X read
+
+
+def cpu_baseline(W, O, torch, views, d, total_flops, max_batches=60, budget_s=20.0):
+    """The float64 oracle on the host, on the first batches of the same workload."""
+    t_used, flops_done, nb = 0.0, 0.0, 0
+    acc = O.GramAccumulator(d)
+    for x in views[:max_batches]:
+        xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        acc.add_batch(xb, "bf16")
+        t_used += time.perf_counter() - t0
+        flops_done += syrk_flops(d, xb.shape[0])
+        nb += 1
+        if t_used > budget_s:
+            break
+    t0 = time.perf_counter()
+    acc.materialize(0.01)
+    t_mat = time.perf_counter() - t0
+    ms = (t_used * total_flops / flops_done + t_mat) * 1e3
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {"value": round(ms, 1), "unit": "ms/Hessian", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 NumPy oracle on the first {nb} of {len(views)} batches "
+                      f"({t_used:.1f} s), scaled by algorithmic flops to the whole Hessian, plus materialize"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the Hessian path runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gptq_hessian_accumulation_amd as hs
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    d = 2560
+    log("staging d=2560 ragged workload")
+    buf, views, sizes = ragged_setup(torch, W, d, seed=1)
+    N = int(sizes.sum())
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} Hessians after {args.warmup} warm-ups")
+    ms, wall, _ = time_hessian(torch, hs, d, views, args.steps, args.warmup, torch.bfloat16)
+    log(f"headline: {ms:.3f} ms per Hessian (host wall {wall:.3f} ms)")
+    _, _, kern = time_hessian(torch, hs, d, views, max(2, args.steps // 2), 1, torch.bfloat16,
+                              kernel_events=True)
+    flops = syrk_flops(d, N)
+    tflops = flops / (ms * 1e-3) / 1e12
+    # roofline of the dominant kernel (the SYRK update): algorithmic bytes per
+    # launch / its mean launch duration, from HIP events around each launch
+    kbytes = np.array([syrk_bytes(d, n, 2) for n in sizes])
+    kflops = np.array([syrk_flops(d, n) for n in sizes])
+    kern_s = kern * 1e-3
+    achieved_bw = kbytes.mean() / kern_s.mean()
+    roof_t = np.maximum(kflops / P_BF16, kbytes / HBM)
+    result = {
+        "metric": METRIC,
+        "value": round(ms, 4),
+        "unit": "ms/Hessian",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": round(ms / PAGES_MS[d], 4),
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "d=2560, 360 ragged calibration batches of U[1,2000] tokens, bf16 N(0,1) x "
+                               "lognormal(0,0.5) column scales, one fp32 Hessian scaled 2/N, damp 1%",
+                   "d": d, "batches": len(sizes), "tokens": N, "seed": 1},
+        "tflops": round(tflops, 2),
+        "mfma_util": round(flops / (ms * 1e-3) / P_BF16, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved_bw / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(achieved_bw / HBM, 4), "traffic": None,
+                     "kernel": "syrk_bf16 (hess_add_batch)", "mean_launch_us": round(kern_s.mean() * 1e6, 2),
+                     "per_batch_roofline_frac": round(float(roof_t.sum() / kern_s.sum()), 4)},
+    }
+    del buf, views
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extras:
+        extra = run_extras(torch, hs, W, args)
+        result["extra"] = extra
+
+    if not args.no_cpu:
+        import oracle as O
+        log("cpu baseline (oracle)")
+        buf, views, sizes = ragged_setup(torch, W, d, seed=1)
+        result["cpu_baseline"] = cpu_baseline(W, O, torch, views, d, flops)
+    print(json.dumps(result), flush=True)
+
+
+def run_extras(torch, hs, W, args):
+    extra = {}
+    steps = max(3, args.steps // 2)
+    # d=4096 ragged (bf16 and fp32), dead columns 1%
+    for dt, tdt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+        log(f"d=4096 ragged {dt}")
+        buf, views, sizes = ragged_setup(torch, W, 4096, seed=2, dtype=dt, dead_frac=0.01)
+        N = int(sizes.sum())
+        ms, _, _ = time_hessian(torch, hs, 4096, views, steps, 1, tdt)
+        fl = syrk_flops(4096, N)
+        extra[f"d4096_ragged_{dt}"] = {"ms": round(ms, 3), "tflops": round(fl / ms / 1e9, 1),
+                                       "mfma_util": round(fl / (ms * 1e-3) / P_BF16, 4), "tokens": N,
+                                       "pages_gb300_ms": PAGES_MS[4096] if dt == "bf16" else 244.0}
+        del buf, views
+    # d=4096, one 32768-token batch
+    for dt, tdt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+        log(f"d=4096 single 32K batch {dt}")
+        gen = W.torch_generator(2, "cuda")
+        sc = W.torch_column_scales(gen, 4096, "cuda")
+        x = W.torch_rows(gen, 32768, 4096, sc, dt, "cuda")
+        ms, _, kern = time_hessian(torch, hs, 4096, [x], steps, 1, tdt, kernel_events=True)
+        fl = syrk_flops(4096, 32768)
+        peak = P_BF16
+        extra[f"d4096_n32768_{dt}"] = {"ms": round(ms, 4), "syrk_ms": round(float(kern[0]), 4),
+                                       "syrk_tflops": round(fl / kern[0] / 1e9, 1),
+                                       "syrk_mfma_util": round(fl / (kern[0] * 1e-3) / peak, 4)}
+        del x
+    # MoE: 64 routed experts, d=2048, 32768 tokens top-8, Zipf(1.1)
+    log("MoE grouped")
+    rng = np.random.default_rng(3)
+    row_idx, offsets = W.moe_routing(rng, 32768, experts=64, topk=8)
+    gen = W.torch_generator(3, "cuda")
+    sc = W.torch_column_scales(gen, 2048, "cuda")
+    x = W.torch_rows(gen, 32768, 2048, sc, "bf16", "cuda")
+    ridx = torch.from_numpy(row_idx).cuda()
+    hsx = [hs.Hessian(2048, torch.bfloat16) for _ in range(64)]
+    outs = torch.empty((2048, 2048), dtype=torch.float32, device="cuda")
+
+    def moe_once():
+        for h in hsx:
+            h.reset()
+        hs.add_batch_grouped(hsx, x, offsets, ridx)
+        for h in hsx:
+            h.materialize(0.01, out=outs)
+
+    moe_once()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        for h in hsx:
+            h.reset()
+        hs.add_batch_grouped(hsx, x, offsets, ridx)
+    e1.record()
+    torch.cuda.synchronize()
+    grouped_ms = e0.elapsed_time(e1) / steps
+    e0.record()
+    for _ in range(steps):
+        moe_once()
+    e2.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e2) / steps
+    fl = sum(syrk_flops(2048, int(offsets[e + 1] - offsets[e])) for e in range(64))
+    extra["moe_64x2048_grouped"] = {"ms_total": round(total_ms, 3), "ms_reset_plus_grouped": round(grouped_ms, 3),
+                                    "tflops_grouped": round(fl / grouped_ms / 1e9, 1),
+                                    "rows": int(offsets[-1])}
+    for h in hsx:
+        h.close()
+    del x, ridx
+    # local 16x16 blocks: 32768 x 4096 bf16, 16 distinct buffers cycled
+    log("local blocks")
+    gen = W.torch_generator(4, "cuda")
+    sc = W.torch_column_scales(gen, 4096, "cuda")
+    xs = [W.torch_rows(gen, 32768, 4096, sc, "bf16", "cuda") for _ in range(16)]
+    out = torch.zeros((256, 16, 16), dtype=torch.float32, device="cuda")
+    for xx in xs[:2]:
+        hs.local_blocks(xx, out=out)
+    torch.cuda.synchronize()
+    e0.record()
+    reps = 4
+    for _ in range(reps):
+        for xx in xs:
+            hs.local_blocks(xx, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    per = e0.elapsed_time(e1) / (reps * 16)
+    byts = 32768 * 4096 * 2 + 256 * 256 * 4 * 2
+    extra["local_32768x4096"] = {"ms_per_update": round(per, 4), "GBps": round(byts / per / 1e6, 1),
+                                 "hbm_frac": round(byts / (per * 1e-3) / HBM, 4), "pages_rtx_pro_6000_ms": 0.40}
+    del xs
+    torch.cuda.empty_cache()
+    return extra
+
+
+if __name__ == "__main__":
+    main()

@@ -79,7 +79,11 @@ bool vec_ok(const void* p, int64_t ld, int64_t d, int es) {
 constexpr double kSimdRate = 2.1e12;  // sustained bf16 MFMA flop/s per SIMD
 constexpr double kHbm = 6.5e12;       // sustained read+write bytes/s
 constexpr int kCUs = 256;
-constexpr int kFlushIters = 64;       // 4096 tokens per float32 chain
+// K-iterations (64 tokens) per float32 accumulation chain: bf16 products are
+// rounded once per 8 tokens, fp32 split products once per 2 tokens.
+constexpr int kFlushItersBF16 = 64;
+constexpr int kFlushItersF32 = 16;
+int flush_iters(int dtype) { return dtype == HESS_F32 ? kFlushItersF32 : kFlushItersBF16; }
 
 struct Shape {
   int wt;
@@ -260,7 +264,7 @@ int hess_add_batch(hess_t h, const void* X, int64_t n_tokens, int64_t ld, hess_s
   P.ngroups = 1;
   P.ks = pl.ks;
   P.kchunk = (int)std::min<int64_t>(pl.kchunk, 1 << 30);
-  P.flush_iters = kFlushIters;
+  P.flush_iters = flush_iters(h->dtype);
   P.total_items = pl.shape.ntiles * pl.ks;
   P.xcd_contig = 1;
   P.s_vec = (h->d % 4) == 0;
@@ -337,7 +341,7 @@ int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld, 
     P.ngroups = cnt;
     P.ks = 1;
     P.kchunk = 1 << 30;
-    P.flush_iters = kFlushIters;
+    P.flush_iters = flush_iters(h0->dtype);
     P.xcd_contig = 0;
     P.s_vec = (h0->d % 4) == 0;
     P.item_prefix[0] = 0;

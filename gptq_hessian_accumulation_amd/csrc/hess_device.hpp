@@ -34,6 +34,12 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, c
                                                  0, 0);
 }
 
+// v_mfma_f32_32x32x2_f32: lane l supplies A[l%32][k = l/32] and B[k = l/32][l%32];
+// same accumulator layout as the 32x32 bf16 instruction.
+__device__ __forceinline__ f32x16 mfma32x32x2_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                  0, 0);

@@ -17,7 +17,10 @@
 // block's Gram pairs each feature with itself over the same tokens.  Each
 // workgroup adds its 16 blocks into `out` with float32 atomics at the end.
 //
-// float32 inputs are split into hi + lo bf16 planes and use four products.
+// float32 inputs are split into hi + lo bf16 planes.  The hi*hi, the cross
+// (hi*lo + lo*hi) and the lo*lo products go to three separate accumulators,
+// combined smallest first at the end, so the small terms are never rounded
+// against the large accumulator.
 
 #include "hess_device.hpp"
 #include "hess_internal.hpp"
@@ -116,9 +119,13 @@ __device__ __forceinline__ void local_body(const void* Xv, int64_t n, int d, int
     }
   };
 
-  f32x4 acc[4];
+  f32x4 acc[4], accx[4], accl[4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < 4; ++b) {
+    acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accx[b] = acc[b];
+    accl[b] = acc[b];
+  }
 
   // operand addressing: lane l, group g = l/16, i = l%16; rows 8g + 4*half + r
   // supplied by lanes 4r + q at feature column 4q of the block
@@ -140,12 +147,10 @@ __device__ __forceinline__ void local_body(const void* Xv, int64_t n, int d, int
       } else {
         s16x4 l0 = tr_read(stage + kLPlane, off0), l1 = tr_read(stage + kLPlane, off1);
         u32x4 al = __builtin_bit_cast(u32x4, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
-        f32x4 c = acc[bb];
-        c = mfma16x16x32(al, al, c);
-        c = mfma16x16x32(al, a, c);
-        c = mfma16x16x32(a, al, c);
-        c = mfma16x16x32(a, a, c);
-        acc[bb] = c;
+        accl[bb] = mfma16x16x32(al, al, accl[bb]);
+        accx[bb] = mfma16x16x32(al, a, accx[bb]);
+        accx[bb] = mfma16x16x32(a, al, accx[bb]);
+        acc[bb] = mfma16x16x32(a, a, acc[bb]);
       }
     }
   };
@@ -163,6 +168,10 @@ __device__ __forceinline__ void local_body(const void* Xv, int64_t n, int d, int
     __syncthreads();
   }
 
+  if constexpr (IN == kInF32) {
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) acc[bb] = (accl[bb] + accx[bb]) + acc[bb];
+  }
   // register r of lane l holds C[4*(l/16) + r][l%16] of each block
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb) {

@@ -28,10 +28,13 @@
 //    partial tile that a reduction kernel adds into S in a fixed order.
 // Diagonal tiles load one panel and skip the wave below the diagonal.
 //
-// float32 inputs are split into x = hi + lo (two bf16 values, hi = bf16(x),
-// lo = bf16(x - hi)) and multiplied with four bf16 products per pair
-// (hi*hi + hi*lo + lo*hi + lo*lo), which reproduces the float32 products to
-// about 2^-16 relative error.
+// float32 inputs are multiplied on the float32 matrix path
+// (v_mfma_f32_32x32x2_f32, exact products): LDS holds the raw float32 words,
+// [feature][token], and each lane feeds one token per instruction.  Their
+// accumulators are flushed every 1024 tokens.  (A two-term bf16 split of
+// float32 values leaves up to 2^-16 relative error per value, too coarse for
+// float32 parity, and issuing its small lo*lo products as separate
+// instructions rounds them away against the large accumulator.)
 
 #include "hess_device.hpp"
 #include "hess_internal.hpp"
@@ -42,7 +45,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 64;               // tokens per K-iteration
-constexpr int kRowBytes = kBK * 2;    // one feature row of a panel in LDS (64 bf16)
 
 __device__ __forceinline__ int swz(int f) { return (f ^ (f >> 3)) & 7; }
 
@@ -50,9 +52,10 @@ template <int WT, int IN, bool VEC>
 struct SyrkTraits {
   static constexpr int B = 64 * WT;                 // workgroup tile edge
   static constexpr int WTE = 32 * WT;               // wave tile edge
-  static constexpr int PLANES = IN == kInF32 ? 2 : 1;
-  static constexpr int PANEL_BYTES = B * kRowBytes;  // one plane of one panel
-  static constexpr int STAGE_BYTES = 2 * PLANES * PANEL_BYTES;
+  // one feature row of a panel in LDS: 64 tokens of bf16, or of (hi|lo) words
+  static constexpr int ROW_BYTES = IN == kInF32 ? kBK * 4 : kBK * 2;
+  static constexpr int PANEL_BYTES = B * ROW_BYTES;
+  static constexpr int STAGE_BYTES = 2 * PANEL_BYTES;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
   static constexpr int FG = B / 8;                  // 8-feature groups per panel
   static constexpr int UNITS_PER_PANEL = FG * 8;    // x 8 token groups
@@ -68,10 +71,14 @@ struct UnitRegs;
 template <>
 struct UnitRegs<kInBF16> {
   u32x4 row[8];
+  uint32_t rmask;  // bit r: token row r is in range
+  uint32_t cmask;  // bit c: feature c is in range
 };
 template <>
 struct UnitRegs<kInF32> {
   u32x4 row[8][2];
+  uint32_t rmask;
+  uint32_t cmask;
 };
 
 template <int WT, int IN, bool VEC>
@@ -86,50 +93,43 @@ struct SyrkTile {
     fg = r - tg * T::FG;
   }
 
-  // Global -> registers for one unit.  Rows at or past k_end and features at
-  // or past d read as zero.  The vector path (16-byte loads, d % 8 == 0) is
-  // branch-free: out-of-range rows and columns load from a clamped in-range
-  // address and are zeroed by a select.
-  __device__ __forceinline__ static void load_unit(const SyrkParams& P, const int32_t* rows, int64_t k0,
+  // Global -> registers for one unit.  Only issues loads: every address is
+  // clamped into range (last valid token row, last valid feature) and the
+  // validity masks travel with the registers, to be applied when the unit is
+  // stored to LDS; nothing here waits for the loaded data.
+  __device__ __forceinline__ static void load_unit(const SyrkParams& P, const int64_t (&xr)[8], int64_t k0,
                                                    int64_t k_end, int f0, UnitRegs<IN>& R) {
     const char* X = static_cast<const char*>(P.X);
+    uint32_t rm = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) rm |= (k0 + r < k_end) ? (1u << r) : 0u;
+    const int nvalid = P.d - f0;  // features of this unit in range (may be <= 0 or >= 8)
+    R.rmask = nvalid > 0 ? rm : 0u;
+    R.cmask = nvalid >= 8 ? 0xFFu : (nvalid > 0 ? ((1u << nvalid) - 1u) : 0u);
     if constexpr (VEC) {
-      const bool col_ok = f0 < P.d;
-      const int fc = col_ok ? f0 : 0;
+      const int fc = nvalid > 0 ? f0 : 0;  // d % 8 == 0 here: a unit is all in or all out
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const int64_t t = k0 + r;
-        const bool ok = col_ok && t < k_end;
-        const int64_t tc = t < k_end ? t : k_end - 1;
-        const int64_t xrow = rows ? (int64_t)rows[tc] : tc;
-        const u32x4* p = reinterpret_cast<const u32x4*>(X + (xrow * P.ld + fc) * T::ESIZE);
+        const u32x4* p = reinterpret_cast<const u32x4*>(X + (xr[r] * P.ld + fc) * T::ESIZE);
         if constexpr (IN == kInBF16) {
-          const u32x4 v = *p;
-          R.row[r] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+          R.row[r] = *p;
         } else {
-          const u32x4 v0 = p[0], v1 = p[1];
-          R.row[r][0] = ok ? v0 : u32x4{0u, 0u, 0u, 0u};
-          R.row[r][1] = ok ? v1 : u32x4{0u, 0u, 0u, 0u};
+          R.row[r][0] = p[0];
+          R.row[r][1] = p[1];
         }
       }
     } else {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const int64_t t = k0 + r;
-        const bool tok_ok = t < k_end;
-        int64_t xrow = 0;
-        if (tok_ok) xrow = rows ? (int64_t)rows[t] : t;
-        const char* rowp = X + (xrow * P.ld + f0) * T::ESIZE;
+        const char* rowp = X + xr[r] * P.ld * T::ESIZE;
         uint32_t w[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          w[c] = 0u;
-          if (tok_ok && f0 + c < P.d) {
-            if constexpr (IN == kInBF16)
-              w[c] = reinterpret_cast<const uint16_t*>(rowp)[c];
-            else
-              w[c] = reinterpret_cast<const uint32_t*>(rowp)[c];
-          }
+          const int fcl = min(f0 + c, P.d - 1);
+          if constexpr (IN == kInBF16)
+            w[c] = reinterpret_cast<const uint16_t*>(rowp)[fcl];
+          else
+            w[c] = reinterpret_cast<const uint32_t*>(rowp)[fcl];
         }
         if constexpr (IN == kInBF16) {
           R.row[r] = u32x4{w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16)};
@@ -141,47 +141,78 @@ struct SyrkTile {
     }
   }
 
-  // Registers -> LDS for one unit: 8 feature rows of 8 tokens (16 bytes).
-  __device__ __forceinline__ static void store_unit(char* stage, int p, int tg, int fg, const UnitRegs<IN>& R) {
-    if constexpr (IN == kInBF16) {
-      u32x4 col[8];
-      transpose8x8_b16(R.row, col);
-      char* panel = stage + p * T::PANEL_BYTES;
+  // Token rows k0 .. k0+7 clamped into range, as row numbers of X (through
+  // the gather index when there is one).
+  __device__ __forceinline__ static void fetch_rows(const int32_t* rows, int64_t k0, int64_t k_end,
+                                                    int32_t (&g)[8]) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int f = fg * 8 + i;
-        *reinterpret_cast<u32x4*>(panel + f * kRowBytes + ((tg ^ swz(f)) << 4)) = col[i];
-      }
-    } else {
-      u32x4 hi[8], lo[8];
+    for (int r = 0; r < 8; ++r) {
+      const int64_t t = k0 + r;
+      const int64_t tc = t < k_end ? t : k_end - 1;
+      g[r] = rows ? rows[tc] : 0;
+    }
+  }
+
+  // Registers -> LDS for one unit: apply the validity masks, then write the
+  // unit's 8 feature rows.  bf16: transpose the 8 x 8 block of 16-bit values;
+  // a feature's 8 tokens are one 16-byte chunk.  fp32: a feature's 8 tokens
+  // are two 16-byte chunks.  Chunk c of feature row f sits at chunk c ^ swz(f).
+  __device__ __forceinline__ static void store_unit(char* stage, int p, int tg, int fg, const UnitRegs<IN>& R) {
+    char* panel = stage + p * T::PANEL_BYTES;
+    if constexpr (IN == kInBF16) {
+      // 16-bit lane masks of the 8 columns: dword q holds columns 2q, 2q+1
+      uint32_t cm[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        cm[q] = ((R.cmask >> (2 * q)) & 1u ? 0x0000FFFFu : 0u) | ((R.cmask >> (2 * q + 1)) & 1u ? 0xFFFF0000u : 0u);
+      u32x4 rowm[8];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        uint32_t h[8], l[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) split_bf16(__uint_as_float(R.row[r][c >> 2][c & 3]), h[c], l[c]);
-        hi[r] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-        lo[r] = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+        const uint32_t rr = (R.rmask >> r) & 1u ? 0xFFFFFFFFu : 0u;
+        rowm[r] = u32x4{R.row[r][0] & cm[0] & rr, R.row[r][1] & cm[1] & rr, R.row[r][2] & cm[2] & rr,
+                        R.row[r][3] & cm[3] & rr};
       }
-      u32x4 colh[8], coll[8];
-      transpose8x8_b16(hi, colh);
-      transpose8x8_b16(lo, coll);
-      char* panel_hi = stage + (2 * p) * T::PANEL_BYTES;
-      char* panel_lo = stage + (2 * p + 1) * T::PANEL_BYTES;
+      u32x4 col[8];
+      transpose8x8_b16(rowm, col);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int f = fg * 8 + i;
-        const int off = f * kRowBytes + ((tg ^ swz(f)) << 4);
-        *reinterpret_cast<u32x4*>(panel_hi + off) = colh[i];
-        *reinterpret_cast<u32x4*>(panel_lo + off) = coll[i];
+        *reinterpret_cast<u32x4*>(panel + f * T::ROW_BYTES + ((tg ^ swz(f)) << 4)) = col[i];
+      }
+    } else {
+      uint32_t w[8][8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const bool ok = ((R.rmask >> r) & 1u) && ((R.cmask >> c) & 1u);
+          w[r][c] = ok ? R.row[r][c >> 2][c & 3] : 0u;
+        }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int f = fg * 8 + i;
+        char* row = panel + f * T::ROW_BYTES;
+        *reinterpret_cast<u32x4*>(row + (((2 * tg) ^ swz(f)) << 4)) = u32x4{w[0][i], w[1][i], w[2][i], w[3][i]};
+        *reinterpret_cast<u32x4*>(row + (((2 * tg + 1) ^ swz(f)) << 4)) = u32x4{w[4][i], w[5][i], w[6][i], w[7][i]};
       }
     }
   }
 
-  // Operand for the 32 features [f0, f0+32) of a plane, K16 step h (tokens 16h..16h+15).
-  __device__ __forceinline__ static u32x4 read_operand(const char* plane, int f0, int h, int lane) {
+  // bf16 operand for the 32 features [f0, f0+32), K16 step h (tokens 16h..16h+15).
+  __device__ __forceinline__ static u32x4 read_operand(const char* panel, int f0, int h, int lane) {
     const int f = f0 + (lane & 31);
     const int c = 2 * h + (lane >> 5);
-    return *reinterpret_cast<const u32x4*>(plane + f * kRowBytes + ((c ^ swz(f)) << 4));
+    return *reinterpret_cast<const u32x4*>(panel + f * T::ROW_BYTES + ((c ^ swz(f)) << 4));
+  }
+
+  // fp32: the words of tokens 16h + 8*(lane/32) + 0..7 of feature f0 + lane%32.
+  __device__ __forceinline__ static void read_words(const char* panel, int f0, int h, int lane, u32x4& w0,
+                                                    u32x4& w1) {
+    const int f = f0 + (lane & 31);
+    const int c = 4 * h + 2 * (lane >> 5);
+    const char* row = panel + f * T::ROW_BYTES;
+    w0 = *reinterpret_cast<const u32x4*>(row + ((c ^ swz(f)) << 4));
+    w1 = *reinterpret_cast<const u32x4*>(row + (((c + 1) ^ swz(f)) << 4));
   }
 };
 
@@ -238,6 +269,20 @@ __device__ __forceinline__ void syrk_body(const SyrkParams& P, char* lds) {
   const int units = npanels * T::UNITS_PER_PANEL;
   UnitRegs<IN> R[T::UPT];
 
+  // gather indices are fetched one K-iteration ahead of the rows they name
+  int32_t gidx[T::UPT][8];
+  auto fetch_iter = [&](int it) {
+    if (!rows) return;
+#pragma unroll
+    for (int q = 0; q < T::UPT; ++q) {
+      const int u = tid + q * kThreads;
+      if (u < units) {
+        int p, tg, fg;
+        K::unit_coords(u, p, tg, fg);
+        K::fetch_rows(rows, k_begin + (int64_t)it * kBK + tg * 8, k_end, gidx[q]);
+      }
+    }
+  };
   auto load_iter = [&](int it) {
 #pragma unroll
     for (int q = 0; q < T::UPT; ++q) {
@@ -246,7 +291,14 @@ __device__ __forceinline__ void syrk_body(const SyrkParams& P, char* lds) {
         int p, tg, fg;
         K::unit_coords(u, p, tg, fg);
         const int f0 = (p == 0 ? fa0 : fb0) + fg * 8;
-        K::load_unit(P, rows, k_begin + (int64_t)it * kBK + tg * 8, k_end, f0, R[q]);
+        const int64_t k0 = k_begin + (int64_t)it * kBK + tg * 8;
+        int64_t xr[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int64_t tc = k0 + r < k_end ? k0 + r : k_end - 1;
+          xr[r] = rows ? (int64_t)gidx[q][r] : tc;
+        }
+        K::load_unit(P, xr, k0, k_end, f0, R[q]);
       }
     }
   };
@@ -264,7 +316,7 @@ __device__ __forceinline__ void syrk_body(const SyrkParams& P, char* lds) {
   auto compute_iter = [&](const char* stage) {
     if (!wave_active) return;
     const char* pa = stage;
-    const char* pb = diag ? stage : stage + T::PLANES * T::PANEL_BYTES;
+    const char* pb = diag ? stage : stage + T::PANEL_BYTES;
     const int fa = wr * T::WTE, fb = wc * T::WTE;
 #pragma unroll
     for (int h = 0; h < kBK / 16; ++h) {
@@ -279,28 +331,22 @@ __device__ __forceinline__ void syrk_body(const SyrkParams& P, char* lds) {
 #pragma unroll
           for (int j = 0; j < WT; ++j) acc[i * WT + j] = mfma32x32x16(b[j], a[i], acc[i * WT + j]);
       } else {
-        u32x4 ah[WT], al[WT], bh[WT], bl[WT];
+        u32x4 a0[WT], a1[WT], b0[WT], b1[WT];
 #pragma unroll
-        for (int i = 0; i < WT; ++i) {
-          ah[i] = K::read_operand(pa, fa + 32 * i, h, lane);
-          al[i] = K::read_operand(pa + T::PANEL_BYTES, fa + 32 * i, h, lane);
-        }
+        for (int i = 0; i < WT; ++i) K::read_words(pa, fa + 32 * i, h, lane, a0[i], a1[i]);
 #pragma unroll
-        for (int j = 0; j < WT; ++j) {
-          bh[j] = K::read_operand(pb, fb + 32 * j, h, lane);
-          bl[j] = K::read_operand(pb + T::PANEL_BYTES, fb + 32 * j, h, lane);
-        }
+        for (int j = 0; j < WT; ++j) K::read_words(pb, fb + 32 * j, h, lane, b0[j], b1[j]);
+        // instruction s: lanes 0-31 multiply token 16h + s, lanes 32-63 token 16h + 8 + s
 #pragma unroll
-        for (int i = 0; i < WT; ++i)
+        for (int s = 0; s < 8; ++s)
 #pragma unroll
-          for (int j = 0; j < WT; ++j) {
-            f32x16 c = acc[i * WT + j];
-            c = mfma32x32x16(bl[j], al[i], c);
-            c = mfma32x32x16(bh[j], al[i], c);
-            c = mfma32x32x16(bl[j], ah[i], c);
-            c = mfma32x32x16(bh[j], ah[i], c);
-            acc[i * WT + j] = c;
-          }
+          for (int i = 0; i < WT; ++i)
+#pragma unroll
+            for (int j = 0; j < WT; ++j) {
+              const float av = __uint_as_float(s < 4 ? a0[i][s] : a1[i][s - 4]);
+              const float bv = __uint_as_float(s < 4 ? b0[j][s] : b1[j][s - 4]);
+              acc[i * WT + j] = mfma32x32x2_f32(bv, av, acc[i * WT + j]);
+            }
       }
     }
   };
@@ -314,7 +360,9 @@ __device__ __forceinline__ void syrk_body(const SyrkParams& P, char* lds) {
 
   // ---- K loop: two LDS stages, registers prefetch one iteration ahead ----
   if (niter > 0) {
+    fetch_iter(0);
     load_iter(0);
+    if (niter > 1) fetch_iter(1);
     store_iter(lds);
     __syncthreads();
     for (int it = 0; it < niter; ++it) {
@@ -322,6 +370,7 @@ __device__ __forceinline__ void syrk_body(const SyrkParams& P, char* lds) {
       char* nxt = lds + ((it + 1) & 1) * T::STAGE_BYTES;
       const bool more = it + 1 < niter;
       if (more) load_iter(it + 1);
+      if (it + 2 < niter) fetch_iter(it + 2);
       compute_iter(cur);
       if (more) store_iter(nxt);
       if (P.flush_iters > 0 && ((it + 1) % P.flush_iters) == 0) flush();
@@ -417,7 +466,7 @@ __global__ void __launch_bounds__(256) syrk_reduce_kernel(float* S, int64_t lds,
   }
 
 HESS_SYRK_KERNEL(syrk_bf16_wt2_vec, 2, kInBF16, true, 2)
-HESS_SYRK_KERNEL(syrk_bf16_wt2_gen, 2, kInBF16, false, 2)
+HESS_SYRK_KERNEL(syrk_bf16_wt2_gen, 2, kInBF16, false, 1)
 HESS_SYRK_KERNEL(syrk_f32_wt2_vec, 2, kInF32, true, 1)
 HESS_SYRK_KERNEL(syrk_f32_wt2_gen, 2, kInF32, false, 1)
 
