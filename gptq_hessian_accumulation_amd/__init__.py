@@ -30,6 +30,7 @@ __all__ = [
     "local_blocks",
     "add_batch_grouped",
     "set_tile_override",
+    "set_staging",
     "library_path",
     "exported_symbols",
 ]
@@ -83,6 +84,8 @@ def _load():
         "hess_reset": (c_int, [vp, vp]),
         "hess_token_count": (c_int, [vp, ctypes.POINTER(i64)]),
         "hess_set_tile_override": (c_int, [c_int]),
+        "hess_set_staging": (c_int, [c_int]),
+        "hess_flush": (c_int, [vp, vp]),
         "hess_info": (c_int, [vp, ctypes.POINTER(i64), ctypes.POINTER(c_int)]),
         "hess_state_buffer": (c_int, [vp, ctypes.POINTER(vp)]),
         "hess_local_blocks": (c_int, [vp, i64, i64, c_int, vp]),
@@ -133,6 +136,11 @@ def _as_rows(x: torch.Tensor, d: int):
         x2 = x2.contiguous()
     ld = x2.stride(0) if x2.shape[0] > 1 else d
     return x2, x2.shape[0], max(ld, d)
+
+
+def set_staging(enable: bool) -> None:
+    """Enable (default) or disable the staging of short batches; process-wide."""
+    _check(_load().hess_set_staging(1 if enable else 0))
 
 
 def set_tile_override(edge: int) -> None:
@@ -199,8 +207,15 @@ class Hessian:
         _check(_load().hess_state_buffer(self._h, ctypes.byref(p)))
         return p.value
 
+    def flush(self, stream=None) -> None:
+        """Fold staged short batches into the Gram sum."""
+        _check(_load().hess_flush(self._h, _stream(stream)))
+
     def state_tensor(self) -> torch.Tensor:
-        """A (d, d) float32 view of the accumulator's device buffer (S, or H after an in-place materialize)."""
+        """A (d, d) float32 view of the accumulator's device buffer (S, or H after an in-place materialize).
+
+        Call flush() first when reading S, so that staged batches are included.
+        """
         ptr, d = self.state_buffer_ptr(), self.d
 
         class _View:

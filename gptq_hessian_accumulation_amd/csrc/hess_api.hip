@@ -31,6 +31,10 @@ struct hess_s {
   float* damp = nullptr;     // 1 float
   float* ws = nullptr;       // split partials (may be null)
   int64_t ws_floats = 0;
+  void* stage = nullptr;     // thin-batch staging rows (stage_cap x stage_ld elements)
+  int64_t stage_cap = 0;     // tokens
+  int64_t stage_ld = 0;      // row stride in elements (d rounded up to 8)
+  int64_t stage_n = 0;       // tokens staged, not yet in S
   int64_t N = 0;
   bool consumed = false;     // in-place materialize done
   bool has_stream = false;
@@ -41,7 +45,8 @@ struct hess_s {
 namespace {
 
 thread_local char g_err[512] = "";
-int g_tile_override = 0;  // 0 = automatic; 128 or 192 forces a SYRK tile edge
+int g_tile_override = 0;  // 0 = automatic; 128 forces the 128-edge SYRK tiles
+bool g_staging = true;    // thin-batch staging enabled (process-wide)
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -70,84 +75,116 @@ int order_stream(hess_t h, hipStream_t s) {
 
 int esize(int dtype) { return dtype == HESS_F32 ? 4 : 2; }
 
-// 16-byte row loads need X and every row start 16-byte aligned and whole
-// 16-byte chunks of features (d a multiple of 8 elements).
+// The vectorized loaders read whole units of 8 features with 16-byte loads:
+// X and every row start 16-byte aligned, d a multiple of 8, and 64 rows of
+// the stride addressable with 32-bit buffer offsets.
 bool vec_ok(const void* p, int64_t ld, int64_t d, int es) {
-  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0 && ((ld * es) & 15) == 0 && ((d * es) & 15) == 0;
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0 && ((ld * es) & 15) == 0 && (d % 8) == 0 &&
+         ld * es * 64 < ((int64_t)1 << 31);
 }
 
-constexpr double kSimdRate = 2.1e12;  // sustained bf16 MFMA flop/s per SIMD
-constexpr double kHbm = 6.5e12;       // sustained read+write bytes/s
-constexpr int kCUs = 256;
+constexpr int kCUs = 256;       // MI355X compute units: one SYRK workgroup each
+constexpr int kTile = 128;      // SYRK tile edge
+constexpr int64_t kWsSlots = 256;  // tail partial tiles a handle can hold
 // K-iterations (64 tokens) per float32 accumulation chain: bf16 products are
-// rounded once per 8 tokens, fp32 split products once per 2 tokens.
+// rounded once per 8 tokens, float32 products once per 2 tokens.
 constexpr int kFlushItersBF16 = 64;
 constexpr int kFlushItersF32 = 16;
 int flush_iters(int dtype) { return dtype == HESS_F32 ? kFlushItersF32 : kFlushItersBF16; }
 
-struct Shape {
-  int wt;
-  int B;
-  int nb;
-  int ntiles;
-};
+int grid8(int64_t items) { return (int)(((items + 7) / 8) * 8); }
 
-Shape make_shape(int64_t d, int wt) {
-  Shape s;
-  s.wt = wt;
-  s.B = syrk_tile_edge(wt);
-  s.nb = (int)((d + s.B - 1) / s.B);
-  s.ntiles = s.nb * (s.nb + 1) / 2;
-  return s;
-}
-
-// Estimated time of one update of width d over `tokens` tokens split into
-// `items` workgroups per tile set; a simple model (matrix-core time per
-// workgroup round, S read-modify-write traffic) used only to pick a shape.
-double estimate(const Shape& s, int64_t items, double tokens_per_item, int dtype) {
-  const double eff = s.wt == 3 ? 0.85 : 0.6;
-  const double mult = dtype == HESS_F32 ? 4.0 : 1.0;
-  const double wave_tile = 32.0 * s.wt;
-  const double t_wg = mult * 2.0 * wave_tile * wave_tile * tokens_per_item / (kSimdRate * eff);
-  const double rounds = std::ceil((double)items / kCUs);
-  const double compute = rounds * t_wg;
-  const double mem = (double)s.ntiles * s.B * s.B * 8.0 / kHbm;
-  return std::max(compute, mem) + 0.25 * std::min(compute, mem);
-}
-
+// Work split of one batch of n tokens over the upper-triangle 128-tiles:
+// whole tiles fill complete rounds of one workgroup per CU; tiles left for a
+// last, partly empty round (or all tiles, when there are fewer tiles than
+// CUs) are split into token ranges so that round is full, when the batch is
+// long enough for the partials' extra traffic to pay off.
 struct Plan {
-  Shape shape;
-  int ks;
-  int64_t kchunk;
+  int nb, ntiles, full_tiles, tail_parts, tail_kchunk, grid_full, grid;
 };
 
-Plan plan_single(hess_t h, int64_t n, bool vec) {
-  std::vector<int> wts;
-  (void)vec;
-  wts = {2};
-  Plan best{};
-  double best_t = 1e30;
-  for (int wt : wts) {
-    Shape s = make_shape(h->d, wt);
-    // token splits: only for few tiles and long batches, within the workspace
-    int ks_max = 1;
-    if (h->ws && wt == 2 && n >= 8192) {
-      const int64_t tile_floats = (int64_t)s.B * s.B;
-      ks_max = (int)std::min<int64_t>(8, h->ws_floats / ((int64_t)s.ntiles * tile_floats));
-      ks_max = std::min<int64_t>(ks_max, std::max<int64_t>(1, n / 4096));
-    }
-    for (int ks = 1; ks <= std::max(1, ks_max); ++ks) {
-      const int64_t kchunk = ((n + ks - 1) / ks + 63) / 64 * 64;
-      const int ks_eff = (int)((n + kchunk - 1) / kchunk);
-      double t = estimate(s, (int64_t)s.ntiles * ks_eff, (double)kchunk, h->dtype);
-      if (ks_eff > 1) t += 2.0 * ks_eff * s.ntiles * s.B * s.B * 4.0 / kHbm;  // partial write + read
-      if (t < best_t) {
-        best_t = t;
-        best = Plan{s, ks_eff, kchunk};
-      }
+Plan plan_single(int64_t d, int64_t n, bool have_ws) {
+  Plan p{};
+  p.nb = (int)((d + kTile - 1) / kTile);
+  p.ntiles = p.nb * (p.nb + 1) / 2;
+  p.full_tiles = p.ntiles;
+  p.tail_parts = 0;
+  p.tail_kchunk = 0;
+  const int full_rounds = p.ntiles / kCUs;
+  const int tail = p.ntiles - full_rounds * kCUs;
+  if (have_ws && tail > 0) {
+    int parts = kCUs / tail;
+    parts = (int)std::min<int64_t>(parts, n / 1024);               // >= 1024 tokens per part
+    parts = (int)std::min<int64_t>(parts, kWsSlots / tail);         // workspace capacity
+    if (parts >= 2) {
+      const int64_t kchunk = ((n + parts - 1) / parts + 63) / 64 * 64;
+      p.full_tiles = full_rounds * kCUs;
+      p.tail_kchunk = (int)kchunk;
+      p.tail_parts = (int)((n + kchunk - 1) / kchunk);
     }
   }
-  return best;
+  p.grid_full = grid8(p.full_tiles);
+  p.grid = p.grid_full;
+  if (p.tail_parts > 0) p.grid += grid8((int64_t)(p.ntiles - p.full_tiles) * p.tail_parts);
+  return p;
+}
+
+// Staging buffer: 64 MiB of rows per handle (a multiple of 64 tokens).
+constexpr int64_t kStageBytes = (int64_t)64 << 20;
+
+int64_t stage_tokens(int64_t d, int es) {
+  const int64_t row = ((d + 7) / 8 * 8) * es;
+  int64_t cap = kStageBytes / row / 64 * 64;
+  return cap >= 256 ? cap : 0;
+}
+
+// A batch goes through the staging buffer when that moves fewer bytes than a
+// pass over the upper-triangle sum: 2 n d esize (copy in and read back) is
+// below 4 d^2, i.e. n < 2 d / esize.
+bool stage_pays(const hess_s* h, int64_t n) {
+  return g_staging && h->stage && n <= h->stage_cap && n * esize(h->dtype) < 2 * h->d;
+}
+
+// One SYRK pass of n rows of X into S, on stream s (already ordered).
+int run_syrk(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s) {
+  const bool vec = vec_ok(X, ld, h->d, esize(h->dtype));
+  const Plan pl = plan_single(h->d, n, h->ws != nullptr);
+  SyrkParams P;
+  std::memset(&P, 0, sizeof(P));
+  P.X = X;
+  P.rows = nullptr;
+  P.ld = ld;
+  P.lds = h->d;
+  P.ws = h->ws;
+  P.d = (int)h->d;
+  P.nb = pl.nb;
+  P.ntiles = pl.ntiles;
+  P.ngroups = 1;
+  P.flush_iters = flush_iters(h->dtype);
+  P.full_tiles = pl.full_tiles;
+  P.tail_parts = pl.tail_parts;
+  P.tail_kchunk = pl.tail_kchunk;
+  P.grid_full = pl.grid_full;
+  P.s_vec = (h->d % 4) == 0;
+  P.item_prefix[0] = 0;
+  P.item_prefix[1] = pl.ntiles;
+  P.g[0] = SyrkGroup{h->S, 0, n};
+  hipError_t e = launch_syrk(P, h->dtype, vec, pl.grid, s);
+  if (e != hipSuccess) return hip_fail(e, "SYRK launch");
+  if (pl.tail_parts > 0) {
+    e = launch_syrk_reduce(h->S, h->d, h->ws, (int)h->d, pl.nb, pl.full_tiles, pl.ntiles - pl.full_tiles,
+                           pl.tail_parts, s);
+    if (e != hipSuccess) return hip_fail(e, "split reduction launch");
+  }
+  return HESS_OK;
+}
+
+// Fold the staged rows into S.
+int flush_stage(hess_t h, hipStream_t s) {
+  if (h->stage_n == 0) return HESS_OK;
+  const int rc = run_syrk(h, h->stage, h->stage_n, h->stage_ld, s);
+  if (rc == HESS_OK) h->stage_n = 0;
+  return rc;
 }
 
 }  // namespace
@@ -171,7 +208,7 @@ const char* hess_strerror(int code) {
 const char* hess_last_error(void) { return g_err; }
 
 int hess_set_tile_override(int edge) {
-  if (edge != 0 && edge != 128 && edge != 192) return fail(HESS_EINVAL, "tile override must be 0, 128 or 192");
+  if (edge != 0 && edge != 128) return fail(HESS_EINVAL, "tile override must be 0 or 128");
   g_tile_override = edge;
   return HESS_OK;
 }
@@ -197,14 +234,16 @@ hess_t hess_create(int64_t d, int in_dtype) {
   if (e == hipSuccess) e = hipMalloc(&h->S, sbytes);
   if (e == hipSuccess) e = hipMalloc(&h->dead, (size_t)d);
   if (e == hipSuccess) e = hipMalloc(&h->damp, 64);
-  // split workspace: only widths whose 128-edge tile count is small enough
-  // to need token splits (256 partial tiles of 128 x 128 floats at most)
+  // workspace for the partial tiles of a split last round
   if (e == hipSuccess) {
-    const Shape s = make_shape(d, 2);
-    if (s.ntiles < 160) {
-      h->ws_floats = (int64_t)256 * 128 * 128;
-      e = hipMalloc(&h->ws, (size_t)h->ws_floats * sizeof(float));
-    }
+    h->ws_floats = kWsSlots * kTile * kTile;
+    e = hipMalloc(&h->ws, (size_t)h->ws_floats * sizeof(float));
+  }
+  // staging rows for thin batches
+  if (e == hipSuccess) {
+    h->stage_cap = stage_tokens(d, esize(in_dtype));
+    h->stage_ld = (d + 7) / 8 * 8;
+    if (h->stage_cap > 0) e = hipMalloc(&h->stage, (size_t)(h->stage_cap * h->stage_ld * esize(in_dtype)));
   }
   if (e == hipSuccess) e = hipMemset(h->S, 0, sbytes);
   if (e == hipSuccess) e = hipMemset(h->damp, 0, 64);
@@ -218,6 +257,7 @@ hess_t hess_create(int64_t d, int in_dtype) {
     if (h->dead) (void)hipFree(h->dead);
     if (h->damp) (void)hipFree(h->damp);
     if (h->ws) (void)hipFree(h->ws);
+    if (h->stage) (void)hipFree(h->stage);
     if (h->ev) (void)hipEventDestroy(h->ev);
     delete h;
     return nullptr;
@@ -233,6 +273,7 @@ int hess_destroy(hess_t h) {
   (void)hipFree(h->dead);
   (void)hipFree(h->damp);
   if (h->ws) (void)hipFree(h->ws);
+  if (h->stage) (void)hipFree(h->stage);
   (void)hipEventDestroy(h->ev);
   delete h;
   return e == hipSuccess ? HESS_OK : hip_fail(e, "hess_destroy");
@@ -247,35 +288,24 @@ int hess_add_batch(hess_t h, const void* X, int64_t n_tokens, int64_t ld, hess_s
   if (!X) return fail(HESS_EINVAL, "X is NULL with n_tokens > 0");
   if (reinterpret_cast<uintptr_t>(X) % esize(h->dtype) != 0) return fail(HESS_EALIGN, "X not element-aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool vec = vec_ok(X, ld, h->d, esize(h->dtype));
-  const Plan pl = plan_single(h, n_tokens, vec);
   int rc = order_stream(h, s);
   if (rc != HESS_OK) return rc;
-
-  SyrkParams P;
-  std::memset(&P, 0, sizeof(P));
-  P.X = X;
-  P.rows = nullptr;
-  P.ld = ld;
-  P.lds = h->d;
-  P.d = (int)h->d;
-  P.nb = pl.shape.nb;
-  P.ntiles = pl.shape.ntiles;
-  P.ngroups = 1;
-  P.ks = pl.ks;
-  P.kchunk = (int)std::min<int64_t>(pl.kchunk, 1 << 30);
-  P.flush_iters = flush_iters(h->dtype);
-  P.total_items = pl.shape.ntiles * pl.ks;
-  P.xcd_contig = 1;
-  P.s_vec = (h->d % 4) == 0;
-  P.item_prefix[0] = 0;
-  P.item_prefix[1] = P.total_items;
-  P.g[0] = SyrkGroup{h->S, h->ws, 0, n_tokens};
-  hipError_t e = launch_syrk(P, pl.shape.wt, h->dtype, vec, s);
-  if (e != hipSuccess) return hip_fail(e, "SYRK launch");
-  if (pl.ks > 1) {
-    e = launch_syrk_reduce(h->S, h->d, h->ws, (int)h->d, pl.shape.B, pl.shape.nb, pl.shape.ntiles, pl.ks, s);
-    if (e != hipSuccess) return hip_fail(e, "split reduction launch");
+  if (stage_pays(h, n_tokens)) {
+    // thin batch: append its rows to the staging buffer
+    if (h->stage_n + n_tokens > h->stage_cap) {
+      rc = flush_stage(h, s);
+      if (rc != HESS_OK) return rc;
+    }
+    char* dst = static_cast<char*>(h->stage) + h->stage_n * h->stage_ld * esize(h->dtype);
+    hipError_t e = launch_copy_rows(X, ld, esize(h->dtype), n_tokens, h->d, dst, h->stage_ld, s);
+    if (e != hipSuccess) return hip_fail(e, "staging copy launch");
+    h->stage_n += n_tokens;
+  } else {
+    // long batch: its own SYRK pass, after whatever is staged
+    rc = flush_stage(h, s);
+    if (rc != HESS_OK) return rc;
+    rc = run_syrk(h, X, n_tokens, ld, s);
+    if (rc != HESS_OK) return rc;
   }
   h->N += n_tokens;
   return HESS_OK;
@@ -309,19 +339,9 @@ int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld, 
     if (rc != HESS_OK) return rc;
   }
   const bool vec = vec_ok(X, ld, h0->d, esize(h0->dtype));
-  // one shape for every group: pick it for the mean group length
-  int nonempty = 0;
-  for (int e = 0; e < n_groups; ++e) nonempty += offsets[e + 1] > offsets[e];
-  const double mean_rows = (double)total / std::max(1, nonempty);
-  int wt = 2;
-  if (false) {
-    const Shape s2 = make_shape(h0->d, 2), s3 = make_shape(h0->d, 3);
-    const double t2 = estimate(s2, (int64_t)s2.ntiles * nonempty, mean_rows, h0->dtype);
-    const double t3 = estimate(s3, (int64_t)s3.ntiles * nonempty, mean_rows, h0->dtype);
-    wt = (g_tile_override == 192 || t3 < t2) ? 3 : 2;
-  }
-  const Shape sh = make_shape(h0->d, wt);
-  // longest groups first, so the longest workgroups start in the first round
+  const int nb = (int)((h0->d + kTile - 1) / kTile);
+  const int ntiles = nb * (nb + 1) / 2;
+  // longest groups first, so their workgroups start in the first round
   std::vector<int> order;
   for (int e = 0; e < n_groups; ++e)
     if (offsets[e + 1] > offsets[e]) order.push_back(e);
@@ -336,22 +356,21 @@ int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld, 
     P.ld = ld;
     P.lds = h0->d;
     P.d = (int)h0->d;
-    P.nb = sh.nb;
-    P.ntiles = sh.ntiles;
+    P.nb = nb;
+    P.ntiles = ntiles;
     P.ngroups = cnt;
-    P.ks = 1;
-    P.kchunk = 1 << 30;
     P.flush_iters = flush_iters(h0->dtype);
-    P.xcd_contig = 0;
+    P.full_tiles = ntiles;
+    P.grid_full = grid8(ntiles);
     P.s_vec = (h0->d % 4) == 0;
     P.item_prefix[0] = 0;
     for (int k = 0; k < cnt; ++k) {
       const int e = order[base + k];
-      P.g[k] = SyrkGroup{hs[e]->S, nullptr, offsets[e], offsets[e + 1]};
-      P.item_prefix[k + 1] = P.item_prefix[k] + sh.ntiles;
+      P.g[k] = SyrkGroup{hs[e]->S, offsets[e], offsets[e + 1]};
+      P.item_prefix[k + 1] = P.item_prefix[k] + ntiles;
     }
-    P.total_items = P.item_prefix[cnt];
-    hipError_t err = launch_syrk(P, wt, h0->dtype, vec, s);
+    const int grid = cnt > 1 ? P.item_prefix[cnt] : P.grid_full;
+    hipError_t err = launch_syrk(P, h0->dtype, vec, grid, s);
     if (err != hipSuccess) return hip_fail(err, "grouped SYRK launch");
   }
   for (int e = 0; e < n_groups; ++e) hs[e]->N += offsets[e + 1] - offsets[e];
@@ -368,6 +387,8 @@ int hess_materialize_ex(hess_t h, float damp_percent, unsigned flags, float* H_o
   if (H_out == h->S) return fail(HESS_EINVAL, "H_out aliases the Gram buffer; pass NULL for in place");
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = order_stream(h, s);
+  if (rc != HESS_OK) return rc;
+  rc = flush_stage(h, s);
   if (rc != HESS_OK) return rc;
   const float scale = h->N > 0 ? (float)(2.0 / (double)h->N) : 0.0f;
   float* H = H_out ? H_out : h->S;
@@ -393,8 +414,23 @@ int hess_reset(hess_t h, hess_stream_t stream) {
   if (rc != HESS_OK) return rc;
   hipError_t e = launch_zero(h->S, h->d * h->d, s);
   if (e != hipSuccess) return hip_fail(e, "reset launch");
+  h->stage_n = 0;
   h->N = 0;
   h->consumed = false;
+  return HESS_OK;
+}
+
+int hess_flush(hess_t h, hess_stream_t stream) {
+  if (!h) return fail(HESS_EINVAL, "null handle");
+  if (h->consumed) return fail(HESS_ESTATE, "handle was materialized in place; hess_reset it first");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = order_stream(h, s);
+  if (rc != HESS_OK) return rc;
+  return flush_stage(h, s);
+}
+
+int hess_set_staging(int enable) {
+  g_staging = enable != 0;
   return HESS_OK;
 }
 

@@ -13,34 +13,41 @@ constexpr int kMaxGroups = 64;  // Hessians per grouped launch
 
 struct SyrkGroup {
   float* S;           // d x d float32 Gram sum (row stride SyrkParams::lds)
-  float* ws;          // split-partial workspace (split launches only)
   int64_t row_begin;  // this group's token rows: [row_begin, row_end) of X, or of rows[]
   int64_t row_end;
 };
 
+// One SYRK launch.  Single Hessian (ngroups == 1): the first full_tiles
+// upper-triangle tiles (row-major order) are each done whole by one
+// workgroup, in grid_full workgroups (a multiple of 8, mapped XCD by XCD);
+// the remaining tiles are split into tail_parts token ranges of tail_kchunk
+// tokens whose partials go to ws and are added by launch_syrk_reduce.
+// Grouped (ngroups > 1): group e owns items [item_prefix[e], item_prefix[e+1]),
+// one whole tile each.
 struct SyrkParams {
   const void* X;        // tokens x features, row stride ld elements
   const int32_t* rows;  // gather: token t of a group is X row rows[t]; nullptr = identity
   int64_t ld;
   int64_t lds;          // row stride of S
+  float* ws;            // tail partials, 128 x 128 floats per (tile, part)
   int d;
-  int nb;               // tile rows per dimension, ceil(d / B)
+  int nb;               // tile rows per dimension, ceil(d / 128)
   int ntiles;           // nb (nb + 1) / 2 upper-triangle tiles
   int ngroups;
-  int ks;               // token splits per tile (1 = add straight into S)
-  int kchunk;           // tokens per split (multiple of 64)
   int flush_iters;      // K-iterations between accumulator flushes
-  int total_items;
-  int xcd_contig;       // map contiguous item ranges to one XCD
-  int s_vec;            // S rows 16-byte aligned (float4 epilogue)
+  int full_tiles;
+  int tail_parts;
+  int tail_kchunk;      // multiple of 64
+  int grid_full;
+  int s_vec;            // S rows 16-byte aligned (float4 read-modify-write)
   int item_prefix[kMaxGroups + 1];
   SyrkGroup g[kMaxGroups];
 };
 
-int syrk_tile_edge(int wt);
-hipError_t launch_syrk(const SyrkParams& P, int wt, int in_dtype, bool vec, hipStream_t stream);
-hipError_t launch_syrk_reduce(float* S, int64_t lds, const float* ws, int d, int B, int nb, int ntiles, int ks,
-                              hipStream_t stream);
+int syrk_tile_edge();
+hipError_t launch_syrk(const SyrkParams& P, int in_dtype, bool vec, int grid, hipStream_t stream);
+hipError_t launch_syrk_reduce(float* S, int64_t lds, const float* ws, int d, int nb, int full_tiles, int tail_tiles,
+                              int parts, hipStream_t stream);
 
 // Materialize: H = neutralize(S * scale) + damp * I.
 hipError_t launch_materialize(const float* S, int64_t lds, int d, float scale, float damp_percent, int neutralize,
@@ -51,5 +58,9 @@ hipError_t launch_local_blocks(const void* X, int in_dtype, int64_t n, int d, in
                                int accumulate, hipStream_t stream);
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
+
+// Copy n rows of d elements (esize bytes each) from X (row stride ld) to dst (row stride dld).
+hipError_t launch_copy_rows(const void* X, int64_t ld, int esize, int64_t n, int64_t d, void* dst, int64_t dld,
+                            hipStream_t stream);
 
 }  // namespace hess

@@ -143,6 +143,25 @@ int hess_materialize(hess_t h, float damp_percent, float* H_out);
 int hess_materialize_ex(hess_t h, float damp_percent, unsigned flags, float* H_out,
                         uint8_t* dead_out, float* damp_out, hess_stream_t stream);
 
+/*
+ * hess_flush -- fold batches held in the handle's staging buffer into S.
+ *
+ * A batch shorter than about 2*d/elem_size tokens is not given its own pass
+ * over the d x d sum: hess_add_batch copies its rows into a staging buffer
+ * allocated by hess_create (64 MiB) and counts its tokens, and the staged
+ * rows are added to S in one pass when the buffer fills, by
+ * hess_materialize*, or by this call.  The Gram sum of the concatenated rows
+ * equals the sum of the batches' Grams (GPTQModel PR 2981, Validation: add_batch
+ * over several batches matches the closed form of their concatenation); only
+ * the float32 rounding order differs.  Needed only before reading S through
+ * hess_state_buffer.
+ */
+int hess_flush(hess_t h, hess_stream_t stream);
+
+/* Tuning and test hook, process-wide: enable (1, default) or disable (0) the
+ * staging of short batches. */
+int hess_set_staging(int enable);
+
 /* S = 0, N = 0 (enqueued on stream); also re-arms a consumed handle. */
 int hess_reset(hess_t h, hess_stream_t stream);
 
@@ -150,8 +169,7 @@ int hess_reset(hess_t h, hess_stream_t stream);
 int hess_token_count(hess_t h, int64_t* n_out);
 
 /* Tuning and test hook, process-wide: force the edge of the upper-triangle
- * tiles used by hess_add_batch (0 = automatic choice per call, 128 or 192).
- * float32 inputs and unaligned X always use 128. */
+ * tiles used by hess_add_batch (0 = automatic choice per call, or 128). */
 int hess_set_tile_override(int edge);
 
 /* Width and input type of a handle (host outputs). */
@@ -159,8 +177,9 @@ int hess_info(hess_t h, int64_t* d_out, int* in_dtype_out);
 
 /*
  * hess_state_buffer -- the device address of the handle's float32 d x d
- * buffer: the Gram sum S (upper triangle valid) or, after an in-place
- * materialize, H.  Read-only for callers except through this API.
+ * buffer: the Gram sum S (upper triangle valid; call hess_flush first so
+ * staged batches are included) or, after an in-place materialize, H.
+ * Read-only for callers except through this API.
  */
 int hess_state_buffer(hess_t h, const float** S_out);
 

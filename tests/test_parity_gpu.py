@@ -6,6 +6,7 @@ odd widths, unaligned rows) are covered; exactness cases (the pages' worked
 example, dyadic inputs whose every float32 sum is exact) are compared bitwise.
 """
 
+import gc
 import sys
 
 import numpy as np
@@ -27,10 +28,12 @@ def _say(msg):
 
 
 @pytest.fixture(autouse=True)
-def _tile_auto():
+def _defaults():
     hs.set_tile_override(0)
+    hs.set_staging(True)
     yield
     hs.set_tile_override(0)
+    hs.set_staging(True)
 
 
 def run_lib(wl: W.Workload, damp=0.01, neutralize=True):
@@ -74,10 +77,13 @@ def test_tiny_case_fp32():
     check_against_oracle(wl)
 
 
+@pytest.mark.parametrize("staging", [True, False])
 @pytest.mark.parametrize("d", [384, 520, 700])
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
-def test_ragged_batches(d, dtype):
-    _say(f"ragged d={d} {dtype}")
+def test_ragged_batches(d, dtype, staging):
+    """Short batches go through the staging buffer (when enabled), long ones straight to the SYRK."""
+    _say(f"ragged d={d} {dtype} staging={staging}")
+    hs.set_staging(staging)
     sizes = [1, 63, 64, 65, 777, 0, 1500]
     wl = W.ragged_case(d, sizes, seed=100 + d, dtype=dtype, dead_frac=0.02)
     check_against_oracle(wl)
@@ -97,6 +103,33 @@ def test_forced_tile_edges(edge):
     hs.set_tile_override(edge)
     wl = W.ragged_case(1000, [300, 2000], seed=55, dtype=W.BF16)
     check_against_oracle(wl)
+
+
+def test_staging_buffer_overflow_and_flush():
+    """d=8192 bf16: 4,096 staged tokens fill the buffer; later batches flush it first."""
+    _say("staging overflow d=8192")
+    d = 8192
+    wl = W.ragged_case(d, [1500, 1500, 1500, 1500, 100], seed=61, dtype=W.BF16, dead_frac=0.0)
+    h = hs.Hessian(d, torch.bfloat16)
+    for b in wl.batches:
+        h.add_batch(to_device(b, W.BF16))
+    h.flush()
+    S = h.state_tensor()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = rng.integers(0, d, 400)
+    cols = rng.integers(0, d, 400)
+    up_r, up_c = np.minimum(rows, cols), np.maximum(rows, cols)
+    diag = np.arange(d)
+    ref_s = O.gram_entries(wl.batches, W.BF16, np.concatenate([up_r, diag]), np.concatenate([up_c, diag]))
+    got = S[torch.from_numpy(np.concatenate([up_r, diag])).cuda(), torch.from_numpy(np.concatenate([up_c, diag])).cuda()]
+    got = got.double().cpu().numpy()
+    N = wl.total_tokens
+    mean_diag = float(np.mean(ref_s[len(up_r):])) * 2.0 / N
+    err = float(np.max(np.abs(got - ref_s))) * 2.0 / N / mean_diag
+    assert h.nsamples == N
+    assert err <= TOL[W.BF16], err
+    h.close()
 
 
 def test_worked_example_bitwise():
@@ -214,12 +247,20 @@ def test_add_batch_allocates_nothing():
     _say("zero allocation")
     h = hs.Hessian(1024, torch.bfloat16)
     x = torch.randn(1500, 1024, device="cuda").to(torch.bfloat16)
+    thin = x[:300]                      # fewer tokens than d: goes through the staging buffer
+    # Warm every path once (code objects load lazily), and drop garbage left by
+    # earlier tests so that torch frees nothing during the measured loop.
     h.add_batch(x)
+    h.add_batch(thin)
+    h.flush()
+    gc.collect()
     torch.cuda.synchronize()
     free0, _ = torch.cuda.mem_get_info()
     alloc0 = torch.cuda.memory_allocated()
     for _ in range(30):
         h.add_batch(x)
+        h.add_batch(thin)
+    h.flush()
     torch.cuda.synchronize()
     free1, _ = torch.cuda.mem_get_info()
     assert torch.cuda.memory_allocated() == alloc0
