@@ -56,46 +56,74 @@ def ragged_setup(torch, W, d, seed, dtype="bf16", count=360, dead_frac=0.0, devi
     return buf, views, sizes
 
 
-def time_hessian(torch, hs, d, views, steps, warmup, dtype, kernel_events=False):
-    """Whole-Hessian timing; optionally per-add_batch HIP events (same stream)."""
+def time_hessian(torch, hs, d, views, steps, warmup, dtype, kernel_timing=False):
+    """Whole-Hessian timing with per-step HIP events on the library's stream.
+
+    With kernel_timing, the library also brackets each SYRK launch with HIP
+    events (on the stream the kernel runs on) during the timed steps.
+    Returns (mean ms, per-step ms array, host wall ms, (launches, tokens, syrk ms) or None).
+    """
     h = hs.Hessian(d, dtype)
     out = torch.empty((d, d), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def one(evs=None):
+    def one():
         h.reset()
-        for i, x in enumerate(views):
-            if evs is not None:
-                evs[i][0].record(stream)
+        for x in views:
             h.add_batch(x)
-            if evs is not None:
-                evs[i][1].record(stream)
         h.materialize(0.01, out=out)
 
     for _ in range(warmup):
         one()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    if kernel_timing:
+        h.set_timing(True)
     wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         one()
-    t1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - wall0) * 1e3 / steps
-    ms = t0.elapsed_time(t1) / steps
-    kern_ms = None
-    if kernel_events:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in views]
-        tot = np.zeros(len(views))
-        for _ in range(steps):
-            one(evs)
-            torch.cuda.synchronize()
-            tot += np.array([a.elapsed_time(b) for a, b in evs])
-        kern_ms = tot / steps
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    kt = None
+    if kernel_timing:
+        kt = h.timing()
+        h.set_timing(False)
     h.close()
-    return ms, wall, kern_ms
+    return ms, per, wall, kt
+
+
+KERNEL_SOURCES = ("syrk.hip", "hess_device.hpp", "hess_internal.hpp", "hess_api.hip")
+
+
+def kernel_source_sha256():
+    """sha256 over the SYRK kernel's sources and its launch planning, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gptq_hessian_accumulation_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic(summary):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
+
+    None when the summary is missing or was taken on a different version of
+    the kernel sources (their sha256 no longer matches).
+    """
+    try:
+        with open(summary) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+        sha = kernel_source_sha256()
+        if kv.get("source_sha256", "").strip() != sha:
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def syrk_flops(d, n):
@@ -140,7 +168,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--print-kernel-sha", action="store_true",
+                    help="print the sha256 of the SYRK kernel sources and exit")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 256 MiB device copy (the byte-counter calibration kernel)")
     args = ap.parse_args()
+    if args.print_kernel_sha:
+        print(kernel_source_sha256())
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               "(the Hessian path runs on a single MI355X).", file=sys.stderr)
@@ -157,19 +192,20 @@ def main():
     N = int(sizes.sum())
     torch.cuda.synchronize()
     log(f"timing {args.steps} Hessians after {args.warmup} warm-ups")
-    ms, wall, _ = time_hessian(torch, hs, d, views, args.steps, args.warmup, torch.bfloat16)
-    log(f"headline: {ms:.3f} ms per Hessian (host wall {wall:.3f} ms)")
-    _, _, kern = time_hessian(torch, hs, d, views, max(2, args.steps // 2), 1, torch.bfloat16,
-                              kernel_events=True)
+    ms, per, wall, _ = time_hessian(torch, hs, d, views, args.steps, args.warmup, torch.bfloat16)
+    log(f"headline: {ms:.3f} ms per Hessian (median {np.median(per):.3f}, host wall {wall:.3f} ms)")
+    # Second pass of the same K steps with each SYRK launch bracketed by HIP
+    # events on its stream (kept out of the headline pass: the extra event
+    # packets between kernels cost time of their own).
+    _, _, _, kt = time_hessian(torch, hs, d, views, args.steps, 1, torch.bfloat16, kernel_timing=True)
     flops = syrk_flops(d, N)
     tflops = flops / (ms * 1e-3) / 1e12
-    # roofline of the dominant kernel (the SYRK update): algorithmic bytes per
-    # launch / its mean launch duration, from HIP events around each launch
-    kbytes = np.array([syrk_bytes(d, n, 2) for n in sizes])
-    kflops = np.array([syrk_flops(d, n) for n in sizes])
-    kern_s = kern * 1e-3
-    achieved_bw = kbytes.mean() / kern_s.mean()
-    roof_t = np.maximum(kflops / P_BF16, kbytes / HBM)
+    # Roofline of the dominant kernel, the SYRK pass (a dense bf16 contraction):
+    # algorithmic flops of the tokens each launch processed, N d (d + 1), over
+    # the launches' HIP-event durations, against the dense bf16 MFMA peak.
+    launches, ktok, kms = kt
+    achieved = syrk_flops(d, ktok) / (kms * 1e-3)
+    traffic = read_traffic(os.path.join(ROOT, "profiles", "syrk_bf16_d2560_ragged_traffic.txt"))
     result = {
         "metric": METRIC,
         "value": round(ms, 4),
@@ -178,6 +214,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_median": round(float(np.median(per)), 4),
+        "ms_min": round(float(per.min()), 4),
+        "ms_p90": round(float(np.percentile(per, 90)), 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": round(ms / PAGES_MS[d], 4),
@@ -188,13 +227,29 @@ def main():
                    "d": d, "batches": len(sizes), "tokens": N, "seed": 1},
         "tflops": round(tflops, 2),
         "mfma_util": round(flops / (ms * 1e-3) / P_BF16, 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved_bw / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
-                     "frac": round(achieved_bw / HBM, 4), "traffic": None,
-                     "kernel": "syrk_bf16 (hess_add_batch)", "mean_launch_us": round(kern_s.mean() * 1e6, 2),
-                     "per_batch_roofline_frac": round(float(roof_t.sum() / kern_s.sum()), 4)},
+        "pages_gb300_ms": PAGES_MS[d],
+        "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": P_BF16 / 1e12,
+                     "unit": "TFLOP/s", "frac": round(achieved / P_BF16, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "kernel": "syrk_bf16_buffer (hess_add_batch SYRK pass)",
+                     "launches_per_hessian": round(launches / args.steps, 2),
+                     "mean_launch_us": round(kms * 1e3 / launches, 2),
+                     "tokens_per_launch": round(ktok / launches, 1)},
     }
     del buf, views
     torch.cuda.empty_cache()
+
+    if args.copy_calib:
+        # A plain copy of known size: 256 MiB read and 256 MiB written per
+        # dispatch.  Hardware byte counters read on this kernel give the factor
+        # that turns the same counters on the SYRK into bytes.
+        src = torch.empty(128 << 20, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 256 MiB device copies")
+        del src, dst
 
     extra = {}
     if not args.no_extras:
@@ -217,7 +272,7 @@ def run_extras(torch, hs, W, args):
         log(f"d=4096 ragged {dt}")
         buf, views, sizes = ragged_setup(torch, W, 4096, seed=2, dtype=dt, dead_frac=0.01)
         N = int(sizes.sum())
-        ms, _, _ = time_hessian(torch, hs, 4096, views, steps, 1, tdt)
+        ms, _, _, _ = time_hessian(torch, hs, 4096, views, steps, 1, tdt)
         fl = syrk_flops(4096, N)
         extra[f"d4096_ragged_{dt}"] = {"ms": round(ms, 3), "tflops": round(fl / ms / 1e9, 1),
                                        "mfma_util": round(fl / (ms * 1e-3) / P_BF16, 4), "tokens": N,
@@ -229,12 +284,14 @@ def run_extras(torch, hs, W, args):
         gen = W.torch_generator(2, "cuda")
         sc = W.torch_column_scales(gen, 4096, "cuda")
         x = W.torch_rows(gen, 32768, 4096, sc, dt, "cuda")
-        ms, _, kern = time_hessian(torch, hs, 4096, [x], steps, 1, tdt, kernel_events=True)
+        ms, _, _, (nl, _, kms) = time_hessian(torch, hs, 4096, [x], steps, 1, tdt, kernel_timing=True)
+        kern = kms / nl
         fl = syrk_flops(4096, 32768)
-        peak = P_BF16
-        extra[f"d4096_n32768_{dt}"] = {"ms": round(ms, 4), "syrk_ms": round(float(kern[0]), 4),
-                                       "syrk_tflops": round(fl / kern[0] / 1e9, 1),
-                                       "syrk_mfma_util": round(fl / (kern[0] * 1e-3) / peak, 4)}
+        peak = P_BF16 if dt == "bf16" else P_F32_MFMA
+        extra[f"d4096_n32768_{dt}"] = {"ms": round(ms, 4), "syrk_ms": round(kern, 4),
+                                       "syrk_tflops": round(fl / kern / 1e9, 1),
+                                       "syrk_util": round(fl / (kern * 1e-3) / peak, 4),
+                                       "peak_tflops": peak / 1e12}
         del x
     # MoE: 64 routed experts, d=2048, 32768 tokens top-8, Zipf(1.1)
     log("MoE grouped")

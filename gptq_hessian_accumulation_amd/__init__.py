@@ -86,6 +86,8 @@ def _load():
         "hess_set_tile_override": (c_int, [c_int]),
         "hess_set_staging": (c_int, [c_int]),
         "hess_flush": (c_int, [vp, vp]),
+        "hess_set_timing": (c_int, [vp, c_int]),
+        "hess_timing": (c_int, [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]),
         "hess_info": (c_int, [vp, ctypes.POINTER(i64), ctypes.POINTER(c_int)]),
         "hess_state_buffer": (c_int, [vp, ctypes.POINTER(vp)]),
         "hess_local_blocks": (c_int, [vp, i64, i64, c_int, vp]),
@@ -144,7 +146,7 @@ def set_staging(enable: bool) -> None:
 
 
 def set_tile_override(edge: int) -> None:
-    """Force the SYRK tile edge (0 = automatic, 128 or 192); process-wide."""
+    """Force the SYRK tile edge (0 = automatic, or 128); process-wide."""
     _check(_load().hess_set_tile_override(int(edge)))
 
 
@@ -190,7 +192,7 @@ class Hessian:
         flags = 0 if neutralize else HESS_NO_NEUTRALIZE
         _check(_load().hess_materialize_ex(self._h, float(damp_percent), flags, out.data_ptr(), dead.data_ptr(),
                                            damp.data_ptr(), _stream(stream)))
-        return out, dead.bool(), damp
+        return out, dead.view(torch.bool), damp
 
     def materialize_in_place(self, damp_percent: float = 0.01, neutralize: bool = True, stream=None):
         """Materialize into the accumulator's own buffer; the handle then needs reset()."""
@@ -200,7 +202,7 @@ class Hessian:
         flags = 0 if neutralize else HESS_NO_NEUTRALIZE
         _check(_load().hess_materialize_ex(self._h, float(damp_percent), flags, None, dead.data_ptr(),
                                            damp.data_ptr(), _stream(stream)))
-        return dead.bool(), damp
+        return dead.view(torch.bool), damp
 
     def state_buffer_ptr(self) -> int:
         p = ctypes.c_void_p()
@@ -226,6 +228,16 @@ class Hessian:
 
     def reset(self, stream=None) -> None:
         _check(_load().hess_reset(self._h, _stream(stream)))
+
+    def set_timing(self, on: bool) -> None:
+        """Bracket every SYRK launch of this handle with HIP events on its stream."""
+        _check(_load().hess_set_timing(self._h, 1 if on else 0))
+
+    def timing(self):
+        """``(launches, tokens, ms)`` of the SYRK launches timed since the last read (waits for them)."""
+        n, t, ms = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_double()
+        _check(_load().hess_timing(self._h, ctypes.byref(n), ctypes.byref(t), ctypes.byref(ms)))
+        return n.value, t.value, ms.value
 
     @property
     def nsamples(self) -> int:

@@ -40,6 +40,12 @@ struct hess_s {
   bool has_stream = false;
   hipStream_t last = nullptr;
   hipEvent_t ev = nullptr;
+  // SYRK launch timing (hess_set_timing): event pairs around each launch of
+  // the current window, and the tokens each launch processed
+  bool timing = false;
+  std::vector<hipEvent_t> tev;
+  std::vector<int64_t> ttok;
+  size_t tcount = 0;
 };
 
 namespace {
@@ -169,8 +175,27 @@ int run_syrk(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s) {
   P.item_prefix[0] = 0;
   P.item_prefix[1] = pl.ntiles;
   P.g[0] = SyrkGroup{h->S, 0, n};
-  hipError_t e = launch_syrk(P, h->dtype, vec, pl.grid, s);
+  hipError_t e = hipSuccess;
+  if (h->timing) {
+    if (h->tev.size() < 2 * (h->tcount + 1)) {
+      for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+        hipEvent_t ev = nullptr;
+        e = hipEventCreate(&ev);
+        if (e == hipSuccess) h->tev.push_back(ev);
+      }
+      if (e != hipSuccess) return hip_fail(e, "timing event");
+    }
+    e = hipEventRecord(h->tev[2 * h->tcount], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  e = launch_syrk(P, h->dtype, vec, pl.grid, s);
   if (e != hipSuccess) return hip_fail(e, "SYRK launch");
+  if (h->timing) {
+    e = hipEventRecord(h->tev[2 * h->tcount + 1], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if (h->ttok.size() <= h->tcount) h->ttok.resize(h->tcount + 1);
+    h->ttok[h->tcount++] = n;
+  }
   if (pl.tail_parts > 0) {
     e = launch_syrk_reduce(h->S, h->d, h->ws, (int)h->d, pl.nb, pl.full_tiles, pl.ntiles - pl.full_tiles,
                            pl.tail_parts, s);
@@ -275,6 +300,7 @@ int hess_destroy(hess_t h) {
   if (h->ws) (void)hipFree(h->ws);
   if (h->stage) (void)hipFree(h->stage);
   (void)hipEventDestroy(h->ev);
+  for (hipEvent_t ev : h->tev) (void)hipEventDestroy(ev);
   delete h;
   return e == hipSuccess ? HESS_OK : hip_fail(e, "hess_destroy");
 }
@@ -431,6 +457,35 @@ int hess_flush(hess_t h, hess_stream_t stream) {
 
 int hess_set_staging(int enable) {
   g_staging = enable != 0;
+  return HESS_OK;
+}
+
+int hess_set_timing(hess_t h, int on) {
+  if (!h) return fail(HESS_EINVAL, "null handle");
+  h->timing = on != 0;
+  h->tcount = 0;
+  return HESS_OK;
+}
+
+int hess_timing(hess_t h, int64_t* launches, int64_t* tokens, double* ms) {
+  if (!h || !launches || !tokens || !ms) return fail(HESS_EINVAL, "null argument");
+  double total = 0.0;
+  int64_t tok = 0;
+  if (h->tcount > 0) {
+    hipError_t e = hipEventSynchronize(h->tev[2 * h->tcount - 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    for (size_t i = 0; i < h->tcount; ++i) {
+      float t = 0.0f;
+      e = hipEventElapsedTime(&t, h->tev[2 * i], h->tev[2 * i + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      total += t;
+      tok += h->ttok[i];
+    }
+  }
+  *launches = (int64_t)h->tcount;
+  *tokens = tok;
+  *ms = total;
+  h->tcount = 0;
   return HESS_OK;
 }
 

@@ -19,6 +19,7 @@ namespace {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
+// Grid-stride 16-byte moves, for any size.
 __global__ void __launch_bounds__(256) copy_rows_vec(const char* X, int64_t ld_bytes, char* dst, int64_t dld_bytes,
                                                      int64_t n, int64_t chunks_per_row) {
   const int64_t total = n * chunks_per_row;
@@ -27,6 +28,18 @@ __global__ void __launch_bounds__(256) copy_rows_vec(const char* X, int64_t ld_b
     *reinterpret_cast<u32x4_t*>(dst + r * dld_bytes + c * 16) =
         *reinterpret_cast<const u32x4_t*>(X + r * ld_bytes + c * 16);
   }
+}
+
+// Staging-size copies (fewer than 2^31 chunks): one 16-byte chunk per
+// thread with 32-bit index arithmetic; many small workgroups keep the most
+// requests in flight for these few-megabyte copies.
+__global__ void __launch_bounds__(256) copy_rows_vec32(const char* X, int64_t ld_bytes, char* dst, int64_t dld_bytes,
+                                                       uint32_t total, uint32_t chunks_per_row) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i >= total) return;
+  const uint32_t r = i / chunks_per_row, c = i - r * chunks_per_row;
+  *reinterpret_cast<u32x4_t*>(dst + (int64_t)r * dld_bytes + c * 16u) =
+      *reinterpret_cast<const u32x4_t*>(X + (int64_t)r * ld_bytes + c * 16u);
 }
 
 template <typename E>
@@ -48,10 +61,16 @@ hipError_t launch_copy_rows(const void* X, int64_t ld, int esize, int64_t n, int
                    ((ld * esize) & 15) == 0 && ((dld * esize) & 15) == 0 && ((d * esize) & 15) == 0;
   if (vec) {
     const int64_t cpr = d * esize / 16;
-    int64_t blocks = (n * cpr + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(copy_rows_vec, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<const char*>(X),
-                       ld * esize, static_cast<char*>(dst), dld * esize, n, cpr);
+    const int64_t total = n * cpr;
+    if (total < ((int64_t)1 << 31)) {
+      const int64_t blocks = (total + 255) / 256;
+      hipLaunchKernelGGL(copy_rows_vec32, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<const char*>(X),
+                         ld * esize, static_cast<char*>(dst), dld * esize, (uint32_t)total, (uint32_t)cpr);
+    } else {
+      const int64_t blocks = 8192;
+      hipLaunchKernelGGL(copy_rows_vec, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<const char*>(X),
+                         ld * esize, static_cast<char*>(dst), dld * esize, n, cpr);
+    }
   } else {
     int64_t blocks = (n * d + 255) / 256;
     if (blocks > 8192) blocks = 8192;

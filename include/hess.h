@@ -172,6 +172,20 @@ int hess_token_count(hess_t h, int64_t* n_out);
  * tiles used by hess_add_batch (0 = automatic choice per call, or 128). */
 int hess_set_tile_override(int edge);
 
+/*
+ * hess_set_timing / hess_timing -- measurement aid.  While timing is on, each
+ * SYRK pass of the handle (one per long batch and one per staging-buffer
+ * flush, hess_add_batch's kernel) is bracketed by a pair of HIP events
+ * recorded on the stream it is launched on.  hess_timing waits for the last
+ * recorded event, then returns (host) the number of launches since timing was
+ * switched on or last read, the tokens they processed and the sum of their
+ * event-measured durations in milliseconds, and starts a new window.
+ * hess_set_timing(h, on) also starts a new window.  Creating the events is
+ * the only host-side allocation; no device memory is allocated.
+ */
+int hess_set_timing(hess_t h, int on);
+int hess_timing(hess_t h, int64_t* launches, int64_t* tokens, double* ms);
+
 /* Width and input type of a handle (host outputs). */
 int hess_info(hess_t h, int64_t* d_out, int* in_dtype_out);
 

@@ -382,3 +382,22 @@ def test_grouped_equals_single_handle_runs():
         assert agreement(A.cpu().numpy(), B.cpu().numpy().astype(np.float64)) <= 1e-6
         single.close()
         grouped[e].close()
+
+
+def test_kernel_timing_counts_launches():
+    _say("SYRK launch timing")
+    h = hs.Hessian(512, torch.bfloat16)
+    x = torch.randn(3000, 512, device="cuda").to(torch.bfloat16)
+    h.set_timing(True)
+    h.add_batch(x)                      # long batch: its own SYRK pass
+    h.add_batch(x[:100])                # short: staged
+    h.add_batch(x[:200])
+    h.flush()                           # one pass over the 300 staged tokens
+    launches, tokens, ms = h.timing()
+    assert (launches, tokens) == (2, 3300)
+    assert ms > 0.0
+    assert h.timing() == (0, 0, 0.0)    # a read starts a new window
+    h.set_timing(False)
+    h.add_batch(x)
+    assert h.timing() == (0, 0, 0.0)
+    h.close()
