@@ -301,7 +301,7 @@ def run_extras(torch, hs, W, args):
     sc = W.torch_column_scales(gen, 2048, "cuda")
     x = W.torch_rows(gen, 32768, 2048, sc, "bf16", "cuda")
     ridx = torch.from_numpy(row_idx).cuda()
-    hsx = [hs.Hessian(2048, torch.bfloat16) for _ in range(64)]
+    hsx = [hs.Hessian(2048, torch.bfloat16, staging_bytes=0) for _ in range(64)]  # grouped updates only
     outs = torch.empty((2048, 2048), dtype=torch.float32, device="cuda")
 
     def moe_once():

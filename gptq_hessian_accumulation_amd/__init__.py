@@ -77,6 +77,7 @@ def _load():
         "hess_strerror": (ctypes.c_char_p, [c_int]),
         "hess_last_error": (ctypes.c_char_p, []),
         "hess_create": (vp, [i64, c_int]),
+        "hess_create_ex": (vp, [i64, c_int, i64]),
         "hess_destroy": (c_int, [vp]),
         "hess_add_batch": (c_int, [vp, vp, i64, i64, vp]),
         "hess_materialize": (c_int, [vp, ctypes.c_float, vp]),
@@ -146,7 +147,7 @@ def set_staging(enable: bool) -> None:
 
 
 def set_tile_override(edge: int) -> None:
-    """Force the SYRK tile edge (0 = automatic, or 128); process-wide."""
+    """Force the SYRK tile edge (0 = automatic, 128 or 256); process-wide."""
     _check(_load().hess_set_tile_override(int(edge)))
 
 
@@ -155,14 +156,19 @@ class Hessian:
 
     ``dtype`` is the activation element type every batch will have
     (``torch.bfloat16`` or ``torch.float32``); the Hessian is always float32.
+    ``staging_bytes`` sizes the buffer that collects short batches (default:
+    256 MiB for bf16 at d >= 3072, else 64 MiB; 0 disables staging).
     """
 
-    def __init__(self, d: int, dtype=torch.bfloat16):
+    def __init__(self, d: int, dtype=torch.bfloat16, staging_bytes: int | None = None):
         lib = _load()
         self.d = int(d)
         self.dtype = dtype
         self._code = _dtype_code(dtype)
-        h = lib.hess_create(self.d, self._code)
+        if staging_bytes is None:
+            h = lib.hess_create(self.d, self._code)
+        else:
+            h = lib.hess_create_ex(self.d, self._code, int(staging_bytes))
         if not h:
             raise HessError(-1, lib.hess_last_error().decode(errors="replace"))
         self._h = ctypes.c_void_p(h)

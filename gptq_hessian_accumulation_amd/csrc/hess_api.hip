@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/hess.h"
@@ -46,9 +47,28 @@ struct hess_s {
   std::vector<hipEvent_t> tev;
   std::vector<int64_t> ttok;
   size_t tcount = 0;
+  // 256-tile path: blocked order of the upper-triangle 256-tiles (device)
+  int32_t* order256 = nullptr;
+  int nb256 = 0;
+  int ntiles256 = 0;
 };
 
 namespace {
+
+// Stream-K workspace of the 256-tile path, one per device, shared by every
+// handle on it and grown by hess_create to the largest width seen.  Launches
+// that use it are ordered: a launch on another stream than the previous user
+// first waits for that user's event.
+struct BigWorkspace {
+  std::mutex mu;
+  float* ptr = nullptr;
+  int64_t slots = 0;          // 256 x 256 float slots
+  hipEvent_t ev = nullptr;
+  bool used = false;
+  hipStream_t last = nullptr;
+};
+constexpr int kMaxDevices = 64;
+BigWorkspace g_big[kMaxDevices];
 
 thread_local char g_err[512] = "";
 int g_tile_override = 0;  // 0 = automatic; 128 forces the 128-edge SYRK tiles
@@ -135,12 +155,11 @@ Plan plan_single(int64_t d, int64_t n, bool have_ws) {
   return p;
 }
 
-// Staging buffer: 64 MiB of rows per handle (a multiple of 64 tokens).
-constexpr int64_t kStageBytes = (int64_t)64 << 20;
-
-int64_t stage_tokens(int64_t d, int es) {
+// Staging buffer: HESS_STAGING_DEFAULT bytes of rows per handle unless
+// hess_create_ex says otherwise (a multiple of 64 tokens, at least 256).
+int64_t stage_tokens(int64_t d, int es, int64_t bytes) {
   const int64_t row = ((d + 7) / 8 * 8) * es;
-  int64_t cap = kStageBytes / row / 64 * 64;
+  int64_t cap = bytes / row / 64 * 64;
   return cap >= 256 ? cap : 0;
 }
 
@@ -151,9 +170,131 @@ bool stage_pays(const hess_s* h, int64_t n) {
   return g_staging && h->stage && n <= h->stage_cap && n * esize(h->dtype) < 2 * h->d;
 }
 
+// Timing events around one SYRK pass (hess_set_timing).
+hipError_t timing_begin(hess_t h, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  while (e == hipSuccess && h->tev.size() < 2 * (h->tcount + 1)) {
+    hipEvent_t ev = nullptr;
+    e = hipEventCreate(&ev);
+    if (e == hipSuccess) h->tev.push_back(ev);
+  }
+  if (e != hipSuccess) return e;
+  return hipEventRecord(h->tev[2 * h->tcount], s);
+}
+
+hipError_t timing_end(hess_t h, hipStream_t s, int64_t n) {
+  const hipError_t e = hipEventRecord(h->tev[2 * h->tcount + 1], s);
+  if (e != hipSuccess) return e;
+  if (h->ttok.size() <= h->tcount) h->ttok.resize(h->tcount + 1);
+  h->ttok[h->tcount++] = n;
+  return hipSuccess;
+}
+
+// ---- 256-tile path ----
+constexpr int kBig = 256;
+constexpr int kBigKI = 32;               // tokens per iteration
+constexpr int kBigMinD = 1024;           // automatic choice: widths at least this wide ...
+constexpr int64_t kBigMinWork = 400;     // ... and at least this many iterations per workgroup
+
+bool big_capable(int64_t d, int dtype) { return dtype == HESS_BF16 && d % 8 == 0 && d >= 8 && d <= 32768; }
+
+// Upper-triangle tiles in blocked order: 4 x 4 super-tiles (row-major over
+// the super-tiles, row-major inside each), so that consecutive tiles share
+// few row and column panels.
+std::vector<int32_t> blocked_order(int nb) {
+  const int G = 4;
+  std::vector<int32_t> o;
+  for (int si = 0; si < nb; si += G)
+    for (int sj = si; sj < nb; sj += G)
+      for (int i = si; i < std::min(nb, si + G); ++i)
+        for (int j = std::max(i, sj); j < std::min(nb, sj + G); ++j) o.push_back((i << 16) | j);
+  return o;
+}
+
+// Workspace slots a launch can use: 2 grid_sk + excess items, grid_sk <= 256
+// and excess items < sk_tiles = ntiles % 256.
+int64_t big_slots(int ntiles) { return ntiles % kCUs ? 2 * kCUs + ntiles % kCUs : 0; }
+
+// The 256-tile kernel has a fixed cost per launch (its parts' workspace
+// round trip and fixup, its imbalance when tiles split into many parts), so
+// it is chosen once each workgroup gets at least 400 iterations of 32
+// tokens; measured on MI355X with N(0,1)-scaled bf16 data: width 4,096 with
+// 32,768 tokens (544 per workgroup) takes 0.50 ms against 0.74 ms on
+// 128-tiles, while width 2,560 with 26,112 tokens (175 per workgroup) is
+// slower than two 128-tile passes.
+bool use_big(const hess_s* h, int64_t n, bool vec) {
+  if (!h->order256 || !vec) return false;
+  if (g_tile_override == kTile) return false;
+  if (g_tile_override == kBig) return true;
+  const int64_t niter = (n + kBigKI - 1) / kBigKI;
+  return h->d >= kBigMinD && (int64_t)h->ntiles256 * niter >= kBigMinWork * kCUs;
+}
+
+// The timing events (hess_set_timing) bracket the main kernel, which does
+// all the multiplications; the fixup that adds the stream-K pieces follows it.
+int run_big(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s) {
+  BigParams B;
+  std::memset(&B, 0, sizeof(B));
+  B.X = X;
+  B.ld = ld;
+  B.S = h->S;
+  B.lds = h->d;
+  B.order = h->order256;
+  B.n = n;
+  B.d = (int)h->d;
+  B.nb = h->nb256;
+  B.ntiles = h->ntiles256;
+  B.niter = (int)((n + kBigKI - 1) / kBigKI);
+  B.dp_tiles = (h->ntiles256 / kCUs) * kCUs;
+  B.sk_tiles = h->ntiles256 - B.dp_tiles;
+  B.parts = 1;
+  B.part_len = B.niter;
+  B.items = B.sk_tiles;
+  B.grid_sk = 0;
+  B.excess_total = 0;
+  if (B.sk_tiles > 0) {
+    // enough aligned parts per tile to give every CU one; the parts past the
+    // first 256 (fewer than sk_tiles) are shared out as pieces
+    B.parts = (int)std::min<int64_t>((kCUs + B.sk_tiles - 1) / B.sk_tiles, B.niter);
+    B.part_len = (B.niter + B.parts - 1) / B.parts;
+    B.items = B.sk_tiles * B.parts;
+    B.grid_sk = std::min(kCUs, B.items);
+    if (B.grid_sk >= 8) B.grid_sk -= B.grid_sk % 8;  // whole XCD rows
+    B.excess_total = (int64_t)(B.items - B.grid_sk) * B.part_len;
+  }
+  const int64_t slots = 2 * (int64_t)B.grid_sk + (B.items - B.grid_sk);
+  BigWorkspace& W = g_big[h->device];
+  std::lock_guard<std::mutex> lock(W.mu);
+  if (slots > W.slots) return fail(HESS_EHIP, "256-tile workspace too small");
+  B.ws = W.ptr;
+  hipError_t e = hipSuccess;
+  if (W.used && W.last != s) {
+    e = hipStreamWaitEvent(s, W.ev, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  if (h->timing) {
+    e = timing_begin(h, s);
+    if (e != hipSuccess) return hip_fail(e, "timing event");
+  }
+  e = launch_syrk_big(B, s);
+  if (e != hipSuccess) return hip_fail(e, "256-tile SYRK launch");
+  if (h->timing) {
+    e = timing_end(h, s, n);
+    if (e != hipSuccess) return hip_fail(e, "timing event");
+  }
+  e = launch_syrk_big_fixup(B, s);
+  if (e != hipSuccess) return hip_fail(e, "256-tile fixup launch");
+  e = hipEventRecord(W.ev, s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  W.used = true;
+  W.last = s;
+  return HESS_OK;
+}
+
 // One SYRK pass of n rows of X into S, on stream s (already ordered).
 int run_syrk(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s) {
   const bool vec = vec_ok(X, ld, h->d, esize(h->dtype));
+  if (use_big(h, n, vec)) return run_big(h, X, n, ld, s);
   const Plan pl = plan_single(h->d, n, h->ws != nullptr);
   SyrkParams P;
   std::memset(&P, 0, sizeof(P));
@@ -177,24 +318,14 @@ int run_syrk(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s) {
   P.g[0] = SyrkGroup{h->S, 0, n};
   hipError_t e = hipSuccess;
   if (h->timing) {
-    if (h->tev.size() < 2 * (h->tcount + 1)) {
-      for (int k = 0; k < 2 && e == hipSuccess; ++k) {
-        hipEvent_t ev = nullptr;
-        e = hipEventCreate(&ev);
-        if (e == hipSuccess) h->tev.push_back(ev);
-      }
-      if (e != hipSuccess) return hip_fail(e, "timing event");
-    }
-    e = hipEventRecord(h->tev[2 * h->tcount], s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    e = timing_begin(h, s);
+    if (e != hipSuccess) return hip_fail(e, "timing event");
   }
   e = launch_syrk(P, h->dtype, vec, pl.grid, s);
   if (e != hipSuccess) return hip_fail(e, "SYRK launch");
   if (h->timing) {
-    e = hipEventRecord(h->tev[2 * h->tcount + 1], s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if (h->ttok.size() <= h->tcount) h->ttok.resize(h->tcount + 1);
-    h->ttok[h->tcount++] = n;
+    e = timing_end(h, s, n);
+    if (e != hipSuccess) return hip_fail(e, "timing event");
   }
   if (pl.tail_parts > 0) {
     e = launch_syrk_reduce(h->S, h->d, h->ws, (int)h->d, pl.nb, pl.full_tiles, pl.ntiles - pl.full_tiles,
@@ -233,18 +364,31 @@ const char* hess_strerror(int code) {
 const char* hess_last_error(void) { return g_err; }
 
 int hess_set_tile_override(int edge) {
-  if (edge != 0 && edge != 128) return fail(HESS_EINVAL, "tile override must be 0 or 128");
+  if (edge != 0 && edge != 128 && edge != 256) return fail(HESS_EINVAL, "tile override must be 0, 128 or 256");
   g_tile_override = edge;
   return HESS_OK;
 }
 
-hess_t hess_create(int64_t d, int in_dtype) {
+// Default staging: large enough at widths >= 3,072 (bf16) that a flush runs
+// on 256-tiles (32,768 tokens at 4,096); 64 MiB otherwise, where flushes run
+// on 128-tiles and the buffer stays resident in the 256 MB Infinity Cache.
+int64_t default_staging(int64_t d, int in_dtype) {
+  return (in_dtype == HESS_BF16 && d >= 3072) ? HESS_STAGING_DEFAULT : ((int64_t)64 << 20);
+}
+
+hess_t hess_create(int64_t d, int in_dtype) { return hess_create_ex(d, in_dtype, default_staging(d, in_dtype)); }
+
+hess_t hess_create_ex(int64_t d, int in_dtype, int64_t staging_bytes) {
   if (d < 1 || d > 65536) {
     fail(HESS_EINVAL, "d = %lld outside [1, 65536]", (long long)d);
     return nullptr;
   }
   if (in_dtype != HESS_BF16 && in_dtype != HESS_F32) {
     fail(HESS_EINVAL, "unknown input dtype %d", in_dtype);
+    return nullptr;
+  }
+  if (staging_bytes < 0 || staging_bytes > ((int64_t)16 << 30)) {
+    fail(HESS_EINVAL, "staging_bytes = %lld outside [0, 16 GiB]", (long long)staging_bytes);
     return nullptr;
   }
   hess_t h = new (std::nothrow) hess_s();
@@ -266,9 +410,36 @@ hess_t hess_create(int64_t d, int in_dtype) {
   }
   // staging rows for thin batches
   if (e == hipSuccess) {
-    h->stage_cap = stage_tokens(d, esize(in_dtype));
+    h->stage_cap = staging_bytes > 0 ? stage_tokens(d, esize(in_dtype), staging_bytes) : 0;
     h->stage_ld = (d + 7) / 8 * 8;
     if (h->stage_cap > 0) e = hipMalloc(&h->stage, (size_t)(h->stage_cap * h->stage_ld * esize(in_dtype)));
+  }
+  // 256-tile path: tile order and the device's shared stream-K workspace
+  if (e == hipSuccess && big_capable(d, in_dtype)) {
+    h->nb256 = (int)((d + kBig - 1) / kBig);
+    const std::vector<int32_t> order = blocked_order(h->nb256);
+    h->ntiles256 = (int)order.size();
+    e = hipMalloc(&h->order256, order.size() * sizeof(int32_t));
+    if (e == hipSuccess)
+      e = hipMemcpy(h->order256, order.data(), order.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess && (h->device < 0 || h->device >= kMaxDevices)) e = hipErrorInvalidDevice;
+    if (e == hipSuccess) {
+      BigWorkspace& W = g_big[h->device];
+      std::lock_guard<std::mutex> lock(W.mu);
+      const int64_t need = big_slots(h->ntiles256);
+      if (!W.ev) e = hipEventCreateWithFlags(&W.ev, hipEventDisableTiming);
+      if (e == hipSuccess && W.slots < need) {
+        if (W.ptr) {
+          e = hipDeviceSynchronize();
+          if (e == hipSuccess) e = hipFree(W.ptr);
+          W.ptr = nullptr;
+          W.slots = 0;
+          W.used = false;
+        }
+        if (e == hipSuccess) e = hipMalloc(&W.ptr, (size_t)need * kBig * kBig * sizeof(float));
+        if (e == hipSuccess) W.slots = need;
+      }
+    }
   }
   if (e == hipSuccess) e = hipMemset(h->S, 0, sbytes);
   if (e == hipSuccess) e = hipMemset(h->damp, 0, 64);
@@ -283,6 +454,7 @@ hess_t hess_create(int64_t d, int in_dtype) {
     if (h->damp) (void)hipFree(h->damp);
     if (h->ws) (void)hipFree(h->ws);
     if (h->stage) (void)hipFree(h->stage);
+    if (h->order256) (void)hipFree(h->order256);
     if (h->ev) (void)hipEventDestroy(h->ev);
     delete h;
     return nullptr;
@@ -299,6 +471,7 @@ int hess_destroy(hess_t h) {
   (void)hipFree(h->damp);
   if (h->ws) (void)hipFree(h->ws);
   if (h->stage) (void)hipFree(h->stage);
+  if (h->order256) (void)hipFree(h->order256);
   (void)hipEventDestroy(h->ev);
   for (hipEvent_t ev : h->tev) (void)hipEventDestroy(ev);
   delete h;

@@ -44,6 +44,39 @@ struct SyrkParams {
   SyrkGroup g[kMaxGroups];
 };
 
+// One launch of the 256-tile SYRK (bf16, 16-byte aligned rows, d % 8 == 0).
+// Tiles order[0 .. dp_tiles) are done whole, one workgroup each (dp_tiles a
+// multiple of 256).  Each of the other sk_tiles tiles is cut into `parts`
+// aligned token ranges of part_len 32-token iterations (item = tile * parts +
+// part); workgroup w < grid_sk does item w, and the items past grid_sk
+// ("excess", excess_total iterations in all) are shared out evenly over the
+// grid_sk workgroups as pieces.  Part 0 of a tile adds into S directly; the
+// other parts and all pieces go to workspace slots, which a fixup kernel adds
+// into S in a fixed order.
+struct BigParams {
+  const void* X;          // tokens x features, row stride ld elements
+  int64_t ld;
+  float* S;               // row stride lds
+  int64_t lds;
+  float* ws;              // 2 * grid_sk + (items - grid_sk) slots of 256 x 256 floats
+  const int32_t* order;   // tile t -> (I << 16) | J, blocked order
+  int64_t n;              // tokens
+  int64_t excess_total;   // (items - grid_sk) * part_len
+  int d;
+  int nb;                 // 256-tiles per dimension
+  int ntiles;
+  int niter;              // 32-token iterations: ceil(n / 32)
+  int dp_tiles;
+  int sk_tiles;
+  int parts;
+  int part_len;
+  int items;              // sk_tiles * parts
+  int grid_sk;            // workgroups after the whole-tile ones (<= items)
+};
+
+hipError_t launch_syrk_big(const BigParams& P, hipStream_t stream);
+hipError_t launch_syrk_big_fixup(const BigParams& P, hipStream_t stream);
+
 int syrk_tile_edge();
 hipError_t launch_syrk(const SyrkParams& P, int in_dtype, bool vec, int grid, hipStream_t stream);
 hipError_t launch_syrk_reduce(float* S, int64_t lds, const float* ws, int d, int nb, int full_tiles, int tail_tiles,

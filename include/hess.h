@@ -76,7 +76,13 @@ const char* hess_last_error(void);
  *
  * Allocates and zeroes the persistent float32 d x d Gram buffer once (GPTQModel
  * PR 2981, Changes: the per-device buffer is allocated once, as float32) plus
- * fixed scratch for split reductions, on the current HIP device.  N = 0.
+ * fixed scratch on the current HIP device: 16 MiB for split reductions, a
+ * staging buffer for short batches (see hess_create_ex), and for bf16
+ * handles with
+ * d % 8 == 0 a small tile-order table.  Such handles also make sure the
+ * device's shared 256-tile workspace holds (512 + ntiles % 256) slots of
+ * 256 KiB, ntiles = nb (nb + 1) / 2 with nb = ceil(d / 256) (162 MiB at
+ * d = 4096); that buffer lives until the process ends.  N = 0.
  *   d         number of input features (Hessian width), 1 <= d <= 65536.
  *   in_dtype  HESS_BF16 or HESS_F32: the element type of every X later given
  *             to hess_add_batch (Model-Optimizer PR 3002, hessian_input_dtype).
@@ -84,6 +90,20 @@ const char* hess_last_error(void);
  * The handle owns its device memory until hess_destroy().
  */
 hess_t hess_create(int64_t d, int in_dtype);
+
+/* Size of a handle's staging buffer for short batches that hess_create
+ * picks for bf16 handles with d >= 3072 (bytes); other handles get 64 MiB. */
+#define HESS_STAGING_DEFAULT ((int64_t)256 << 20)
+
+/*
+ * hess_create_ex -- hess_create with the staging buffer's size chosen by the
+ * caller: staging_bytes in [0, 16 GiB]; 0 (or too small for 256 rows)
+ * disables staging for the handle, e.g. for Hessians only ever updated by
+ * hess_add_batch_grouped.  hess_create picks 256 MiB (HESS_STAGING_DEFAULT)
+ * for bf16 handles with d >= 3072, so that a staged flush is long enough for
+ * the 256-tile kernel, and 64 MiB otherwise.
+ */
+hess_t hess_create_ex(int64_t d, int in_dtype, int64_t staging_bytes);
 
 /* Frees the handle and its device memory after draining its last stream. */
 int hess_destroy(hess_t h);
@@ -148,7 +168,7 @@ int hess_materialize_ex(hess_t h, float damp_percent, unsigned flags, float* H_o
  *
  * A batch shorter than about 2*d/elem_size tokens is not given its own pass
  * over the d x d sum: hess_add_batch copies its rows into a staging buffer
- * allocated by hess_create (64 MiB) and counts its tokens, and the staged
+ * allocated by hess_create (64 or 256 MiB, see hess_create_ex) and counts its tokens, and the staged
  * rows are added to S in one pass when the buffer fills, by
  * hess_materialize*, or by this call.  The Gram sum of the concatenated rows
  * equals the sum of the batches' Grams (GPTQModel PR 2981, Validation: add_batch
@@ -169,7 +189,11 @@ int hess_reset(hess_t h, hess_stream_t stream);
 int hess_token_count(hess_t h, int64_t* n_out);
 
 /* Tuning and test hook, process-wide: force the edge of the upper-triangle
- * tiles used by hess_add_batch (0 = automatic choice per call, or 128). */
+ * tiles used by hess_add_batch (0 = automatic choice per call, 128, or 256).
+ * 256-tiles apply to bf16 handles with d % 8 == 0 and 16-byte aligned rows;
+ * other calls keep 128-tiles.  The automatic choice takes 256-tiles at
+ * d >= 1,024 when a pass (one batch, or one staging flush) gives each of
+ * the 256 workgroups at least 400 iterations of 32 tokens. */
 int hess_set_tile_override(int edge);
 
 /*

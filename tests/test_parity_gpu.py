@@ -97,7 +97,7 @@ def test_edge_widths(d, dtype):
     check_against_oracle(wl)
 
 
-@pytest.mark.parametrize("edge", [128])
+@pytest.mark.parametrize("edge", [128, 256])
 def test_forced_tile_edges(edge):
     _say(f"forced tile {edge}")
     hs.set_tile_override(edge)
@@ -105,12 +105,74 @@ def test_forced_tile_edges(edge):
     check_against_oracle(wl)
 
 
+@pytest.mark.parametrize("staging", [True, False])
+@pytest.mark.parametrize("d", [8, 256, 264, 520, 696, 1032])
+def test_big_tiles_ragged(d, staging):
+    """The 256-tile kernel at any batch length: one-token tiles, partial stream-K shares, edge tiles."""
+    _say(f"256-tile ragged d={d} staging={staging}")
+    hs.set_tile_override(256)
+    hs.set_staging(staging)
+    wl = W.ragged_case(d, [1, 31, 33, 100, 1000, 0, 3000], seed=300 + d, dtype=W.BF16, dead_frac=0.02)
+    check_against_oracle(wl)
+
+
+def _sampled_gram_check(h, wl, n_samples=400, seed=0):
+    """Compare sampled upper entries and the whole diagonal of S with the oracle's exact sums."""
+    d = wl.d
+    h.flush()
+    S = h.state_tensor()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, d, n_samples)
+    cols = rng.integers(0, d, n_samples)
+    # always include the corners of the last (edge) tile and a diagonal-tile pair
+    rows = np.concatenate([rows, [d - 1, 0, d - 1, d // 2]])
+    cols = np.concatenate([cols, [d - 1, d - 1, 0, d // 2 + 1]])
+    up_r, up_c = np.minimum(rows, cols), np.maximum(rows, cols)
+    diag = np.arange(d)
+    r_all, c_all = np.concatenate([up_r, diag]), np.concatenate([up_c, diag])
+    ref = O.gram_entries(wl.batches, W.BF16, r_all, c_all)
+    got = S[torch.from_numpy(r_all).cuda(), torch.from_numpy(c_all).cuda()].double().cpu().numpy()
+    N = wl.total_tokens
+    mean_diag = float(np.mean(ref[len(up_r):])) * 2.0 / N
+    return float(np.max(np.abs(got - ref))) * 2.0 / N / mean_diag
+
+
+@pytest.mark.parametrize("d,n", [(2560, 13056), (4096, 16384), (5888, 700)])
+def test_big_tiles_full_size_sampled(d, n):
+    """Full-width batches on the 256-tile kernel: a staged flush at width 2,560, a long batch at
+    4,096, and width 5,888 (256 whole tiles plus stream-K tiles), on sampled entries."""
+    _say(f"256-tile sampled d={d} n={n}")
+    hs.set_tile_override(256)
+    hs.set_staging(False)
+    wl = W.ragged_case(d, [n], seed=400 + d, dtype=W.BF16, dead_frac=0.0)
+    h = hs.Hessian(d, torch.bfloat16)
+    h.add_batch(to_device(wl.batches[0], W.BF16))
+    err = _sampled_gram_check(h, wl)
+    assert h.nsamples == n
+    assert err <= TOL[W.BF16], err
+    h.close()
+
+
+def test_big_tiles_chosen_automatically():
+    """Width 4,096 with 24,576 tokens (408 iterations per workgroup) takes the 256-tile kernel
+    without an override; the result is checked on sampled entries."""
+    _say("256-tile automatic choice d=4096 n=24576")
+    hs.set_staging(False)
+    wl = W.ragged_case(4096, [24576], seed=78, dtype=W.BF16, dead_frac=0.0)
+    h = hs.Hessian(4096, torch.bfloat16)
+    h.add_batch(to_device(wl.batches[0], W.BF16))
+    err = _sampled_gram_check(h, wl)
+    assert err <= TOL[W.BF16], err
+    h.close()
+
+
 def test_staging_buffer_overflow_and_flush():
-    """d=8192 bf16: 4,096 staged tokens fill the buffer; later batches flush it first."""
+    """d=8192 bf16 with a 64 MiB staging buffer: 4,096 staged tokens fill it; later batches flush it first."""
     _say("staging overflow d=8192")
     d = 8192
     wl = W.ragged_case(d, [1500, 1500, 1500, 1500, 100], seed=61, dtype=W.BF16, dead_frac=0.0)
-    h = hs.Hessian(d, torch.bfloat16)
+    h = hs.Hessian(d, torch.bfloat16, staging_bytes=64 << 20)
     for b in wl.batches:
         h.add_batch(to_device(b, W.BF16))
     h.flush()
@@ -239,6 +301,21 @@ def test_two_streams_are_ordered():
     H, _, _ = h.materialize(0.01, stream=s1)
     s1.synchronize()
     Hr, _, _, _ = run_oracle(wl, 0.01)
+    assert agreement(H.cpu().numpy(), Hr) <= TOL[W.BF16]
+    h.close()
+
+
+def test_staging_size_zero_disables_staging():
+    _say("staging_bytes=0")
+    wl = W.ragged_case(520, [3, 200, 1], seed=91, dtype=W.BF16)
+    h = hs.Hessian(520, torch.bfloat16, staging_bytes=0)
+    h.set_timing(True)
+    for b in wl.batches:
+        h.add_batch(to_device(b, W.BF16))
+    launches, tokens, _ = h.timing()
+    assert (launches, tokens) == (3, 204)   # every batch had its own pass
+    H, _, _ = h.materialize(0.0, neutralize=False)
+    Hr, _, _, _ = run_oracle(wl, 0.0, False)
     assert agreement(H.cpu().numpy(), Hr) <= TOL[W.BF16]
     h.close()
 
