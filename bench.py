@@ -97,19 +97,20 @@ def time_hessian(torch, hs, d, views, steps, warmup, dtype, kernel_timing=False)
 
 
 KERNEL_SOURCES = ("syrk.hip", "hess_device.hpp", "hess_internal.hpp", "hess_api.hip")
+BIG_KERNEL_SOURCES = ("syrk_big.hip", "hess_device.hpp", "hess_internal.hpp", "hess_api.hip")
 
 
-def kernel_source_sha256():
-    """sha256 over the SYRK kernel's sources and its launch planning, in a fixed order."""
+def kernel_source_sha256(sources=KERNEL_SOURCES):
+    """sha256 over a kernel's sources and its launch planning, in a fixed order."""
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "gptq_hessian_accumulation_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def read_traffic(summary):
+def read_traffic(summary, sources=KERNEL_SOURCES):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
 
     None when the summary is missing or was taken on a different version of
@@ -118,7 +119,7 @@ def read_traffic(summary):
     try:
         with open(summary) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
-        sha = kernel_source_sha256()
+        sha = kernel_source_sha256(sources)
         if kv.get("source_sha256", "").strip() != sha:
             return None
         return float(kv["traffic_bytes_per_launch"])
@@ -167,6 +168,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--extras", default="all",
+                    help="comma-separated subset of d4096_ragged,d4096_single,moe,local (default all)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--print-kernel-sha", action="store_true",
                     help="print the sha256 of the SYRK kernel sources and exit")
@@ -174,7 +177,8 @@ def main():
                     help="also run a plain 256 MiB device copy (the byte-counter calibration kernel)")
     args = ap.parse_args()
     if args.print_kernel_sha:
-        print(kernel_source_sha256())
+        print("syrk", kernel_source_sha256())
+        print("syrk_big", kernel_source_sha256(BIG_KERNEL_SOURCES))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -267,8 +271,10 @@ def main():
 def run_extras(torch, hs, W, args):
     extra = {}
     steps = max(3, args.steps // 2)
+    want = set(args.extras.split(",")) if args.extras != "all" else {"d4096_ragged", "d4096_single", "moe", "local"}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # d=4096 ragged (bf16 and fp32), dead columns 1%
-    for dt, tdt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+    for dt, tdt in (() if "d4096_ragged" not in want else (("bf16", torch.bfloat16), ("f32", torch.float32))):
         log(f"d=4096 ragged {dt}")
         buf, views, sizes = ragged_setup(torch, W, 4096, seed=2, dtype=dt, dead_frac=0.01)
         N = int(sizes.sum())
@@ -279,7 +285,7 @@ def run_extras(torch, hs, W, args):
                                        "pages_gb300_ms": PAGES_MS[4096] if dt == "bf16" else 244.0}
         del buf, views
     # d=4096, one 32768-token batch
-    for dt, tdt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+    for dt, tdt in (() if "d4096_single" not in want else (("bf16", torch.bfloat16), ("f32", torch.float32))):
         log(f"d=4096 single 32K batch {dt}")
         gen = W.torch_generator(2, "cuda")
         sc = W.torch_column_scales(gen, 4096, "cuda")
@@ -292,71 +298,82 @@ def run_extras(torch, hs, W, args):
                                        "syrk_tflops": round(fl / kern / 1e9, 1),
                                        "syrk_util": round(fl / (kern * 1e-3) / peak, 4),
                                        "peak_tflops": peak / 1e12}
+        if dt == "bf16":
+            # roofline of this launch's main kernel (the 256-tile SYRK): algorithmic
+            # flops N d (d + 1) over its event-timed duration; counter traffic per launch
+            traffic = read_traffic(os.path.join(ROOT, "profiles", "syrk_big_bf16_d4096_n32768_traffic.txt"),
+                                   BIG_KERNEL_SOURCES)
+            extra["d4096_n32768_bf16"]["roofline"] = {
+                "bound": "mfma", "achieved": round(fl / kern / 1e9, 1), "peak": P_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": round(fl / (kern * 1e-3) / P_BF16, 4), "traffic": None if traffic is None else round(traffic),
+                "kernel": "syrk_big_bf16 (256-tile SYRK main kernel; its fixup follows)"}
         del x
-    # MoE: 64 routed experts, d=2048, 32768 tokens top-8, Zipf(1.1)
-    log("MoE grouped")
-    rng = np.random.default_rng(3)
-    row_idx, offsets = W.moe_routing(rng, 32768, experts=64, topk=8)
-    gen = W.torch_generator(3, "cuda")
-    sc = W.torch_column_scales(gen, 2048, "cuda")
-    x = W.torch_rows(gen, 32768, 2048, sc, "bf16", "cuda")
-    ridx = torch.from_numpy(row_idx).cuda()
-    hsx = [hs.Hessian(2048, torch.bfloat16, staging_bytes=0) for _ in range(64)]  # grouped updates only
-    outs = torch.empty((2048, 2048), dtype=torch.float32, device="cuda")
+    if "moe" in want:
+        # MoE: 64 routed experts, d=2048, 32768 tokens top-8, Zipf(1.1)
+        log("MoE grouped")
+        rng = np.random.default_rng(3)
+        row_idx, offsets = W.moe_routing(rng, 32768, experts=64, topk=8)
+        gen = W.torch_generator(3, "cuda")
+        sc = W.torch_column_scales(gen, 2048, "cuda")
+        x = W.torch_rows(gen, 32768, 2048, sc, "bf16", "cuda")
+        ridx = torch.from_numpy(row_idx).cuda()
+        hsx = [hs.Hessian(2048, torch.bfloat16, staging_bytes=0) for _ in range(64)]  # grouped updates only
+        outs = torch.empty((2048, 2048), dtype=torch.float32, device="cuda")
 
-    def moe_once():
-        for h in hsx:
-            h.reset()
-        hs.add_batch_grouped(hsx, x, offsets, ridx)
-        for h in hsx:
-            h.materialize(0.01, out=outs)
+        def moe_once():
+            for h in hsx:
+                h.reset()
+            hs.add_batch_grouped(hsx, x, offsets, ridx)
+            for h in hsx:
+                h.materialize(0.01, out=outs)
 
-    moe_once()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e2 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        for h in hsx:
-            h.reset()
-        hs.add_batch_grouped(hsx, x, offsets, ridx)
-    e1.record()
-    torch.cuda.synchronize()
-    grouped_ms = e0.elapsed_time(e1) / steps
-    e0.record()
-    for _ in range(steps):
         moe_once()
-    e2.record()
-    torch.cuda.synchronize()
-    total_ms = e0.elapsed_time(e2) / steps
-    fl = sum(syrk_flops(2048, int(offsets[e + 1] - offsets[e])) for e in range(64))
-    extra["moe_64x2048_grouped"] = {"ms_total": round(total_ms, 3), "ms_reset_plus_grouped": round(grouped_ms, 3),
-                                    "tflops_grouped": round(fl / grouped_ms / 1e9, 1),
-                                    "rows": int(offsets[-1])}
-    for h in hsx:
-        h.close()
-    del x, ridx
-    # local 16x16 blocks: 32768 x 4096 bf16, 16 distinct buffers cycled
-    log("local blocks")
-    gen = W.torch_generator(4, "cuda")
-    sc = W.torch_column_scales(gen, 4096, "cuda")
-    xs = [W.torch_rows(gen, 32768, 4096, sc, "bf16", "cuda") for _ in range(16)]
-    out = torch.zeros((256, 16, 16), dtype=torch.float32, device="cuda")
-    for xx in xs[:2]:
-        hs.local_blocks(xx, out=out)
-    torch.cuda.synchronize()
-    e0.record()
-    reps = 4
-    for _ in range(reps):
-        for xx in xs:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e2 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            for h in hsx:
+                h.reset()
+            hs.add_batch_grouped(hsx, x, offsets, ridx)
+        e1.record()
+        torch.cuda.synchronize()
+        grouped_ms = e0.elapsed_time(e1) / steps
+        e0.record()
+        for _ in range(steps):
+            moe_once()
+        e2.record()
+        torch.cuda.synchronize()
+        total_ms = e0.elapsed_time(e2) / steps
+        fl = sum(syrk_flops(2048, int(offsets[e + 1] - offsets[e])) for e in range(64))
+        extra["moe_64x2048_grouped"] = {"ms_total": round(total_ms, 3), "ms_reset_plus_grouped": round(grouped_ms, 3),
+                                        "tflops_grouped": round(fl / grouped_ms / 1e9, 1),
+                                        "rows": int(offsets[-1])}
+        for h in hsx:
+            h.close()
+        del x, ridx
+    if "local" in want:
+        # local 16x16 blocks: 32768 x 4096 bf16, 16 distinct buffers cycled
+        log("local blocks")
+        gen = W.torch_generator(4, "cuda")
+        sc = W.torch_column_scales(gen, 4096, "cuda")
+        xs = [W.torch_rows(gen, 32768, 4096, sc, "bf16", "cuda") for _ in range(16)]
+        out = torch.zeros((256, 16, 16), dtype=torch.float32, device="cuda")
+        for xx in xs[:2]:
             hs.local_blocks(xx, out=out)
-    e1.record()
-    torch.cuda.synchronize()
-    per = e0.elapsed_time(e1) / (reps * 16)
-    byts = 32768 * 4096 * 2 + 256 * 256 * 4 * 2
-    extra["local_32768x4096"] = {"ms_per_update": round(per, 4), "GBps": round(byts / per / 1e6, 1),
-                                 "hbm_frac": round(byts / (per * 1e-3) / HBM, 4), "pages_rtx_pro_6000_ms": 0.40}
-    del xs
+        torch.cuda.synchronize()
+        e0.record()
+        reps = 4
+        for _ in range(reps):
+            for xx in xs:
+                hs.local_blocks(xx, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        per = e0.elapsed_time(e1) / (reps * 16)
+        byts = 32768 * 4096 * 2 + 256 * 256 * 4 * 2
+        extra["local_32768x4096"] = {"ms_per_update": round(per, 4), "GBps": round(byts / per / 1e6, 1),
+                                     "hbm_frac": round(byts / (per * 1e-3) / HBM, 4), "pages_rtx_pro_6000_ms": 0.40}
+        del xs
     torch.cuda.empty_cache()
     return extra
 

@@ -47,8 +47,8 @@ struct SyrkParams {
 // One launch of the 256-tile SYRK (bf16, 16-byte aligned rows, d % 8 == 0).
 // Tiles order[0 .. dp_tiles) are done whole, one workgroup each (dp_tiles a
 // multiple of 256).  Each of the other sk_tiles tiles is cut into `parts`
-// aligned token ranges of part_len 32-token iterations (item = tile * parts +
-// part); workgroup w < grid_sk does item w, and the items past grid_sk
+// aligned token ranges of part_len 32-token iterations (item = part *
+// sk_tiles + tile); workgroup w < grid_sk does item w, and the items past grid_sk
 // ("excess", excess_total iterations in all) are shared out evenly over the
 // grid_sk workgroups as pieces.  Part 0 of a tile adds into S directly; the
 // other parts and all pieces go to workspace slots, which a fixup kernel adds

@@ -295,8 +295,9 @@ __global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) {
 
   // work of this workgroup: one whole tile (the first dp_tiles tiles of the
   // order, XCD by XCD), or one aligned part of a tile plus a share of the
-  // excess parts.  Consecutive workgroups of an XCD take consecutive items,
-  // so at any time they read the same token range of a few panels.
+  // excess parts.  Items are numbered part-major (item = part * sk_tiles +
+  // tile) and consecutive workgroups of an XCD take consecutive items, so an
+  // XCD's workgroups read the same token range of neighbouring tiles' panels.
   const int bid = blockIdx.x;
   if (bid < P.dp_tiles) {
     const int per = P.dp_tiles / 8;
@@ -306,7 +307,7 @@ __global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) {
   const int b = bid - P.dp_tiles;
   const int w = (P.grid_sk % 8 == 0) ? (b & 7) * (P.grid_sk / 8) + (b >> 3) : b;
   {
-    const int t = w / P.parts, p = w - t * P.parts;
+    const int p = w / P.sk_tiles, t = w - p * P.sk_tiles;
     const int k0 = p * P.part_len;
     const int k1 = min(P.niter, k0 + P.part_len);
     if (k0 < k1) segment(P.dp_tiles + t, k0, k1, (P.parts == 1 || p == 0) ? -1 : w);
@@ -319,7 +320,7 @@ __global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) {
       const int off = (int)(q - (int64_t)e * P.part_len);
       const int len = (int)min(qend - (int64_t)e * P.part_len, (int64_t)P.part_len) - off;
       const int item = P.grid_sk + e;
-      const int t = item / P.parts, p = item - t * P.parts;
+      const int p = item / P.sk_tiles, t = item - p * P.sk_tiles;
       // iterations past the batch (the last part of a tile may be short)
       // read empty ranges and add zeros
       segment(P.dp_tiles + t, p * P.part_len + off, p * P.part_len + off + len, P.grid_sk + w + e);
@@ -346,7 +347,7 @@ __global__ void __launch_bounds__(256) syrk_big_fixup(BigParams P) {
   if (threadIdx.x == 0) {
     int cnt = 0;
     for (int p = 0; p < P.parts; ++p) {
-      const int item = t * P.parts + p;
+      const int item = p * P.sk_tiles + t;
       if (item < P.grid_sk) {
         // a main item; part 0 wrote S itself, empty parts wrote nothing
         if (p > 0 && p * P.part_len < P.niter && cnt < kMaxSlots) slots[cnt++] = item;
