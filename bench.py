@@ -204,12 +204,15 @@ def main():
     _, _, _, kt = time_hessian(torch, hs, d, views, args.steps, 1, torch.bfloat16, kernel_timing=True)
     flops = syrk_flops(d, N)
     tflops = flops / (ms * 1e-3) / 1e12
-    # Roofline of the dominant kernel, the SYRK pass (a dense bf16 contraction):
+    # Roofline of the dominant kernel, the SYRK pass of each staging flush (a
+    # dense bf16 contraction, on 256-tiles at this width and flush length):
     # algorithmic flops of the tokens each launch processed, N d (d + 1), over
-    # the launches' HIP-event durations, against the dense bf16 MFMA peak.
+    # the launches' HIP-event durations (main kernel), against the dense bf16
+    # MFMA peak.
     launches, ktok, kms = kt
     achieved = syrk_flops(d, ktok) / (kms * 1e-3)
-    traffic = read_traffic(os.path.join(ROOT, "profiles", "syrk_bf16_d2560_ragged_traffic.txt"))
+    traffic = read_traffic(os.path.join(ROOT, "profiles", "syrk_big_bf16_d2560_ragged_traffic.txt"),
+                           BIG_KERNEL_SOURCES)
     result = {
         "metric": METRIC,
         "value": round(ms, 4),
@@ -235,7 +238,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": P_BF16 / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved / P_BF16, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "kernel": "syrk_bf16_buffer (hess_add_batch SYRK pass)",
+                     "kernel": "syrk_big_bf16 (256-tile SYRK main kernel of each staging flush)",
                      "launches_per_hessian": round(launches / args.steps, 2),
                      "mean_launch_us": round(kms * 1e3 / launches, 2),
                      "tokens_per_launch": round(ktok / launches, 1)},

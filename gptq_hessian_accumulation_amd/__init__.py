@@ -157,7 +157,7 @@ class Hessian:
     ``dtype`` is the activation element type every batch will have
     (``torch.bfloat16`` or ``torch.float32``); the Hessian is always float32.
     ``staging_bytes`` sizes the buffer that collects short batches (default:
-    256 MiB for bf16 at d >= 3072, else 64 MiB; 0 disables staging).
+    512 MiB for bf16 at d >= 1024, else 64 MiB; 0 disables staging).
     """
 
     def __init__(self, d: int, dtype=torch.bfloat16, staging_bytes: int | None = None):

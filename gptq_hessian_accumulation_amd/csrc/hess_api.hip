@@ -194,7 +194,7 @@ hipError_t timing_end(hess_t h, hipStream_t s, int64_t n) {
 constexpr int kBig = 256;
 constexpr int kBigKI = 32;               // tokens per iteration
 constexpr int kBigMinD = 1024;           // automatic choice: widths at least this wide ...
-constexpr int64_t kBigMinWork = 400;     // ... and at least this many iterations per workgroup
+constexpr int64_t kBigMinWork = 300;     // ... and at least this many iterations per workgroup
 
 bool big_capable(int64_t d, int dtype) { return dtype == HESS_BF16 && d % 8 == 0 && d >= 8 && d <= 32768; }
 
@@ -217,10 +217,10 @@ int64_t big_slots(int ntiles) { return ntiles % kCUs ? 2 * kCUs + ntiles % kCUs 
 
 // The 256-tile kernel has a fixed cost per launch (its parts' workspace
 // round trip and fixup, its imbalance when tiles split into many parts), so
-// it is chosen once each workgroup gets at least 400 iterations of 32
-// tokens; measured on MI355X with N(0,1)-scaled bf16 data: width 4,096 with
-// 32,768 tokens (544 per workgroup) takes 0.50 ms against 0.74 ms on
-// 128-tiles, while width 2,560 with 26,112 tokens (175 per workgroup) is
+// it is chosen once each workgroup gets at least 300 iterations of 32
+// tokens.  Measured on MI355X with N(0,1)-scaled bf16 data: width 2,560 with
+// 52,224 tokens (350 per workgroup) takes 398 us against 436 us for four
+// 128-tile passes of 13,056, and with 26,112 tokens (175 per workgroup) is
 // slower than two 128-tile passes.
 bool use_big(const hess_s* h, int64_t n, bool vec) {
   if (!h->order256 || !vec) return false;
@@ -369,11 +369,13 @@ int hess_set_tile_override(int edge) {
   return HESS_OK;
 }
 
-// Default staging: large enough at widths >= 3,072 (bf16) that a flush runs
-// on 256-tiles (32,768 tokens at 4,096); 64 MiB otherwise, where flushes run
-// on 128-tiles and the buffer stays resident in the 256 MB Infinity Cache.
+// Default staging: for bf16 at widths >= 1,024, 512 MiB, so that a flush
+// is long enough for the 256-tile kernel (104,448 tokens at 2,560: one ragged
+// calibration Hessian of ~375K tokens takes 4 passes; measured 3.8 ms per
+// Hessian against 4.8 ms with 64 MiB staging and 128-tile passes); 64 MiB
+// otherwise.
 int64_t default_staging(int64_t d, int in_dtype) {
-  return (in_dtype == HESS_BF16 && d >= 3072) ? HESS_STAGING_DEFAULT : ((int64_t)64 << 20);
+  return (in_dtype == HESS_BF16 && d >= 1024) ? HESS_STAGING_DEFAULT : ((int64_t)64 << 20);
 }
 
 hess_t hess_create(int64_t d, int in_dtype) { return hess_create_ex(d, in_dtype, default_staging(d, in_dtype)); }
