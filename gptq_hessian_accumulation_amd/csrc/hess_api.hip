@@ -35,7 +35,12 @@ struct hess_s {
   void* stage = nullptr;     // thin-batch staging rows (stage_cap x stage_ld elements)
   int64_t stage_cap = 0;     // tokens
   int64_t stage_ld = 0;      // row stride in elements (d rounded up to 8)
-  int64_t stage_n = 0;       // tokens staged, not yet in S
+  int64_t stage_n = 0;       // tokens staged, not yet in S (with the zero rows of stage_t8)
+  int64_t stage_real = 0;    // ... of which batch rows
+  // bf16 staging in the transposed layout of the 256-tile kernel: 8-token
+  // blocks of d 16-byte chunks (8 tokens of one feature), each batch padded
+  // with zero rows to a multiple of 8; always flushed by that kernel
+  bool stage_t8 = false;
   int64_t N = 0;
   bool consumed = false;     // in-place materialize done
   bool has_stream = false;
@@ -232,9 +237,13 @@ bool use_big(const hess_s* h, int64_t n, bool vec) {
 
 // The timing events (hess_set_timing) bracket the main kernel, which does
 // all the multiplications; the fixup that adds the stream-K pieces follows it.
-int run_big(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s) {
+//
+// t8: X is a transposed staging buffer (ld = chunks per 8-token block, n a
+// multiple of 8); n_real = rows that are batch rows, for the timing record.
+int run_big(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s, bool t8 = false, int64_t n_real = -1) {
   BigParams B;
   std::memset(&B, 0, sizeof(B));
+  B.t8 = t8 ? 1 : 0;
   B.X = X;
   B.ld = ld;
   B.S = h->S;
@@ -279,7 +288,7 @@ int run_big(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s) {
   e = launch_syrk_big(B, s);
   if (e != hipSuccess) return hip_fail(e, "256-tile SYRK launch");
   if (h->timing) {
-    e = timing_end(h, s, n);
+    e = timing_end(h, s, n_real >= 0 ? n_real : n);
     if (e != hipSuccess) return hip_fail(e, "timing event");
   }
   e = launch_syrk_big_fixup(B, s);
@@ -338,8 +347,9 @@ int run_syrk(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s) {
 // Fold the staged rows into S.
 int flush_stage(hess_t h, hipStream_t s) {
   if (h->stage_n == 0) return HESS_OK;
-  const int rc = run_syrk(h, h->stage, h->stage_n, h->stage_ld, s);
-  if (rc == HESS_OK) h->stage_n = 0;
+  const int rc = h->stage_t8 ? run_big(h, h->stage, h->stage_n, h->d, s, true, h->stage_real)
+                             : run_syrk(h, h->stage, h->stage_n, h->stage_ld, s);
+  if (rc == HESS_OK) h->stage_n = h->stage_real = 0;
   return rc;
 }
 
@@ -442,6 +452,13 @@ hess_t hess_create_ex(int64_t d, int in_dtype, int64_t staging_bytes) {
         if (e == hipSuccess) W.slots = need;
       }
     }
+    // transposed staging when a full buffer's flush takes the 256-tile
+    // kernel (with the tile override at create: 256 always, 128 never)
+    if (h->stage_cap > 0 && g_tile_override != kTile) {
+      const int64_t niter = h->stage_cap / kBigKI;
+      h->stage_t8 = g_tile_override == kBig ||
+                    (d >= kBigMinD && (int64_t)h->ntiles256 * niter >= kBigMinWork * kCUs);
+    }
   }
   if (e == hipSuccess) e = hipMemset(h->S, 0, sbytes);
   if (e == hipSuccess) e = hipMemset(h->damp, 0, 64);
@@ -493,14 +510,17 @@ int hess_add_batch(hess_t h, const void* X, int64_t n_tokens, int64_t ld, hess_s
   if (rc != HESS_OK) return rc;
   if (stage_pays(h, n_tokens)) {
     // thin batch: append its rows to the staging buffer
-    if (h->stage_n + n_tokens > h->stage_cap) {
+    const int64_t rows = h->stage_t8 ? (n_tokens + 7) / 8 * 8 : n_tokens;
+    if (h->stage_n + rows > h->stage_cap) {
       rc = flush_stage(h, s);
       if (rc != HESS_OK) return rc;
     }
     char* dst = static_cast<char*>(h->stage) + h->stage_n * h->stage_ld * esize(h->dtype);
-    hipError_t e = launch_copy_rows(X, ld, esize(h->dtype), n_tokens, h->d, dst, h->stage_ld, s);
+    hipError_t e = h->stage_t8 ? launch_copy_rows_t8(X, ld, n_tokens, h->d, dst, s)
+                               : launch_copy_rows(X, ld, esize(h->dtype), n_tokens, h->d, dst, h->stage_ld, s);
     if (e != hipSuccess) return hip_fail(e, "staging copy launch");
-    h->stage_n += n_tokens;
+    h->stage_n += rows;
+    h->stage_real += n_tokens;
   } else {
     // long batch: its own SYRK pass, after whatever is staged
     rc = flush_stage(h, s);
@@ -615,7 +635,7 @@ int hess_reset(hess_t h, hess_stream_t stream) {
   if (rc != HESS_OK) return rc;
   hipError_t e = launch_zero(h->S, h->d * h->d, s);
   if (e != hipSuccess) return hip_fail(e, "reset launch");
-  h->stage_n = 0;
+  h->stage_n = h->stage_real = 0;
   h->N = 0;
   h->consumed = false;
   return HESS_OK;

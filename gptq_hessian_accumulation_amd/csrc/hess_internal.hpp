@@ -54,7 +54,9 @@ struct SyrkParams {
 // other parts and all pieces go to workspace slots, which a fixup kernel adds
 // into S in a fixed order.
 struct BigParams {
-  const void* X;          // tokens x features, row stride ld elements
+  const void* X;          // tokens x features, row stride ld elements; with t8, the transposed
+                          // staging layout: 8-token blocks of ld 16-byte chunks (chunk f of
+                          // block b = tokens 8b..8b+7 of feature f), n a multiple of 8
   int64_t ld;
   float* S;               // row stride lds
   int64_t lds;
@@ -72,6 +74,7 @@ struct BigParams {
   int part_len;
   int items;              // sk_tiles * parts
   int grid_sk;            // workgroups after the whole-tile ones (<= items)
+  int t8;                 // X is in the transposed staging layout
 };
 
 hipError_t launch_syrk_big(const BigParams& P, hipStream_t stream);
@@ -91,6 +94,11 @@ hipError_t launch_local_blocks(const void* X, int in_dtype, int64_t n, int d, in
                                int accumulate, hipStream_t stream);
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
+
+// Transposed staging copy (bf16): n rows of X (row stride ld) into 8-token
+// blocks at dst, chunk f of block b = tokens 8b..8b+7 of feature f (16
+// bytes), blocks of d chunks; rows n .. round_up(n, 8) - 1 are written as zeros.
+hipError_t launch_copy_rows_t8(const void* X, int64_t ld, int64_t n, int64_t d, void* dst, hipStream_t stream);
 
 // Copy n rows of d elements (esize bytes each) from X (row stride ld) to dst (row stride dld).
 hipError_t launch_copy_rows(const void* X, int64_t ld, int esize, int64_t n, int64_t d, void* dst, int64_t dld,

@@ -10,7 +10,14 @@
 //
 // The copy is a bandwidth kernel: 16-byte vector moves when rows allow it,
 // element moves otherwise.
+//
+// bf16 handles whose flushes take the 256-tile kernel stage in that kernel's
+// operand layout instead: 8-token blocks, each d 16-byte chunks holding 8
+// consecutive tokens of one feature (the k-run of one matrix-core operand
+// lane), with every batch padded by zero rows to a multiple of 8 tokens.
+// Zero rows add nothing to the Gram sum.
 
+#include "hess_device.hpp"
 #include "hess_internal.hpp"
 
 namespace hess {
@@ -52,7 +59,66 @@ __global__ void __launch_bounds__(256) copy_rows_elem(const E* X, int64_t ld, E*
   }
 }
 
+// Transposed staging copy, 16-byte aligned rows: workgroup (g, F) moves
+// tokens 8g..8g+7 (zeros past n) of features F..F+255.  Its 256 threads read
+// the 8 x 512-byte row pieces into LDS with 16-byte loads, then thread t
+// gathers feature F + t's 8 tokens and writes them as one chunk, so that
+// both the reads and the writes are contiguous across the workgroup.
+__global__ void __launch_bounds__(256) copy_rows_t8(const char* X, int64_t ld_bytes, char* dst, int64_t n, int d,
+                                                    int fq) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[8][256];
+  const int t = threadIdx.x;
+  const int64_t g = blockIdx.x / fq;
+  const int F = (int)(blockIdx.x - g * fq) * 256;
+  {
+    const int r = t >> 5, q = t & 31;
+    const int64_t tok = 8 * g + r;
+    const int f = F + 8 * q;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (tok < n && f < d) v = *reinterpret_cast<const u32x4*>(X + tok * ld_bytes + (int64_t)f * 2);
+    *reinterpret_cast<u32x4*>(&tile[r][8 * q]) = v;
+  }
+  __syncthreads();
+  const int f = F + t;
+  if (f < d) {
+    u32x4 c;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) c[p] = (uint32_t)tile[2 * p][t] | ((uint32_t)tile[2 * p + 1][t] << 16);
+    *reinterpret_cast<u32x4*>(dst + (g * d + f) * 16) = c;
+  }
+}
+
+// Transposed staging copy, any alignment: one element per thread.
+__global__ void __launch_bounds__(256) copy_rows_t8_elem(const uint16_t* X, int64_t ld, uint16_t* dst, int64_t n,
+                                                         int64_t d, int64_t total) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / d, f = i - t * d;
+    dst[((t >> 3) * d + f) * 8 + (t & 7)] = t < n ? X[t * ld + f] : (uint16_t)0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_copy_rows_t8(const void* X, int64_t ld, int64_t n, int64_t d, void* dst, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (d % 8 != 0) return hipErrorInvalidValue;
+  const int64_t blocks8 = (n + 7) / 8;
+  const bool vec = (reinterpret_cast<uintptr_t>(X) & 15u) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0 &&
+                   ((ld * 2) & 15) == 0;
+  const int64_t fq = (d + 255) / 256;
+  const int64_t wgs = blocks8 * fq;
+  if (vec && wgs < ((int64_t)1 << 31)) {
+    hipLaunchKernelGGL(copy_rows_t8, dim3((unsigned)wgs), dim3(256), 0, stream, static_cast<const char*>(X), ld * 2,
+                       static_cast<char*>(dst), n, (int)d, (int)fq);
+  } else {
+    const int64_t elems = blocks8 * 8 * d;
+    int64_t blocks = (elems + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(copy_rows_t8_elem, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(X), ld, static_cast<uint16_t*>(dst), n, d, elems);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_copy_rows(const void* X, int64_t ld, int esize, int64_t n, int64_t d, void* dst, int64_t dld,
                             hipStream_t stream) {

@@ -19,19 +19,27 @@
 //    that each accumulator register holds part of a row (float4 output).
 //  * Activations go from memory straight into LDS (buffer_load_dwordx4 with
 //    the lds modifier): no registers hold loads and no VALU transposes them.
-//    LDS keeps each 32-token stage token-major (a 512-byte row of 256
-//    features per token) with its 16-byte chunks XOR-swizzled; the matrix
-//    operands (8 consecutive tokens of one feature) are read transposed with
-//    ds_read_b64_tr_b16, two per operand.  The swizzle makes both the 64-lane
-//    DMA writes (1 KB contiguous each) and the transposed reads free of bank
-//    conflicts.
+//    Row-major X: LDS keeps each 32-token stage token-major (a 512-byte row
+//    of 256 features per token) with its 16-byte chunks XOR-swizzled; the
+//    matrix operands (8 consecutive tokens of one feature) are read
+//    transposed with ds_read_b64_tr_b16, two per operand.  The swizzle makes
+//    both the 64-lane DMA writes (1 KB contiguous each) and the transposed
+//    reads free of bank conflicts.  A staging buffer in the transposed
+//    layout (8-token chunks of one feature, written so by the staging copy)
+//    lands in LDS operand-ready: one ds_read_b128 per operand, 32 lanes
+//    reading 512 contiguous bytes.
+//  * The loads are written as inline asm (m0 is an input operand) and
+//    placed by hand among the matrix instructions of each iteration's second
+//    half.  The compiler neither tracks nor waits for them; the kernel's own
+//    s_waitcnt before each barrier and before the output are the only
+//    waits, which is also what the loads need.
 //  * Five LDS stages of 32 tokens (5 x 32 KB, all of the CU's LDS): the
 //    loads of up to four iterations are in flight while one is multiplied;
 //    one barrier per iteration, placed between the two 16-token halves so
 //    that the matrix cores keep running while a wave waits there and while
-//    the next stage's first operands are read.  Each stage is its own LDS
-//    variable and the barrier is the bare s_barrier, so the compiler waits
-//    only for the stage about to be read (vmcnt), not for all loads.
+//    the next stage's first operands are read.  The barrier is the bare
+//    s_barrier after an explicit vmcnt wait for this wave's loads of the
+//    stage about to be read.
 //  * Loads never need masks: each iteration's buffer descriptor ends at the
 //    batch's last row (rows past it read zero), features past d get an
 //    out-of-range offset (zero), and iterations past a segment read an empty
@@ -80,6 +88,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(uint64_t base, int64
                                            0x00020000);
 }
 
+// The same descriptor as four scalar words, for the load instruction written out.
+__device__ __forceinline__ u32x4 rsrc_words(uint64_t base, int64_t bytes) {
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) & 0xffffu;
+  r[2] = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// One 64-lane 16-byte load from memory into LDS at m0 + 16 * lane (zeros
+// for offsets past the descriptor's range).  m0 is set by the compiler as
+// an input operand; the s_nop covers the m0-write to LDS-DMA hazard.
+__device__ __forceinline__ void lds_dma16(const u32x4& r, uint32_t voff, uint32_t m0) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
+}
+
 __device__ __forceinline__ u32x4 tr_pair(const char* p) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HESS_LDS s16x4*)(p));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HESS_LDS s16x4*)(p + 4 * kRowB));
@@ -93,12 +118,20 @@ __device__ __forceinline__ int64_t excess_start(const BigParams& P, int w) {
   return (int64_t)w * P.excess_total / P.grid_sk;
 }
 
-__global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) {
+template <bool T8>
+__device__ __forceinline__ void big_body(const BigParams& P) {
   __shared__ __attribute__((aligned(1024))) char st0[kStageB];
   __shared__ __attribute__((aligned(1024))) char st1[kStageB];
   __shared__ __attribute__((aligned(1024))) char st2[kStageB];
   __shared__ __attribute__((aligned(1024))) char st3[kStageB];
   __shared__ __attribute__((aligned(1024))) char st4[kStageB];
+
+  // LDS addresses of the stages, for the load instructions' m0
+  const uint32_t L0 = (uint32_t)reinterpret_cast<uintptr_t>((HESS_LDS char*)st0);
+  const uint32_t L1 = (uint32_t)reinterpret_cast<uintptr_t>((HESS_LDS char*)st1);
+  const uint32_t L2 = (uint32_t)reinterpret_cast<uintptr_t>((HESS_LDS char*)st2);
+  const uint32_t L3 = (uint32_t)reinterpret_cast<uintptr_t>((HESS_LDS char*)st3);
+  const uint32_t L4 = (uint32_t)reinterpret_cast<uintptr_t>((HESS_LDS char*)st4);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -119,47 +152,96 @@ __global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) {
     offA[m] = tl * kRowB + (((4 * (4 * wr + m) + el) ^ kl) << 4) + bl;
     offB[m] = tl * kRowB + (((4 * (4 * wc + m) + el) ^ kl) << 4) + bl;
   }
+  // transposed staging: this lane's chunks in panels A and B (row l / 32)
+  const int t8A = (lane >> 5) * 4096 + (128 * wr + (lane & 31)) * 16;
+  const int t8B = (lane >> 5) * 4096 + (128 * wc + (lane & 31)) * 16;
 
   auto segment = [&](int tile, int k0, int k1, int slot) {
     f32x16 acc[4][4];
     const int code = P.order[tile];
     const int I = code >> 16, J = code & 0xffff;
     const bool diag = I == J;
+    // on a diagonal tile the below-diagonal quadrant's wave only loads
     const bool active = !(diag && wr == 1 && wc == 0);
 
     // DMA offsets: wave w loads 1-KB blocks gb = 8w + i of a stage (panel
-    // gb / 16, token rows 2*(gb % 16) and +1); lane j fills bytes 16j..16j+15
+    // gb / 16); lane j fills bytes 16j..16j+15.  Row-major X: block gb holds
+    // token rows 2*(gb % 16) and +1.  Transposed staging: the panel is 4
+    // rows (8-token blocks) of 256 16-byte chunks (8 tokens of one feature);
+    // block gb holds features 64*(gb % 4) .. +63 of row (gb % 16) / 4.
     uint32_t voff[kDma];
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
       const int gb = kDma * wave + i;
       const int p = gb >> 4, b = gb & 15;
-      const int t = 2 * b + (lane >> 5);
-      const int f = (p ? J : I) * kT + 8 * chunk_at(t, lane & 31);
-      voff[i] = (f < P.d && !(p && diag)) ? (uint32_t)t * row_bytes + (uint32_t)f * 2u : kOOB;
+      if constexpr (T8) {
+        const int c = b >> 2;
+        const int f = (p ? J : I) * kT + 64 * (b & 3) + lane;
+        voff[i] = (f < P.d && !(p && diag)) ? ((uint32_t)c * (uint32_t)P.ld + (uint32_t)f) * 16u : kOOB;
+      } else {
+        const int t = 2 * b + (lane >> 5);
+        const int f = (p ? J : I) * kT + 8 * chunk_at(t, lane & 31);
+        voff[i] = (f < P.d && !(p && diag)) ? (uint32_t)t * row_bytes + (uint32_t)f * 2u : kOOB;
+      }
     }
+    // the iteration's tokens: rows (row-major X) or 8-token blocks of ld
+    // chunks (transposed staging, n a multiple of 8)
     auto desc = [&](int j) {
       const int64_t tok = (int64_t)j * kKI;
       const int64_t valid = j < k1 ? max((int64_t)0, min((int64_t)kKI, P.n - tok)) : 0;
-      const uint64_t base = reinterpret_cast<uint64_t>(P.X) + (uint64_t)tok * row_bytes;
-      return make_rsrc(base, valid * row_bytes);
+      if constexpr (T8) {
+        const uint64_t blk = (uint64_t)P.ld * 16u;
+        return rsrc_words(reinterpret_cast<uint64_t>(P.X) + (uint64_t)(tok / 8) * blk,
+                          ((valid + 7) / 8) * (int64_t)blk);
+      } else {
+        const uint64_t base = reinterpret_cast<uint64_t>(P.X) + (uint64_t)tok * row_bytes;
+        return rsrc_words(base, valid * row_bytes);
+      }
     };
-    auto issue = [&](char* stage, __amdgpu_buffer_rsrc_t r) {
-      char* dst = stage + wave * (kDma * 1024);
+    // load i of this wave's 8 for a stage at LDS address stage_lds
+    auto dma1 = [&](uint32_t stage_lds, const u32x4& r, int i) {
+      lds_dma16(r, voff[i], stage_lds + (uint32_t)(wave * (kDma * 1024) + i * 1024));
+    };
+    auto issue = [&](uint32_t stage_lds, const u32x4& r) {
 #pragma unroll
-      for (int i = 0; i < kDma; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (HESS_LDS void*)(dst + i * 1024), 16, voff[i], 0, 0, 0);
+      for (int i = 0; i < kDma; ++i) dma1(stage_lds, r, i);
     };
-    auto dma = [&](char* stage, int j) { issue(stage, desc(j)); };
+    auto dma = [&](uint32_t stage_lds, int j) { issue(stage_lds, desc(j)); };
     // operands of one 16-token half (ks) of a stage: A blocks of this wave's
     // rows, B blocks of its columns
     auto rd = [&](const char* stage, int ks, u32x4 (&a)[4], u32x4 (&b)[4]) {
-      const char* pa = stage + ks * 16 * kRowB;
-      const char* pb = (diag ? stage : stage + kPanelB) + ks * 16 * kRowB;
+      if constexpr (T8) {
+        // one 16-byte read per operand: row 2 ks + l/32 of the panel, the
+        // chunk of its feature (32 consecutive lanes read 512 contiguous bytes)
+        const char* pa = stage + ks * 2 * 4096;
+        const char* pb = (diag ? stage : stage + kPanelB) + ks * 2 * 4096;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) a[m] = tr_pair(pa + offA[m]);
+        for (int m = 0; m < 4; ++m) a[m] = *reinterpret_cast<const u32x4*>(pa + t8A + m * 32 * 16);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) b[m] = tr_pair(pb + offB[m]);
+        for (int m = 0; m < 4; ++m) b[m] = *reinterpret_cast<const u32x4*>(pb + t8B + m * 32 * 16);
+      } else {
+        const char* pa = stage + ks * 16 * kRowB;
+        const char* pb = (diag ? stage : stage + kPanelB) + ks * 16 * kRowB;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] = tr_pair(pa + offA[m]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) b[m] = tr_pair(pb + offB[m]);
+      }
+    };
+    // operand j of one half: A block j (j < 4) or B block j - 4
+    auto rd1 = [&](const char* stage, int ks, int j, u32x4 (&a)[4], u32x4 (&b)[4]) {
+      const int m = j & 3;
+      if constexpr (T8) {
+        const char* pa = stage + ks * 2 * 4096;
+        const char* pb = (diag ? stage : stage + kPanelB) + ks * 2 * 4096;
+        if (j < 4) a[m] = *reinterpret_cast<const u32x4*>(pa + t8A + m * 32 * 16);
+        else b[m] = *reinterpret_cast<const u32x4*>(pb + t8B + m * 32 * 16);
+      } else {
+        const char* pa = stage + ks * 16 * kRowB;
+        const char* pb = (diag ? stage : stage + kPanelB) + ks * 16 * kRowB;
+        if (j < 4) a[m] = tr_pair(pa + offA[m]);
+        else b[m] = tr_pair(pb + offB[m]);
+      }
     };
     auto mm = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
 #pragma unroll
@@ -180,13 +262,18 @@ __global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) {
     // during the previous iteration.  Multiply the first half while reading
     // the second; then wait for my loads of iteration i + 1 and meet the
     // other waves (after that barrier stage i + 1 is complete and nobody
-    // reads stage i - 1 any more), multiply the second half while reading
-    // the first half of stage i + 1, and start the loads of iteration i + 4
-    // into stage i - 1.  The load descriptor is built before the barrier.
+    // reads stage i - 1 any more), and multiply the second half while
+    // reading the first half of stage i + 1 and starting the loads of
+    // iteration i + 4 into stage i - 1: after each pair of matrix
+    // instructions one operand read and one load.  A load instruction waits
+    // at issue until the CU's address unit takes it; spread out this way the
+    // wait holds up at most one matrix instruction (issued back to back, the
+    // four waves' 32 loads kept each wave from the matrix cores for ~350
+    // cycles of every ~1,800).  The descriptor is built before the barrier.
     // Iterations past the segment multiply the zeros their empty loads wrote.
     u32x4 xa[4], xb[4], ya[4], yb[4];
-    auto step = [&](const char* cur, const char* nxt, char* dtgt, int i) {
-      const __amdgpu_buffer_rsrc_t r = desc(k0 + i + 4);
+    auto step = [&](const char* cur, const char* nxt, uint32_t dtgt, int i) {
+      const u32x4 r = desc(k0 + i + 4);
       if (active) {
         rd(cur, 1, ya, yb);
         mm(xa, xb);
@@ -197,14 +284,18 @@ __global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) {
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       if (active) {
-        mm(ya, yb);
-        rd(nxt, 0, xa, xb);
-        interleave();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int m = j >> 1, n = 2 * (j & 1);
+          acc[m][n] = mfma32x32x16(yb[n], ya[m], acc[m][n]);
+          acc[m][n + 1] = mfma32x32x16(yb[n + 1], ya[m], acc[m][n + 1]);
+          rd1(nxt, 0, j, xa, xb);
+          dma1(dtgt, r, j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        issue(dtgt, r);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // the loads of iteration i + 4, issued while the last matrix
-      // instructions run (after every read of the next stage)
-      issue(dtgt, r);
       __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -215,20 +306,20 @@ __global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) {
 
     // the previous segment's output stores leave the count before these loads
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    dma(st0, k0);
-    dma(st1, k0 + 1);
-    dma(st2, k0 + 2);
-    dma(st3, k0 + 3);
+    dma(L0, k0);
+    dma(L1, k0 + 1);
+    dma(L2, k0 + 2);
+    dma(L3, k0 + 3);
     __builtin_amdgcn_s_waitcnt(0x4F78);  // vmcnt(24): iteration k0 has landed
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (active) rd(st0, 0, xa, xb);
     for (int i = 0; i < k1 - k0; i += 5) {
-      step(st0, st1, st4, i);
-      step(st1, st2, st0, i + 1);
-      step(st2, st3, st1, i + 2);
-      step(st3, st4, st2, i + 3);
-      step(st4, st0, st3, i + 4);
+      step(st0, st1, L4, i);
+      step(st1, st2, L0, i + 1);
+      step(st2, st3, L1, i + 2);
+      step(st3, st4, L2, i + 3);
+      step(st4, st0, L3, i + 4);
     }
     // drain the trailing (empty-range) loads; every wave is done with the stages
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
@@ -298,24 +389,35 @@ __global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) {
   // excess parts.  Items are numbered part-major (item = part * sk_tiles +
   // tile) and consecutive workgroups of an XCD take consecutive items, so an
   // XCD's workgroups read the same token range of neighbouring tiles' panels.
+  // The pieces go through one loop with one call of segment, so that the
+  // main loop exists once in the code.
   const int bid = blockIdx.x;
-  if (bid < P.dp_tiles) {
-    const int per = P.dp_tiles / 8;
-    segment((bid & 7) * per + (bid >> 3), 0, P.niter, -1);
-    return;
-  }
+  const bool dp = bid < P.dp_tiles;
   const int b = bid - P.dp_tiles;
-  const int w = (P.grid_sk % 8 == 0) ? (b & 7) * (P.grid_sk / 8) + (b >> 3) : b;
-  {
-    const int p = w / P.sk_tiles, t = w - p * P.sk_tiles;
-    const int k0 = p * P.part_len;
-    const int k1 = min(P.niter, k0 + P.part_len);
-    if (k0 < k1) segment(P.dp_tiles + t, k0, k1, (P.parts == 1 || p == 0) ? -1 : w);
+  const int w = dp ? 0 : (P.grid_sk % 8 == 0) ? (b & 7) * (P.grid_sk / 8) + (b >> 3) : b;
+  int64_t q = 0, qend = 0;
+  if (!dp && P.excess_total > 0) {
+    q = excess_start(P, w);
+    qend = excess_start(P, w + 1);
   }
-  if (P.excess_total > 0) {
-    int64_t q = excess_start(P, w);
-    const int64_t qend = excess_start(P, w + 1);
-    while (q < qend) {
+  for (int piece = 0;; ++piece) {
+    int tile, k0, k1, slot;
+    if (piece == 0) {
+      if (dp) {
+        const int per = P.dp_tiles / 8;
+        tile = (bid & 7) * per + (bid >> 3);
+        k0 = 0;
+        k1 = P.niter;
+        slot = -1;
+      } else {
+        const int p = w / P.sk_tiles, t = w - p * P.sk_tiles;
+        tile = P.dp_tiles + t;
+        k0 = p * P.part_len;
+        k1 = min(P.niter, k0 + P.part_len);
+        slot = (P.parts == 1 || p == 0) ? -1 : w;
+      }
+    } else {
+      if (q >= qend) break;
       const int e = (int)(q / P.part_len);
       const int off = (int)(q - (int64_t)e * P.part_len);
       const int len = (int)min(qend - (int64_t)e * P.part_len, (int64_t)P.part_len) - off;
@@ -323,11 +425,22 @@ __global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) {
       const int p = item / P.sk_tiles, t = item - p * P.sk_tiles;
       // iterations past the batch (the last part of a tile may be short)
       // read empty ranges and add zeros
-      segment(P.dp_tiles + t, p * P.part_len + off, p * P.part_len + off + len, P.grid_sk + w + e);
+      tile = P.dp_tiles + t;
+      k0 = p * P.part_len + off;
+      k1 = k0 + len;
+      slot = P.grid_sk + w + e;
       q += len;
     }
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    k0 = __builtin_amdgcn_readfirstlane(k0);
+    k1 = __builtin_amdgcn_readfirstlane(k1);
+    slot = __builtin_amdgcn_readfirstlane(slot);
+    if (k0 < k1) segment(tile, k0, k1, slot);
   }
 }
+
+__global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) { big_body<false>(P); }
+__global__ void __launch_bounds__(256, 1) syrk_big_bf16_t8(BigParams P) { big_body<true>(P); }
 
 // S_tile += the other parts and the pieces of tile t, in item order (pieces
 // of one excess item in workgroup order): a fixed order, so results do not
@@ -398,7 +511,10 @@ __global__ void __launch_bounds__(256) syrk_big_fixup(BigParams P) {
 hipError_t launch_syrk_big(const BigParams& P, hipStream_t stream) {
   const int grid = P.dp_tiles + P.grid_sk;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(syrk_big_bf16, dim3(grid), dim3(256), 0, stream, P);
+  if (P.t8)
+    hipLaunchKernelGGL(syrk_big_bf16_t8, dim3(grid), dim3(256), 0, stream, P);
+  else
+    hipLaunchKernelGGL(syrk_big_bf16, dim3(grid), dim3(256), 0, stream, P);
   return hipGetLastError();
 }
 

@@ -103,6 +103,12 @@ hess_t hess_create(int64_t d, int in_dtype);
  * for bf16 handles with d >= 1024, so that a staged flush is long enough for
  * the 256-tile kernel (104,448 tokens at d = 2560), and 64 MiB otherwise.
  * A smaller buffer saves memory at the cost of more, shorter flushes.
+ * When a full buffer's flush would take the 256-tile kernel (bf16, d % 8 ==
+ * 0, d >= 1,024 and enough tokens; see hess_set_tile_override), the staged
+ * rows are kept in that kernel's operand layout: blocks of 8 tokens, each
+ * 16-byte chunk holding the 8 tokens of one feature, every batch padded
+ * with zero rows to a multiple of 8 (padding counts toward the capacity,
+ * not toward N).  Such a handle's flushes always run on 256-tiles.
  */
 hess_t hess_create_ex(int64_t d, int in_dtype, int64_t staging_bytes);
 
@@ -194,7 +200,10 @@ int hess_token_count(hess_t h, int64_t* n_out);
  * 256-tiles apply to bf16 handles with d % 8 == 0 and 16-byte aligned rows;
  * other calls keep 128-tiles.  The automatic choice takes 256-tiles at
  * d >= 1,024 when a pass (one batch, or one staging flush) gives each of
- * the 256 workgroups at least 300 iterations of 32 tokens. */
+ * the 256 workgroups at least 300 iterations of 32 tokens.  The setting at
+ * hess_create also fixes a handle's staging layout: 256 makes it the
+ * transposed one whenever the handle stages, 128 keeps rows (see
+ * hess_create_ex). */
 int hess_set_tile_override(int edge);
 
 /*

@@ -116,6 +116,58 @@ def test_big_tiles_ragged(d, staging):
     check_against_oracle(wl)
 
 
+@pytest.mark.parametrize("d", [1032, 2048])
+def test_transposed_staging_ragged(d):
+    """bf16 at widths >= 1,024 with the default staging buffer stages in the 256-tile kernel's
+    transposed layout: batch lengths that are not multiples of 8 (zero-padded blocks), a long
+    batch between staged ones (the staged rows are flushed first), and a final partial flush."""
+    _say(f"transposed staging ragged d={d}")
+    sizes = [1, 7, 9, 500, d - 1, 3, 2 * d + 5, 17, 800, 8, 0, 255]
+    wl = W.ragged_case(d, sizes, seed=500 + d, dtype=W.BF16, dead_frac=0.02)
+    check_against_oracle(wl)
+
+
+def test_transposed_staging_overflow():
+    """A 256-token transposed staging buffer (tile override 256 at create) overflows and is
+    flushed again and again; padded batch lengths count toward its capacity."""
+    _say("transposed staging overflow d=520")
+    hs.set_tile_override(256)
+    d = 520
+    wl = W.ragged_case(d, [100, 101, 99, 7, 250, 1, 249, 64, 65, 0, 200], seed=77, dtype=W.BF16, dead_frac=0.02)
+    H = None
+    for damp, neut in ((0.0, False), (0.01, True)):
+        h = hs.Hessian(d, torch.bfloat16, staging_bytes=300 * 2 * d)
+        for b in wl.batches:
+            h.add_batch(to_device(b, W.BF16))
+        H, dead, dmp = h.materialize(damp, neutralize=neut)
+        torch.cuda.synchronize()
+        Hr, deadr, dmpr, Nr = run_oracle(wl, damp, neut)
+        assert h.nsamples == Nr
+        assert np.array_equal(dead.cpu().numpy(), deadr)
+        err = agreement(H.cpu().numpy(), Hr)
+        assert err <= TOL[W.BF16], err
+        h.close()
+
+
+def test_transposed_staging_unaligned_rows():
+    """Rows that are not 16-byte aligned (odd row stride) take the element-wise transposed copy."""
+    _say("transposed staging unaligned rows d=1032")
+    d = 1032
+    wl = W.ragged_case(d, [5, 300, 41], seed=91, dtype=W.BF16, dead_frac=0.0)
+    h = hs.Hessian(d, torch.bfloat16)
+    for b in wl.batches:
+        xb = to_device(b, W.BF16)
+        wide = torch.zeros((xb.shape[0], d + 1), dtype=torch.bfloat16, device=xb.device)
+        wide[:, :d] = xb
+        h.add_batch(wide[:, :d])                       # row stride d + 1 elements
+    H, dead, dmp = h.materialize(0.01)
+    torch.cuda.synchronize()
+    Hr, deadr, dmpr, Nr = run_oracle(wl, 0.01, True)
+    assert h.nsamples == Nr
+    assert agreement(H.cpu().numpy(), Hr) <= TOL[W.BF16]
+    h.close()
+
+
 def _sampled_gram_check(h, wl, n_samples=400, seed=0):
     """Compare sampled upper entries and the whole diagonal of S with the oracle's exact sums."""
     d = wl.d
@@ -477,4 +529,14 @@ def test_kernel_timing_counts_launches():
     h.set_timing(False)
     h.add_batch(x)
     assert h.timing() == (0, 0, 0.0)
+    h.close()
+    # transposed staging pads each batch to 8 rows; the record counts batch rows
+    h = hs.Hessian(1032, torch.bfloat16)
+    x = torch.randn(300, 1032, device="cuda").to(torch.bfloat16)
+    h.set_timing(True)
+    h.add_batch(x[:101])
+    h.add_batch(x[:5])
+    h.flush()
+    launches, tokens, ms = h.timing()
+    assert (launches, tokens) == (1, 106)
     h.close()
