@@ -14,20 +14,25 @@
 //    all 256 CUs tops out near 14 TB/s on this chip (a kernel whose reads hit
 //    in L2 reaches ~24 TB/s), so at 128 x 128 the loads, not the matrix
 //    cores, set the pace.
-//  * 4 waves, one per SIMD, each own a 128 x 128 quadrant: 16 accumulators of
-//    v_mfma_f32_32x32x16_bf16 (256 registers).  The B operand goes first so
-//    that each accumulator register holds part of a row (float4 output).
+//  * 4 waves, one per SIMD, each own a 128 x 128 quadrant: 64 accumulators of
+//    v_mfma_f32_16x16x32_bf16 (256 registers), one instruction per
+//    accumulator per 32-token stage.  With activations of N(0,1) scale the
+//    matrix cores are power-limited on this chip: measured with every other
+//    cost removed, 16x16x32 sustains about 2.0 PFLOP/s where 32x32x16 gets
+//    1.65 (half the accumulator traffic per flop; the clock stays higher).
+//    The B operand goes first so that each lane's 4 results are consecutive
+//    in a row of S (float4 output).
 //  * Activations go from memory straight into LDS (buffer_load_dwordx4 with
 //    the lds modifier): no registers hold loads and no VALU transposes them.
 //    Row-major X: LDS keeps each 32-token stage token-major (a 512-byte row
 //    of 256 features per token) with its 16-byte chunks XOR-swizzled; the
 //    matrix operands (8 consecutive tokens of one feature) are read
 //    transposed with ds_read_b64_tr_b16, two per operand.  The swizzle makes
-//    both the 64-lane DMA writes (1 KB contiguous each) and the transposed
-//    reads free of bank conflicts.  A staging buffer in the transposed
-//    layout (8-token chunks of one feature, written so by the staging copy)
-//    lands in LDS operand-ready: one ds_read_b128 per operand, 32 lanes
-//    reading 512 contiguous bytes.
+//    the transposed reads free of bank conflicts and keeps the 64-lane DMA
+//    writes 1 KB contiguous.  A staging buffer in the transposed layout
+//    (8-token chunks of one feature, written so by the staging copy) lands
+//    in LDS operand-ready: one ds_read_b128 per operand, 16 lanes reading
+//    256 contiguous bytes.
 //  * The loads are written as inline asm (m0 is an input operand) and
 //    placed by hand among the matrix instructions of each iteration's second
 //    half.  The compiler neither tracks nor waits for them; the kernel's own
@@ -35,11 +40,10 @@
 //    waits, which is also what the loads need.
 //  * Five LDS stages of 32 tokens (5 x 32 KB, all of the CU's LDS): the
 //    loads of up to four iterations are in flight while one is multiplied;
-//    one barrier per iteration, placed between the two 16-token halves so
-//    that the matrix cores keep running while a wave waits there and while
-//    the next stage's first operands are read.  The barrier is the bare
-//    s_barrier after an explicit vmcnt wait for this wave's loads of the
-//    stage about to be read.
+//    one barrier per iteration.  The operands of the stage being multiplied
+//    sit in one register set while the next stage's are read into the other
+//    (2 x 64 registers).  The barrier is the bare s_barrier after an
+//    explicit vmcnt wait for this wave's loads of the next stage.
 //  * Loads never need masks: each iteration's buffer descriptor ends at the
 //    batch's last row (rows past it read zero), features past d get an
 //    out-of-range offset (zero), and iterations past a segment read an empty
@@ -54,9 +58,10 @@
 //    of a blocked tile order, so they share activation panels in that XCD's L2.
 //  * Diagonal tiles load one panel and leave the below-diagonal wave idle.
 //
-// A float32 accumulation chain here is one segment (at most the batch, and a
-// staged flush is at most 13,056 tokens at width 2,560 or 8,192 at 4,096);
-// each chain adds sums of 8 exact products.
+// A float32 accumulation chain here is one segment's iterations: at most a
+// batch, or one staged flush (104,448 tokens at width 2,560 with the default
+// 512 MiB staging, i.e. 3,264 additions); each addition brings in one
+// instruction's sum of 32 exact products.
 
 #include "hess_device.hpp"
 #include "hess_internal.hpp"
@@ -73,12 +78,12 @@ constexpr int kStageB = 2 * kPanelB;         // 32 KB
 constexpr int kDma = kStageB / 1024 / 4;     // 1-KB loads per wave per stage (8)
 constexpr uint32_t kOOB = 0x80000000u;       // an offset past any descriptor's range
 
-// Logical 16-byte chunk (8 features) stored at physical chunk pc of token
-// row t.  Forward: pc = c ^ 8*bit1(c) ^ 2*(t % 4).
-__device__ __forceinline__ int chunk_at(int t, int pc) {
-  const int q = pc ^ (2 * (t & 3));
-  return q ^ (8 * ((q >> 1) & 1));
-}
+// Physical 16-byte chunk of logical chunk c (8 features) in token row t of a
+// row-major stage: c ^ 2 (t % 4) ^ 8 ((t / 8) % 2), an involution.  In a
+// transposed read the 16 lanes of a group read 4 consecutive rows t and two
+// adjacent chunks, which land in 8 distinct chunks of one 128-byte half of
+// the bank space; the group 8 tokens further on lands in the other half.
+__device__ __forceinline__ int chunk_pos(int t, int c) { return c ^ (2 * (t & 3)) ^ (8 * ((t >> 3) & 1)); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(uint64_t base, int64_t bytes) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
@@ -139,25 +144,30 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
   const int wr = wave >> 1, wc = wave & 1;
   const uint32_t row_bytes = (uint32_t)(P.ld * 2);
 
-  // operand read offsets: lane l reads, for a 32-feature block fq of a panel,
-  // token 8*(l/32) + (l%16)/4 (+4 for the second read) and features
-  // 32 fq + 16*((l/16)%2) + 4*(l%4) .. +3
-  const int tl = 8 * (lane >> 5) + ((lane & 15) >> 2);
-  const int kl = (8 * ((lane >> 4) & 1)) ^ (2 * ((lane & 15) >> 2));
-  const int el = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int bl = 8 * (lane & 1);
-  int offA[4], offB[4];
+  // Operand of a 16-feature block f0..f0+15 of a panel for
+  // v_mfma_f32_16x16x32_bf16: lane l holds feature f0 + l%16, tokens
+  // 8 (l/16) .. +7 of the stage.
+  //  * row-major stage: two transposed reads; in each, the 16 lanes of group
+  //    g = l/16 read tokens 8 g + (l%16)/4 (+4 for the second read), features
+  //    f0 + 4 (l%4) .. +3 (bytes 8 (l%2) of chunk (f0 + 4 (l%4)) / 8);
+  //  * transposed stage: one 16-byte read of row l/16 (the l/16-th 8-token
+  //    block), chunk f0 + l%16.
+  const int tl = 8 * (lane >> 4) + ((lane & 15) >> 2);
+  int offA[8], offB[8];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    offA[m] = tl * kRowB + (((4 * (4 * wr + m) + el) ^ kl) << 4) + bl;
-    offB[m] = tl * kRowB + (((4 * (4 * wc + m) + el) ^ kl) << 4) + bl;
+  for (int m = 0; m < 8; ++m) {
+    offA[m] = tl * kRowB + (chunk_pos(tl, (128 * wr + 16 * m + 4 * (lane & 3)) >> 3) << 4) + 8 * (lane & 1);
+    offB[m] = tl * kRowB + (chunk_pos(tl, (128 * wc + 16 * m + 4 * (lane & 3)) >> 3) << 4) + 8 * (lane & 1);
   }
-  // transposed staging: this lane's chunks in panels A and B (row l / 32)
-  const int t8A = (lane >> 5) * 4096 + (128 * wr + (lane & 31)) * 16;
-  const int t8B = (lane >> 5) * 4096 + (128 * wc + (lane & 31)) * 16;
+  const int t8A = (lane >> 4) * 4096 + (128 * wr + (lane & 15)) * 16;
+  const int t8B = (lane >> 4) * 4096 + (128 * wc + (lane & 15)) * 16;
 
   auto segment = [&](int tile, int k0, int k1, int slot) {
-    f32x16 acc[4][4];
+    // accumulator (m, n): tile rows 128 wr + 16 m + (0..15), columns
+    // 128 wc + 16 n + (0..15); lane l holds row 16 m + l%16, columns
+    // 16 n + 4 (l/16) .. +3 (the column block is the instruction's first
+    // operand, so each lane's four values are consecutive in a row of S)
+    f32x4 acc[8][8];
     const int code = P.order[tile];
     const int I = code >> 16, J = code & 0xffff;
     const bool diag = I == J;
@@ -166,9 +176,10 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
 
     // DMA offsets: wave w loads 1-KB blocks gb = 8w + i of a stage (panel
     // gb / 16); lane j fills bytes 16j..16j+15.  Row-major X: block gb holds
-    // token rows 2*(gb % 16) and +1.  Transposed staging: the panel is 4
-    // rows (8-token blocks) of 256 16-byte chunks (8 tokens of one feature);
-    // block gb holds features 64*(gb % 4) .. +63 of row (gb % 16) / 4.
+    // token rows 2*(gb % 16) and +1, chunk j%32 of row t at chunk_pos(t, .).
+    // Transposed staging: the panel is 4 rows (8-token blocks) of 256 16-byte
+    // chunks (8 tokens of one feature); block gb holds features
+    // 64*(gb % 4) .. +63 of row (gb % 16) / 4.
     uint32_t voff[kDma];
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
@@ -180,7 +191,7 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
         voff[i] = (f < P.d && !(p && diag)) ? ((uint32_t)c * (uint32_t)P.ld + (uint32_t)f) * 16u : kOOB;
       } else {
         const int t = 2 * b + (lane >> 5);
-        const int f = (p ? J : I) * kT + 8 * chunk_at(t, lane & 31);
+        const int f = (p ? J : I) * kT + 8 * chunk_pos(t, lane & 31);  // chunk_pos is its own inverse
         voff[i] = (f < P.d && !(p && diag)) ? (uint32_t)t * row_bytes + (uint32_t)f * 2u : kOOB;
       }
     }
@@ -207,90 +218,45 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
       for (int i = 0; i < kDma; ++i) dma1(stage_lds, r, i);
     };
     auto dma = [&](uint32_t stage_lds, int j) { issue(stage_lds, desc(j)); };
-    // operands of one 16-token half (ks) of a stage: A blocks of this wave's
-    // rows, B blocks of its columns
-    auto rd = [&](const char* stage, int ks, u32x4 (&a)[4], u32x4 (&b)[4]) {
+    // operand j of a stage: A block j (j < 8, this wave's rows) or B block
+    // j - 8 (its columns)
+    const int t8Bd = t8B + (diag ? 0 : kPanelB);
+    auto rd1 = [&](const char* stage, int j, u32x4 (&a)[8], u32x4 (&b)[8]) {
+      const int m = j & 7;
+      const char* pb = diag ? stage : stage + kPanelB;
       if constexpr (T8) {
-        // one 16-byte read per operand: row 2 ks + l/32 of the panel, the
-        // chunk of its feature (32 consecutive lanes read 512 contiguous bytes)
-        const char* pa = stage + ks * 2 * 4096;
-        const char* pb = (diag ? stage : stage + kPanelB) + ks * 2 * 4096;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) a[m] = *reinterpret_cast<const u32x4*>(pa + t8A + m * 32 * 16);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) b[m] = *reinterpret_cast<const u32x4*>(pb + t8B + m * 32 * 16);
+        if (j < 8) a[m] = *reinterpret_cast<const u32x4*>(stage + t8A + m * 16 * 16);
+        else b[m] = *reinterpret_cast<const u32x4*>(stage + t8Bd + m * 16 * 16);
       } else {
-        const char* pa = stage + ks * 16 * kRowB;
-        const char* pb = (diag ? stage : stage + kPanelB) + ks * 16 * kRowB;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) a[m] = tr_pair(pa + offA[m]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) b[m] = tr_pair(pb + offB[m]);
-      }
-    };
-    // operand j of one half: A block j (j < 4) or B block j - 4
-    auto rd1 = [&](const char* stage, int ks, int j, u32x4 (&a)[4], u32x4 (&b)[4]) {
-      const int m = j & 3;
-      if constexpr (T8) {
-        const char* pa = stage + ks * 2 * 4096;
-        const char* pb = (diag ? stage : stage + kPanelB) + ks * 2 * 4096;
-        if (j < 4) a[m] = *reinterpret_cast<const u32x4*>(pa + t8A + m * 32 * 16);
-        else b[m] = *reinterpret_cast<const u32x4*>(pb + t8B + m * 32 * 16);
-      } else {
-        const char* pa = stage + ks * 16 * kRowB;
-        const char* pb = (diag ? stage : stage + kPanelB) + ks * 16 * kRowB;
-        if (j < 4) a[m] = tr_pair(pa + offA[m]);
+        if (j < 8) a[m] = tr_pair(stage + offA[m]);
         else b[m] = tr_pair(pb + offB[m]);
       }
     };
-    auto mm = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc[m][n] = mfma32x32x16(b[n], a[m], acc[m][n]);
-    };
-    // 16 matrix instructions of one half, each followed by one of the 16
-    // transposed reads of the other half's operands
-    auto interleave = [&]() {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      }
-    };
-    // Iteration i (stage cur): the first half's operands (xa, xb) were read
-    // during the previous iteration.  Multiply the first half while reading
-    // the second; then wait for my loads of iteration i + 1 and meet the
-    // other waves (after that barrier stage i + 1 is complete and nobody
-    // reads stage i - 1 any more), and multiply the second half while
-    // reading the first half of stage i + 1 and starting the loads of
-    // iteration i + 4 into stage i - 1: after each pair of matrix
-    // instructions one operand read and one load.  A load instruction waits
-    // at issue until the CU's address unit takes it; spread out this way the
-    // wait holds up at most one matrix instruction (issued back to back, the
-    // four waves' 32 loads kept each wave from the matrix cores for ~350
-    // cycles of every ~1,800).  The descriptor is built before the barrier.
-    // Iterations past the segment multiply the zeros their empty loads wrote.
-    u32x4 xa[4], xb[4], ya[4], yb[4];
-    auto step = [&](const char* cur, const char* nxt, uint32_t dtgt, int i) {
+    // Iteration i (stage cur, operands xa, xb read during iteration i - 1):
+    // wait for my loads of iteration i + 1 and meet the other waves (after
+    // that barrier stage i + 1 is complete and nobody reads stage i - 1 any
+    // more); then the 64 matrix instructions of stage i, with the 16 operand
+    // reads of stage i + 1 (into ya, yb) and the 8 loads of iteration i + 4
+    // into stage i - 1 placed among them by hand: after every 4 matrix
+    // instructions one read, after every 8 one load.  A load instruction
+    // waits at issue until the CU's address unit takes it; spread out this
+    // way the wait holds up at most one matrix instruction.  Iterations past
+    // the segment multiply the zeros their empty loads wrote.
+    auto step = [&](const char* nxt, uint32_t dtgt, int i, const u32x4 (&xa)[8], const u32x4 (&xb)[8],
+                    u32x4 (&ya)[8], u32x4 (&yb)[8]) {
       const u32x4 r = desc(k0 + i + 4);
-      if (active) {
-        rd(cur, 1, ya, yb);
-        mm(xa, xb);
-        interleave();
-      }
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): iterations i + 2 and i + 3 stay in flight
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       if (active) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int m = j >> 1, n = 2 * (j & 1);
-          acc[m][n] = mfma32x32x16(yb[n], ya[m], acc[m][n]);
-          acc[m][n + 1] = mfma32x32x16(yb[n + 1], ya[m], acc[m][n + 1]);
-          rd1(nxt, 0, j, xa, xb);
-          dma1(dtgt, r, j);
+        for (int g = 0; g < 16; ++g) {
+          const int m = g >> 1, n = 4 * (g & 1);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[m][n + u] = mfma16x16x32(xb[n + u], xa[m], acc[m][n + u]);
+          rd1(nxt, g, ya, yb);
+          if (g & 1) dma1(dtgt, r, g >> 1);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
@@ -300,9 +266,9 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
     };
 
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int n = 0; n < 4; ++n) acc[m][n] = f32x16{};
+      for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{};
 
     // the previous segment's output stores leave the count before these loads
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -313,40 +279,55 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
     __builtin_amdgcn_s_waitcnt(0x4F78);  // vmcnt(24): iteration k0 has landed
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (active) rd(st0, 0, xa, xb);
-    for (int i = 0; i < k1 - k0; i += 5) {
-      step(st0, st1, L4, i);
-      step(st1, st2, L0, i + 1);
-      step(st2, st3, L1, i + 2);
-      step(st3, st4, L2, i + 3);
-      step(st4, st0, L3, i + 4);
+    u32x4 xa[8], xb[8], ya[8], yb[8];
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) rd1(st0, j, xa, xb);
     }
-    // drain the trailing (empty-range) loads; every wave is done with the stages
+    // ten iterations per trip: five stages, two operand register sets; the
+    // exit is checked after every second iteration (an extra iteration
+    // multiplies zeros)
+    const int niter = k1 - k0;
+    for (int i = 0;; i += 10) {
+      step(st1, L4, i, xa, xb, ya, yb);
+      step(st2, L0, i + 1, ya, yb, xa, xb);
+      if (i + 2 >= niter) break;
+      step(st3, L1, i + 2, xa, xb, ya, yb);
+      step(st4, L2, i + 3, ya, yb, xa, xb);
+      if (i + 4 >= niter) break;
+      step(st0, L3, i + 4, xa, xb, ya, yb);
+      step(st1, L4, i + 5, ya, yb, xa, xb);
+      if (i + 6 >= niter) break;
+      step(st2, L0, i + 6, xa, xb, ya, yb);
+      step(st3, L1, i + 7, ya, yb, xa, xb);
+      if (i + 8 >= niter) break;
+      step(st4, L2, i + 8, xa, xb, ya, yb);
+      step(st0, L3, i + 9, ya, yb, xa, xb);
+      if (i + 10 >= niter) break;
+    }
+    // drain the trailing loads; every wave is done with the stages
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (!active) return;
 
-    // accumulator (m, n, register 4q + e) of this lane: tile row
-    // 128 wr + 32 m + lane%32, column 128 wc + 32 n + 8 q + 4*(lane/32) + e
-    // (the lane index goes through an empty asm so that these per-lane offsets
-    // are computed here, not hoisted out of the segment loop to sit in
-    // registers through the main loop)
+    // tile-local row and first column of accumulator (m, n) for this lane
+    // (the lane index goes through an empty asm so that these per-lane
+    // offsets are computed here, not hoisted out of the segment loop to sit
+    // in registers through the main loop)
     int lv = lane;
     asm volatile("" : "+v"(lv));
-    const int rr = 128 * wr + (lv & 31);
-    const int cc = 128 * wc + 4 * (lv >> 5);
+    const int rr = 128 * wr + (lv & 15);
+    const int cc = 128 * wc + 4 * (lv >> 4);
     if (slot >= 0) {
       float* W = P.ws + (int64_t)slot * (kT * kT);
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 v{acc[m][n][4 * q], acc[m][n][4 * q + 1], acc[m][n][4 * q + 2], acc[m][n][4 * q + 3]};
-            *reinterpret_cast<float4*>(W + (rr + 32 * m) * kT + cc + 32 * n + 8 * q) = v;
-          }
+        for (int n = 0; n < 8; ++n) {
+          const f32x4 a = acc[m][n];
+          *reinterpret_cast<float4*>(W + (rr + 16 * m) * kT + cc + 16 * n) = float4{a[0], a[1], a[2], a[3]};
+        }
       return;
     }
     // whole tile: S += acc, branch-free.  Elements past d get an offset past
@@ -355,31 +336,28 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
     const __amdgpu_buffer_rsrc_t sr =
         make_rsrc(reinterpret_cast<uint64_t>(P.S) + (uint64_t)((int64_t)I * kT * P.lds * 4), (int64_t)kT * P.lds * 4);
     const int rlim = P.d - I * kT, clim = P.d - J * kT;  // tile-local row / column limits
-    auto soff = [&](int m, int n, int q) -> uint32_t {
-      const int r = rr + 32 * m, c = cc + 32 * n + 8 * q;
+    auto soff = [&](int m, int n) -> uint32_t {
+      const int r = rr + 16 * m, c = cc + 16 * n;
       return (r < rlim && c < clim) ? (uint32_t)(((int64_t)r * P.lds + J * kT + c) * 4) : kOOB;
     };
-    // 8 batches of 8 float4 (row block m = k / 2, column blocks 2 (k % 2) and
-    // +1); the loads of batch k + 1 are in flight while batch k is added
+    // 8 batches of 8 float4 (row block m); the loads of batch m + 1 are in
+    // flight while batch m is added
     float4 sv[2][8];
-    auto sload = [&](int k, float4 (&dst)[8]) {
+    auto sload = [&](int m, float4 (&dst)[8]) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        dst[u] = __builtin_bit_cast(
-            float4, __builtin_amdgcn_raw_buffer_load_b128(sr, soff(k >> 1, 2 * (k & 1) + (u >> 2), u & 3), 0, 0));
+      for (int n = 0; n < 8; ++n)
+        dst[n] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(sr, soff(m, n), 0, 0));
     };
     sload(0, sv[0]);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (k + 1 < 8) sload(k + 1, sv[(k + 1) & 1]);
-      const int m = k >> 1;
+    for (int m = 0; m < 8; ++m) {
+      if (m + 1 < 8) sload(m + 1, sv[(m + 1) & 1]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int n = 2 * (k & 1) + (u >> 2), q = u & 3;
-        const float4 sx = sv[k & 1][u];
-        const float4 v{sx.x + acc[m][n][4 * q], sx.y + acc[m][n][4 * q + 1], sx.z + acc[m][n][4 * q + 2],
-                       sx.w + acc[m][n][4 * q + 3]};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), sr, soff(m, n, q), 0, 0);
+      for (int n = 0; n < 8; ++n) {
+        const float4 sx = sv[m & 1][n];
+        const f32x4 a = acc[m][n];
+        const float4 v{sx.x + a[0], sx.y + a[1], sx.z + a[2], sx.w + a[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), sr, soff(m, n), 0, 0);
       }
     }
   };

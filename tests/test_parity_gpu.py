@@ -206,6 +206,22 @@ def test_big_tiles_full_size_sampled(d, n):
     h.close()
 
 
+def test_transposed_staging_full_flush_sampled():
+    """One full default staging buffer at width 2,560 (104,448 tokens in 2,000-token batches,
+    the longest float32 chain a staged flush makes) against the oracle's exact sums."""
+    _say("transposed staging full flush d=2560")
+    d = 2560
+    sizes = [2000] * 52 + [448]
+    wl = W.ragged_case(d, sizes, seed=2560, dtype=W.BF16, dead_frac=0.0)
+    h = hs.Hessian(d, torch.bfloat16)
+    for b in wl.batches:
+        h.add_batch(to_device(b, W.BF16))
+    err = _sampled_gram_check(h, wl)
+    assert h.nsamples == sum(sizes)
+    assert err <= TOL[W.BF16], err
+    h.close()
+
+
 def test_big_tiles_chosen_automatically():
     """Width 4,096 with 24,576 tokens (408 iterations per workgroup) takes the 256-tile kernel
     without an override; the result is checked on sampled entries."""
