@@ -238,7 +238,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": P_BF16 / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved / P_BF16, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "kernel": "syrk_big_bf16 (256-tile SYRK main kernel of each staging flush)",
+                     "kernel": "syrk_big_bf16_t8 (256-tile SYRK main kernel of each staging flush, transposed staging)",
                      "launches_per_hessian": round(launches / args.steps, 2),
                      "mean_launch_us": round(kms * 1e3 / launches, 2),
                      "tokens_per_launch": round(ktok / launches, 1)},
@@ -309,7 +309,7 @@ def run_extras(torch, hs, W, args):
             extra["d4096_n32768_bf16"]["roofline"] = {
                 "bound": "mfma", "achieved": round(fl / kern / 1e9, 1), "peak": P_BF16 / 1e12, "unit": "TFLOP/s",
                 "frac": round(fl / (kern * 1e-3) / P_BF16, 4), "traffic": None if traffic is None else round(traffic),
-                "kernel": "syrk_big_bf16 (256-tile SYRK main kernel; its fixup follows)"}
+                "kernel": "syrk_big_bf16 (256-tile SYRK main kernel, row-major batch; its fixup follows)"}
         del x
     if "moe" in want:
         # MoE: 64 routed experts, d=2048, 32768 tokens top-8, Zipf(1.1)

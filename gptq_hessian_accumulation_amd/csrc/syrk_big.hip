@@ -77,6 +77,9 @@ constexpr int kPanelB = kKI * kRowB;         // 16 KB
 constexpr int kStageB = 2 * kPanelB;         // 32 KB
 constexpr int kDma = kStageB / 1024 / 4;     // 1-KB loads per wave per stage (8)
 constexpr uint32_t kOOB = 0x80000000u;       // an offset past any descriptor's range
+constexpr int kDist = 4;                     // iterations between a stage's load and its use
+// s_waitcnt immediate: vmcnt(n), no wait on the other counters
+constexpr int vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // Physical 16-byte chunk of logical chunk c (8 features) in token row t of a
 // row-major stage: c ^ 2 (t % 4) ^ 8 ((t / 8) % 2), an involution.  In a
@@ -244,9 +247,10 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
     // the segment multiply the zeros their empty loads wrote.
     auto step = [&](const char* nxt, uint32_t dtgt, int i, const u32x4 (&xa)[8], const u32x4 (&xb)[8],
                     u32x4 (&ya)[8], u32x4 (&yb)[8]) {
-      const u32x4 r = desc(k0 + i + 4);
+      const u32x4 r = desc(k0 + i + kDist);
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): iterations i + 2 and i + 3 stay in flight
+      // my loads of iteration i + 1 have landed; those of i + 2 .. i + kDist - 1 stay in flight
+      __builtin_amdgcn_s_waitcnt(vm_wait(kDma * (kDist - 2)));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       if (active) {
@@ -272,11 +276,11 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
 
     // the previous segment's output stores leave the count before these loads
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    dma(L0, k0);
-    dma(L1, k0 + 1);
-    dma(L2, k0 + 2);
-    dma(L3, k0 + 3);
-    __builtin_amdgcn_s_waitcnt(0x4F78);  // vmcnt(24): iteration k0 has landed
+    const uint32_t Ls[5] = {L0, L1, L2, L3, L4};
+    char* const St[5] = {st0, st1, st2, st3, st4};
+#pragma unroll
+    for (int q = 0; q < kDist; ++q) dma(Ls[q], k0 + q);
+    __builtin_amdgcn_s_waitcnt(vm_wait(kDma * (kDist - 1)));  // iteration k0 has landed
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     u32x4 xa[8], xb[8], ya[8], yb[8];
@@ -289,20 +293,20 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
     // multiplies zeros)
     const int niter = k1 - k0;
     for (int i = 0;; i += 10) {
-      step(st1, L4, i, xa, xb, ya, yb);
-      step(st2, L0, i + 1, ya, yb, xa, xb);
+      step(St[1], Ls[kDist % 5], i, xa, xb, ya, yb);
+      step(St[2], Ls[(1 + kDist) % 5], i + 1, ya, yb, xa, xb);
       if (i + 2 >= niter) break;
-      step(st3, L1, i + 2, xa, xb, ya, yb);
-      step(st4, L2, i + 3, ya, yb, xa, xb);
+      step(St[3], Ls[(2 + kDist) % 5], i + 2, xa, xb, ya, yb);
+      step(St[4], Ls[(3 + kDist) % 5], i + 3, ya, yb, xa, xb);
       if (i + 4 >= niter) break;
-      step(st0, L3, i + 4, xa, xb, ya, yb);
-      step(st1, L4, i + 5, ya, yb, xa, xb);
+      step(St[0], Ls[(4 + kDist) % 5], i + 4, xa, xb, ya, yb);
+      step(St[1], Ls[(5 + kDist) % 5], i + 5, ya, yb, xa, xb);
       if (i + 6 >= niter) break;
-      step(st2, L0, i + 6, xa, xb, ya, yb);
-      step(st3, L1, i + 7, ya, yb, xa, xb);
+      step(St[2], Ls[(6 + kDist) % 5], i + 6, xa, xb, ya, yb);
+      step(St[3], Ls[(7 + kDist) % 5], i + 7, ya, yb, xa, xb);
       if (i + 8 >= niter) break;
-      step(st4, L2, i + 8, xa, xb, ya, yb);
-      step(st0, L3, i + 9, ya, yb, xa, xb);
+      step(St[4], Ls[(8 + kDist) % 5], i + 8, xa, xb, ya, yb);
+      step(St[0], Ls[(9 + kDist) % 5], i + 9, ya, yb, xa, xb);
       if (i + 10 >= niter) break;
     }
     // drain the trailing loads; every wave is done with the stages
