@@ -86,6 +86,7 @@ def _load():
         "hess_token_count": (c_int, [vp, ctypes.POINTER(i64)]),
         "hess_set_tile_override": (c_int, [c_int]),
         "hess_set_staging": (c_int, [c_int]),
+        "hess_set_group_chunk": (c_int, [i64]),
         "hess_flush": (c_int, [vp, vp]),
         "hess_set_timing": (c_int, [vp, c_int]),
         "hess_timing": (c_int, [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]),
@@ -144,6 +145,11 @@ def _as_rows(x: torch.Tensor, d: int):
 def set_staging(enable: bool) -> None:
     """Enable (default) or disable the staging of short batches; process-wide."""
     _check(_load().hess_set_staging(1 if enable else 0))
+
+
+def set_group_chunk(nbytes: int) -> None:
+    """Cap the rows gathered per 256-tile grouped launch (bytes; 0 = the whole buffer); process-wide."""
+    _check(_load().hess_set_group_chunk(int(nbytes)))
 
 
 def set_tile_override(edge: int) -> None:

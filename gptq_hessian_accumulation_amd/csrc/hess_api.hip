@@ -68,6 +68,8 @@ struct BigWorkspace {
   std::mutex mu;
   float* ptr = nullptr;
   int64_t slots = 0;          // 256 x 256 float slots
+  void* gptr = nullptr;       // grouped updates: gathered rows in transposed staging layout
+  int64_t gbytes = 0;
   hipEvent_t ev = nullptr;
   bool used = false;
   hipStream_t last = nullptr;
@@ -77,6 +79,7 @@ BigWorkspace g_big[kMaxDevices];
 
 thread_local char g_err[512] = "";
 int g_tile_override = 0;  // 0 = automatic; 128 forces the 128-edge SYRK tiles
+int64_t g_group_chunk = 0; // test hook: cap on the gathered bytes per grouped launch (0 = scratch size)
 bool g_staging = true;    // thin-batch staging enabled (process-wide)
 
 int fail(int code, const char* fmt, ...) {
@@ -200,6 +203,7 @@ constexpr int kBig = 256;
 constexpr int kBigKI = 32;               // tokens per iteration
 constexpr int kBigMinD = 1024;           // automatic choice: widths at least this wide ...
 constexpr int64_t kBigMinWork = 300;     // ... and at least this many iterations per workgroup
+constexpr int64_t kGroupScratch = (int64_t)512 << 20;  // gathered rows of grouped updates, per device
 
 bool big_capable(int64_t d, int dtype) { return dtype == HESS_BF16 && d % 8 == 0 && d >= 8 && d <= 32768; }
 
@@ -353,6 +357,94 @@ int flush_stage(hess_t h, hipStream_t s) {
   return rc;
 }
 
+// Grouped update on 256-tiles: the groups' rows are gathered into the
+// device's scratch in the transposed staging layout (a multiple of 8 rows per
+// group, zero-padded), then one launch takes whole upper tiles of every
+// group.  Groups that do not fit are split; the scratch is refilled as many
+// times as needed (each fill is one copy and one SYRK launch).
+int grouped_big(hess_t* hs, int n_groups, const void* X, int64_t ld, const int32_t* row_idx,
+                const int64_t* offsets, hipStream_t s) {
+  const hess_t h0 = hs[0];
+  const int64_t d = h0->d;
+  BigWorkspace& W = g_big[h0->device];
+  std::lock_guard<std::mutex> lock(W.mu);
+  if (!W.gptr) return fail(HESS_EHIP, "grouped scratch missing");
+  int64_t cap_bytes = W.gbytes;
+  if (g_group_chunk > 0) cap_bytes = std::min(cap_bytes, g_group_chunk);
+  const int64_t cap_blocks = cap_bytes / (d * 16);  // 8-token blocks per fill
+  if (cap_blocks < 1) return fail(HESS_EINVAL, "grouped scratch smaller than one 8-row block");
+  // pieces (group, first row, rows), largest groups first
+  struct Piece { int e; int64_t beg, cnt; };
+  std::vector<int> order;
+  for (int e = 0; e < n_groups; ++e)
+    if (offsets[e + 1] > offsets[e]) order.push_back(e);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return offsets[a + 1] - offsets[a] > offsets[b + 1] - offsets[b]; });
+  std::vector<Piece> pieces;
+  for (int e : order)
+    for (int64_t b = offsets[e]; b < offsets[e + 1]; b += cap_blocks * 8)
+      pieces.push_back({e, b, std::min(cap_blocks * 8, offsets[e + 1] - b)});
+  hipError_t err = hipSuccess;
+  if (W.used && W.last != s) {
+    err = hipStreamWaitEvent(s, W.ev, 0);
+    if (err != hipSuccess) return hip_fail(err, "hipStreamWaitEvent");
+  }
+  BigParams P;
+  std::memset(&P, 0, sizeof(P));
+  P.ld = d;
+  P.lds = d;
+  P.order = h0->order256;
+  P.d = (int)d;
+  P.nb = h0->nb256;
+  P.ntiles = h0->ntiles256;
+  P.t8 = 1;
+  size_t next = 0;
+  while (next < pieces.size()) {
+    // one fill: as many pieces as fit (at most kBigMaxGroups)
+    GatherParams Gp;
+    std::memset(&Gp, 0, sizeof(Gp));
+    BigGroupParams Gb;
+    std::memset(&Gb, 0, sizeof(Gb));
+    int64_t blocks = 0;
+    int k = 0;
+    while (next < pieces.size() && k < kBigMaxGroups) {
+      const Piece& pc = pieces[next];
+      const int64_t nblk = (pc.cnt + 7) / 8;
+      if (blocks + nblk > cap_blocks) break;
+      Gp.beg[k] = pc.beg;
+      Gp.cnt[k] = pc.cnt;
+      Gp.blk[k] = blocks;
+      Gp.blk_prefix[k] = blocks;
+      Gb.blk[k] = blocks;
+      Gb.n[k] = pc.cnt;
+      Gb.S[k] = hs[pc.e]->S;
+      blocks += nblk;
+      ++k;
+      ++next;
+    }
+    Gp.blk_prefix[k] = blocks;
+    Gp.X = X;
+    Gp.rows = row_idx;
+    Gp.dst = W.gptr;
+    Gp.ld = ld;
+    Gp.d = (int)d;
+    Gp.fq = (int)((d + 255) / 256);
+    Gp.ngroups = k;
+    err = launch_gather_rows_t8(Gp, s);
+    if (err != hipSuccess) return hip_fail(err, "grouped gather launch");
+    Gb.X = W.gptr;
+    Gb.ngroups = k;
+    Gb.nitems = k * P.ntiles;
+    err = launch_syrk_big_grouped(P, Gb, s);
+    if (err != hipSuccess) return hip_fail(err, "grouped 256-tile SYRK launch");
+  }
+  err = hipEventRecord(W.ev, s);
+  if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+  W.used = true;
+  W.last = s;
+  return HESS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -450,6 +542,11 @@ hess_t hess_create_ex(int64_t d, int in_dtype, int64_t staging_bytes) {
         }
         if (e == hipSuccess) e = hipMalloc(&W.ptr, (size_t)need * kBig * kBig * sizeof(float));
         if (e == hipSuccess) W.slots = need;
+      }
+      // grouped updates gather their rows here (one buffer per device)
+      if (e == hipSuccess && d >= kBigMinD && !W.gptr) {
+        e = hipMalloc(&W.gptr, (size_t)kGroupScratch);
+        if (e == hipSuccess) W.gbytes = kGroupScratch;
       }
     }
     // transposed staging when a full buffer's flush takes the 256-tile
@@ -560,6 +657,12 @@ int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld, 
     if (rc != HESS_OK) return rc;
   }
   const bool vec = vec_ok(X, ld, h0->d, esize(h0->dtype));
+  if (vec && h0->order256 && h0->d >= kBigMinD && g_tile_override != kTile) {
+    const int rc = grouped_big(hs, n_groups, X, ld, row_idx, offsets, s);
+    if (rc != HESS_OK) return rc;
+    for (int e = 0; e < n_groups; ++e) hs[e]->N += offsets[e + 1] - offsets[e];
+    return HESS_OK;
+  }
   const int nb = (int)((h0->d + kTile - 1) / kTile);
   const int ntiles = nb * (nb + 1) / 2;
   // longest groups first, so their workgroups start in the first round
@@ -648,6 +751,12 @@ int hess_flush(hess_t h, hess_stream_t stream) {
   int rc = order_stream(h, s);
   if (rc != HESS_OK) return rc;
   return flush_stage(h, s);
+}
+
+int hess_set_group_chunk(int64_t bytes) {
+  if (bytes < 0) return fail(HESS_EINVAL, "group chunk must be >= 0");
+  g_group_chunk = bytes;
+  return HESS_OK;
 }
 
 int hess_set_staging(int enable) {

@@ -80,6 +80,41 @@ struct BigParams {
 hipError_t launch_syrk_big(const BigParams& P, hipStream_t stream);
 hipError_t launch_syrk_big_fixup(const BigParams& P, hipStream_t stream);
 
+// Grouped 256-tile launch on transposed staging: whole upper tiles of up to
+// kBigMaxGroups Hessians of one width, each group's tokens at
+// X + blk[g] 8-token blocks (blocks of d 16-byte chunks), n[g] tokens
+// (a multiple of 8), sum into S[g] (row stride d).
+constexpr int kBigMaxGroups = 64;
+struct BigGroupParams {
+  const void* X;
+  int nitems;             // ngroups * ntiles, groups in order of decreasing n
+  int ngroups;
+  int64_t blk[kBigMaxGroups];
+  int64_t n[kBigMaxGroups];
+  float* S[kBigMaxGroups];
+};
+// P supplies the geometry: order, d, nb, ntiles, ld = lds = d.
+hipError_t launch_syrk_big_grouped(const BigParams& P, const BigGroupParams& G, hipStream_t stream);
+
+// Transposed staging copy of gathered rows: group g's rows are
+// rows[beg[g] .. beg[g] + cnt[g]) of X (or X rows beg[g] .. if rows is
+// null), written as 8-token blocks starting at block blk[g] of dst, the last
+// block zero-padded.  blk_prefix[g] = blocks of groups 0..g-1 (the grid).
+struct GatherParams {
+  const void* X;
+  const int32_t* rows;
+  void* dst;
+  int64_t ld;
+  int d;
+  int fq;                 // 256-feature quarters per row: ceil(d / 256)
+  int ngroups;
+  int64_t beg[kBigMaxGroups];
+  int64_t cnt[kBigMaxGroups];
+  int64_t blk[kBigMaxGroups];
+  int64_t blk_prefix[kBigMaxGroups + 1];
+};
+hipError_t launch_gather_rows_t8(const GatherParams& P, hipStream_t stream);
+
 int syrk_tile_edge();
 hipError_t launch_syrk(const SyrkParams& P, int in_dtype, bool vec, int grid, hipStream_t stream);
 hipError_t launch_syrk_reduce(float* S, int64_t lds, const float* ws, int d, int nb, int full_tiles, int tail_tiles,

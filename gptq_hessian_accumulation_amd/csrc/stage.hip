@@ -97,7 +97,54 @@ __global__ void __launch_bounds__(256) copy_rows_t8_elem(const uint16_t* X, int6
   }
 }
 
+// Transposed staging copy of gathered rows for grouped updates: workgroup
+// (block, F) finds its group by the block prefix, then moves as
+// copy_rows_t8 does, with each token's row looked up in rows (or taken in
+// order).  Rows are 16-byte aligned (checked by the caller).
+__global__ void __launch_bounds__(256) gather_rows_t8(GatherParams P) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[8][256];
+  const int t = threadIdx.x;
+  const int64_t gb = blockIdx.x / P.fq;
+  const int F = (int)(blockIdx.x - gb * P.fq) * 256;
+  int lo = 0, hi = P.ngroups;  // last group g with blk_prefix[g] <= gb
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (P.blk_prefix[mid] <= gb) lo = mid;
+    else hi = mid;
+  }
+  const int g = lo;
+  const int64_t b = gb - P.blk_prefix[g];
+  {
+    const int r = t >> 5, q = t & 31;
+    const int64_t tok = 8 * b + r;
+    const int f = F + 8 * q;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (tok < P.cnt[g] && f < P.d) {
+      const int64_t pos = P.beg[g] + tok;
+      const int64_t row = P.rows ? (int64_t)P.rows[pos] : pos;
+      v = *reinterpret_cast<const u32x4*>(static_cast<const char*>(P.X) + row * P.ld * 2 + (int64_t)f * 2);
+    }
+    *reinterpret_cast<u32x4*>(&tile[r][8 * q]) = v;
+  }
+  __syncthreads();
+  const int f = F + t;
+  if (f < P.d) {
+    u32x4 c;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) c[p] = (uint32_t)tile[2 * p][t] | ((uint32_t)tile[2 * p + 1][t] << 16);
+    *reinterpret_cast<u32x4*>(static_cast<char*>(P.dst) + ((P.blk[g] + b) * P.d + f) * 16) = c;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gather_rows_t8(const GatherParams& P, hipStream_t stream) {
+  const int64_t wgs = P.blk_prefix[P.ngroups] * P.fq;
+  if (wgs <= 0) return hipSuccess;
+  if (wgs >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_rows_t8, dim3((unsigned)wgs), dim3(256), 0, stream, P);
+  return hipGetLastError();
+}
 
 hipError_t launch_copy_rows_t8(const void* X, int64_t ld, int64_t n, int64_t d, void* dst, hipStream_t stream) {
   if (n <= 0) return hipSuccess;

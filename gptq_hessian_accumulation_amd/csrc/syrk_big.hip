@@ -126,8 +126,8 @@ __device__ __forceinline__ int64_t excess_start(const BigParams& P, int w) {
   return (int64_t)w * P.excess_total / P.grid_sk;
 }
 
-template <bool T8>
-__device__ __forceinline__ void big_body(const BigParams& P) {
+template <bool T8, bool Grouped>
+__device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParams* G) {
   __shared__ __attribute__((aligned(1024))) char st0[kStageB];
   __shared__ __attribute__((aligned(1024))) char st1[kStageB];
   __shared__ __attribute__((aligned(1024))) char st2[kStageB];
@@ -165,7 +165,8 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
   const int t8A = (lane >> 4) * 4096 + (128 * wr + (lane & 15)) * 16;
   const int t8B = (lane >> 4) * 4096 + (128 * wc + (lane & 15)) * 16;
 
-  auto segment = [&](int tile, int k0, int k1, int slot) {
+  // one tile's iterations k0..k1-1 of the tokens at X (n of them) into S
+  auto segment = [&](int tile, int k0, int k1, int slot, const void* X, int64_t n, float* S) {
     // accumulator (m, n): tile rows 128 wr + 16 m + (0..15), columns
     // 128 wc + 16 n + (0..15); lane l holds row 16 m + l%16, columns
     // 16 n + 4 (l/16) .. +3 (the column block is the instruction's first
@@ -202,13 +203,13 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
     // chunks (transposed staging, n a multiple of 8)
     auto desc = [&](int j) {
       const int64_t tok = (int64_t)j * kKI;
-      const int64_t valid = j < k1 ? max((int64_t)0, min((int64_t)kKI, P.n - tok)) : 0;
+      const int64_t valid = j < k1 ? max((int64_t)0, min((int64_t)kKI, n - tok)) : 0;
       if constexpr (T8) {
         const uint64_t blk = (uint64_t)P.ld * 16u;
-        return rsrc_words(reinterpret_cast<uint64_t>(P.X) + (uint64_t)(tok / 8) * blk,
+        return rsrc_words(reinterpret_cast<uint64_t>(X) + (uint64_t)(tok / 8) * blk,
                           ((valid + 7) / 8) * (int64_t)blk);
       } else {
-        const uint64_t base = reinterpret_cast<uint64_t>(P.X) + (uint64_t)tok * row_bytes;
+        const uint64_t base = reinterpret_cast<uint64_t>(X) + (uint64_t)tok * row_bytes;
         return rsrc_words(base, valid * row_bytes);
       }
     };
@@ -338,7 +339,7 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
     // the descriptor's range: their loads read zero and their stores are
     // dropped.
     const __amdgpu_buffer_rsrc_t sr =
-        make_rsrc(reinterpret_cast<uint64_t>(P.S) + (uint64_t)((int64_t)I * kT * P.lds * 4), (int64_t)kT * P.lds * 4);
+        make_rsrc(reinterpret_cast<uint64_t>(S) + (uint64_t)((int64_t)I * kT * P.lds * 4), (int64_t)kT * P.lds * 4);
     const int rlim = P.d - I * kT, clim = P.d - J * kT;  // tile-local row / column limits
     auto soff = [&](int m, int n) -> uint32_t {
       const int r = rr + 16 * m, c = cc + 16 * n;
@@ -365,6 +366,26 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
       }
     }
   };
+
+  if constexpr (Grouped) {
+    // Whole tiles of several Hessians (groups sorted by token count, largest
+    // first; item = group * ntiles + tile), dealt to the workgroups in rounds
+    // of 256 in snake order (forward, then backward) so that each
+    // workgroup's share is about even; within a round the 32 workgroups of
+    // an XCD take consecutive tiles of one group.
+    const int bid = blockIdx.x;
+    const int q = (bid & 7) * 32 + (bid >> 3);
+    for (int r = 0;; ++r) {
+      const int item = r * 256 + ((r & 1) ? 255 - q : q);
+      if (item >= G->nitems) break;
+      const int g = item / P.ntiles, t = item - g * P.ntiles;
+      const int64_t ng = G->n[g];
+      const int k1 = (int)((ng + kKI - 1) / kKI);
+      const char* Xg = static_cast<const char*>(G->X) + G->blk[g] * (int64_t)P.ld * 16;
+      segment(__builtin_amdgcn_readfirstlane(t), 0, __builtin_amdgcn_readfirstlane(k1), -1, Xg, ng, G->S[g]);
+    }
+    return;
+  }
 
   // work of this workgroup: one whole tile (the first dp_tiles tiles of the
   // order, XCD by XCD), or one aligned part of a tile plus a share of the
@@ -417,12 +438,18 @@ __device__ __forceinline__ void big_body(const BigParams& P) {
     k0 = __builtin_amdgcn_readfirstlane(k0);
     k1 = __builtin_amdgcn_readfirstlane(k1);
     slot = __builtin_amdgcn_readfirstlane(slot);
-    if (k0 < k1) segment(tile, k0, k1, slot);
+    if (k0 < k1) segment(tile, k0, k1, slot, P.X, P.n, P.S);
   }
 }
 
-__global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) { big_body<false>(P); }
-__global__ void __launch_bounds__(256, 1) syrk_big_bf16_t8(BigParams P) { big_body<true>(P); }
+__global__ void __launch_bounds__(256, 1) syrk_big_bf16(BigParams P) { big_body<false, false>(P, nullptr); }
+__global__ void __launch_bounds__(256, 1) syrk_big_bf16_t8(BigParams P) { big_body<true, false>(P, nullptr); }
+
+// Grouped launch on transposed staging: the tile geometry comes from P
+// (order, d, nb, ntiles, ld = d, lds = d), the groups from G.
+__global__ void __launch_bounds__(256, 1) syrk_big_t8_grouped(BigParams P, BigGroupParams G) {
+  big_body<true, true>(P, &G);
+}
 
 // S_tile += the other parts and the pieces of tile t, in item order (pieces
 // of one excess item in workgroup order): a fixed order, so results do not
@@ -497,6 +524,12 @@ hipError_t launch_syrk_big(const BigParams& P, hipStream_t stream) {
     hipLaunchKernelGGL(syrk_big_bf16_t8, dim3(grid), dim3(256), 0, stream, P);
   else
     hipLaunchKernelGGL(syrk_big_bf16, dim3(grid), dim3(256), 0, stream, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_syrk_big_grouped(const BigParams& P, const BigGroupParams& G, hipStream_t stream) {
+  if (G.nitems <= 0) return hipSuccess;
+  hipLaunchKernelGGL(syrk_big_t8_grouped, dim3(256), dim3(256), 0, stream, P, G);
   return hipGetLastError();
 }
 

@@ -508,6 +508,78 @@ def test_grouped_experts(gather):
         hsx[e].close()
 
 
+def _grouped_check(d, T, E, topk, seed, gather, chunk=0, empty=(), tol=None):
+    """Grouped update of E experts against the oracle's per-expert Gram sums."""
+    rng = np.random.default_rng(seed)
+    x = W.encode(W.normal_rows(rng, T, d, W.column_scales(rng, d)), W.BF16)
+    row_idx, offsets = W.moe_routing(rng, T, experts=E, topk=topk)
+    for e in empty:  # drop expert e's rows: an empty group
+        n_e = offsets[e + 1] - offsets[e]
+        row_idx = np.concatenate([row_idx[:offsets[e]], row_idx[offsets[e + 1]:]])
+        offsets[e + 1:] -= n_e
+    hsx = [hs.Hessian(d, torch.bfloat16, staging_bytes=0) for _ in range(E)]
+    hs.set_group_chunk(chunk)
+    try:
+        if gather:
+            hs.add_batch_grouped(hsx, to_device(x, W.BF16), offsets, torch.from_numpy(row_idx).cuda())
+            src, idx = x, row_idx
+        else:
+            xg = x[row_idx]
+            hs.add_batch_grouped(hsx, to_device(xg, W.BF16), offsets)
+            src, idx = xg, np.arange(xg.shape[0], dtype=np.int32)
+    finally:
+        hs.set_group_chunk(0)
+    ref = O.grouped_grams(src, W.BF16, idx, offsets)
+    for e in range(E):
+        S_e, N_e = ref[e]
+        assert hsx[e].nsamples == N_e
+        H, _, _ = hsx[e].materialize(0.0, neutralize=False)
+        Hr, _, _ = O.materialize(S_e, N_e, 0.0, neutralize=False)
+        if N_e == 0:
+            assert not H.cpu().numpy().any()
+        else:
+            assert agreement(H.cpu().numpy(), Hr) <= (TOL[W.BF16] if tol is None else tol), e
+        hsx[e].close()
+
+
+@pytest.mark.parametrize("gather", [True, False])
+def test_grouped_big_tiles(gather):
+    """Width 1,032 (edge tiles) on the 256-tile grouped path: 9 experts, one of them empty,
+    group sizes not multiples of 8 or 32."""
+    _say(f"grouped 256-tile gather={gather}")
+    _grouped_check(1032, 700, 9, 3, seed=52, gather=gather, empty=(4,))
+
+
+@pytest.mark.parametrize("chunk", [1032 * 16 * 3, 1032 * 16 * 40])
+def test_grouped_big_tiles_refills(chunk):
+    """A gather buffer of 3 (or 40) 8-row blocks: groups are split over many fills."""
+    _say(f"grouped 256-tile refills chunk={chunk}")
+    _grouped_check(1032, 500, 6, 2, seed=53, gather=True, chunk=chunk)
+
+
+def test_grouped_moe_full_size_sampled():
+    """The MoE workload at full size (32,768 tokens, top-8 of 64 experts, width 2,048): sampled
+    entries and the whole diagonal of the largest, the smallest and two middle experts."""
+    _say("grouped MoE full size")
+    rng = np.random.default_rng(3)
+    d, T, E = 2048, 32768, 64
+    x = W.encode(W.normal_rows(rng, T, d, W.column_scales(rng, d)), W.BF16)
+    row_idx, offsets = W.moe_routing(rng, T, experts=E, topk=8)
+    hsx = [hs.Hessian(d, torch.bfloat16, staging_bytes=0) for _ in range(E)]
+    hs.add_batch_grouped(hsx, to_device(x, W.BF16), offsets, torch.from_numpy(row_idx).cuda())
+    sizes = np.diff(offsets)
+    order = np.argsort(-sizes, kind="stable")
+    for e in [int(order[0]), int(order[-1]), int(order[E // 3]), int(order[2 * E // 3])]:
+        rows = row_idx[offsets[e]:offsets[e + 1]]
+        wl = W.Workload(d=d, dtype=W.BF16, batches=[x[rows]], dead_cols=np.zeros(0, dtype=np.int64),
+                        scales=np.ones(d))
+        err = _sampled_gram_check(hsx[e], wl, n_samples=300, seed=e)
+        assert hsx[e].nsamples == len(rows)
+        assert err <= TOL[W.BF16], (e, err)
+    for h in hsx:
+        h.close()
+
+
 def test_grouped_equals_single_handle_runs():
     _say("grouped equals single")
     rng = np.random.default_rng(51)
