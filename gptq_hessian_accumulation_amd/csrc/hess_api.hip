@@ -16,6 +16,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <queue>
 #include <vector>
 
 #include "../../include/hess.h"
@@ -70,6 +71,9 @@ struct BigWorkspace {
   int64_t slots = 0;          // 256 x 256 float slots
   void* gptr = nullptr;       // grouped updates: gathered rows in transposed staging layout
   int64_t gbytes = 0;
+  int32_t* hsched = nullptr;  // pinned host copy of a grouped launch's schedule
+  hipEvent_t sched_ev = nullptr;
+  bool sched_pending = false; // a copy out of hsched may still be running
   hipEvent_t ev = nullptr;
   bool used = false;
   hipStream_t last = nullptr;
@@ -203,7 +207,10 @@ constexpr int kBig = 256;
 constexpr int kBigKI = 32;               // tokens per iteration
 constexpr int kBigMinD = 1024;           // automatic choice: widths at least this wide ...
 constexpr int64_t kBigMinWork = 300;     // ... and at least this many iterations per workgroup
-constexpr int64_t kGroupScratch = (int64_t)512 << 20;  // gathered rows of grouped updates, per device
+constexpr int64_t kGroupScratchMax = (int64_t)4 << 30;  // largest gather buffer of grouped updates, per device
+// its tail holds one launch's schedule: 257 offsets and at most 64 groups x ntiles items (d <= 32768)
+constexpr int64_t kGroupSchedBytes = (int64_t)(kCUs + 1 + kBigMaxGroups * (128 * 129 / 2)) * 4;
+constexpr int64_t kGroupItemCost = 24;   // a tile's prologue and output, in 32-token iterations
 
 bool big_capable(int64_t d, int dtype) { return dtype == HESS_BF16 && d % 8 == 0 && d >= 8 && d <= 32768; }
 
@@ -368,8 +375,36 @@ int grouped_big(hess_t* hs, int n_groups, const void* X, int64_t ld, const int32
   const int64_t d = h0->d;
   BigWorkspace& W = g_big[h0->device];
   std::lock_guard<std::mutex> lock(W.mu);
-  if (!W.gptr) return fail(HESS_EHIP, "grouped scratch missing");
-  int64_t cap_bytes = W.gbytes;
+  // the gather buffer: grown (never shrunk) to this call's rows, up to 4 GiB
+  int64_t need = 0;
+  for (int e = 0; e < n_groups; ++e) need += (offsets[e + 1] - offsets[e] + 7) / 8 * 8 * d * 2;
+  need = std::min(need, kGroupScratchMax) + kGroupSchedBytes;
+  if (W.gbytes < need) {
+    hipError_t e = hipSuccess;
+    if (W.gptr) {
+      e = hipDeviceSynchronize();
+      if (e == hipSuccess) e = hipFree(W.gptr);
+      W.gptr = nullptr;
+      W.gbytes = 0;
+    }
+    if (e == hipSuccess) e = hipMalloc(&W.gptr, (size_t)need);
+    if (e != hipSuccess) {
+      W.gptr = nullptr;
+      const int code = (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) ? HESS_ENOMEM : HESS_EHIP;
+      return fail(code, "grouped gather buffer (%lld bytes): %s", (long long)need, hipGetErrorString(e));
+    }
+    W.gbytes = need;
+  }
+  if (!W.hsched) {
+    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&W.hsched), (size_t)kGroupSchedBytes, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&W.sched_ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (W.hsched) (void)hipHostFree(W.hsched);
+      W.hsched = nullptr;
+      return hip_fail(e, "grouped schedule buffer");
+    }
+  }
+  int64_t cap_bytes = W.gbytes - kGroupSchedBytes;
   if (g_group_chunk > 0) cap_bytes = std::min(cap_bytes, g_group_chunk);
   const int64_t cap_blocks = cap_bytes / (d * 16);  // 8-token blocks per fill
   if (cap_blocks < 1) return fail(HESS_EINVAL, "grouped scratch smaller than one 8-row block");
@@ -432,9 +467,56 @@ int grouped_big(hess_t* hs, int n_groups, const void* X, int64_t ld, const int32
     Gp.ngroups = k;
     err = launch_gather_rows_t8(Gp, s);
     if (err != hipSuccess) return hip_fail(err, "grouped gather launch");
+    // the schedule: items longest first, each to the least-loaded workgroup
+    // (cost: 32-token iterations plus a fixed cost for the tile's prologue
+    // and output); workgroup w's items are kept in the order dealt
+    const int nitems = k * P.ntiles;
+    std::vector<std::vector<int32_t>> lists(kCUs);
+    {
+      std::vector<int> idx(k);
+      for (int g = 0; g < k; ++g) idx[g] = g;
+      std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return Gb.n[a] > Gb.n[b]; });
+      using Slot = std::pair<int64_t, int>;
+      std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> pq;
+      for (int w = 0; w < kCUs; ++w) pq.push({0, w});
+      for (int g : idx) {
+        const int64_t cost = (Gb.n[g] + kBigKI - 1) / kBigKI + kGroupItemCost;
+        for (int t = 0; t < P.ntiles; ++t) {
+          Slot sl = pq.top();
+          pq.pop();
+          lists[sl.second].push_back(g * P.ntiles + t);
+          pq.push({sl.first + cost, sl.second});
+        }
+      }
+    }
+    // the schedule goes through the pinned host buffer (once the previous
+    // copy out of it has run) into the gather buffer's last bytes
+    if (W.sched_pending) {
+      err = hipEventSynchronize(W.sched_ev);
+      if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize");
+      W.sched_pending = false;
+    }
+    // slot s runs on workgroup (s / 32) + 8 (s % 32), i.e. slots 32x .. 32x+31
+    // on XCD x: ties go to the lowest slot, so the first 256 items (the
+    // largest groups' tiles in blocked order) reach the XCDs 32 at a time and
+    // neighbouring tiles share panels in one L2
+    int32_t* sched = W.hsched;
+    sched[0] = kCUs + 1;
+    for (int w = 0; w < kCUs; ++w) {
+      const std::vector<int32_t>& li = lists[(w & 7) * 32 + (w >> 3)];
+      std::copy(li.begin(), li.end(), sched + sched[w]);
+      sched[w + 1] = sched[w] + (int32_t)li.size();
+    }
+    int32_t* dsched = reinterpret_cast<int32_t*>(static_cast<char*>(W.gptr) + W.gbytes - kGroupSchedBytes);
+    err = hipMemcpyAsync(dsched, sched, (size_t)(kCUs + 1 + nitems) * sizeof(int32_t), hipMemcpyHostToDevice, s);
+    if (err != hipSuccess) return hip_fail(err, "grouped schedule copy");
+    err = hipEventRecord(W.sched_ev, s);
+    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+    W.sched_pending = true;
     Gb.X = W.gptr;
+    Gb.sched = dsched;
     Gb.ngroups = k;
-    Gb.nitems = k * P.ntiles;
+    Gb.nitems = nitems;
     err = launch_syrk_big_grouped(P, Gb, s);
     if (err != hipSuccess) return hip_fail(err, "grouped 256-tile SYRK launch");
   }
@@ -543,11 +625,7 @@ hess_t hess_create_ex(int64_t d, int in_dtype, int64_t staging_bytes) {
         if (e == hipSuccess) e = hipMalloc(&W.ptr, (size_t)need * kBig * kBig * sizeof(float));
         if (e == hipSuccess) W.slots = need;
       }
-      // grouped updates gather their rows here (one buffer per device)
-      if (e == hipSuccess && d >= kBigMinD && !W.gptr) {
-        e = hipMalloc(&W.gptr, (size_t)kGroupScratch);
-        if (e == hipSuccess) W.gbytes = kGroupScratch;
-      }
+
     }
     // transposed staging when a full buffer's flush takes the 256-tile
     // kernel (with the tile override at create: 256 always, 128 never)

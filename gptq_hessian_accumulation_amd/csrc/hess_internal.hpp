@@ -87,7 +87,8 @@ hipError_t launch_syrk_big_fixup(const BigParams& P, hipStream_t stream);
 constexpr int kBigMaxGroups = 64;
 struct BigGroupParams {
   const void* X;
-  int nitems;             // ngroups * ntiles, groups in order of decreasing n
+  const int32_t* sched;   // workgroup w's items: sched[sched[w] .. sched[w + 1]) (257 offsets first)
+  int nitems;             // ngroups * ntiles (item = group * ntiles + tile)
   int ngroups;
   int64_t blk[kBigMaxGroups];
   int64_t n[kBigMaxGroups];

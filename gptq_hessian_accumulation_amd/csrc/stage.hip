@@ -60,31 +60,41 @@ __global__ void __launch_bounds__(256) copy_rows_elem(const E* X, int64_t ld, E*
 }
 
 // Transposed staging copy, 16-byte aligned rows: workgroup (g, F) moves
-// tokens 8g..8g+7 (zeros past n) of features F..F+255.  Its 256 threads read
-// the 8 x 512-byte row pieces into LDS with 16-byte loads, then thread t
-// gathers feature F + t's 8 tokens and writes them as one chunk, so that
-// both the reads and the writes are contiguous across the workgroup.
+// tokens 8g..8g+7 (zeros past n) of features F .. F + kCQ * 256 - 1.  Its
+// 256 threads read the 8 rows' pieces into LDS with 16-byte loads (all
+// quarters' loads in flight at once), then thread t gathers each quarter's
+// feature F + 256 k + t over the 8 tokens and writes them as one chunk, so
+// that both the reads and the writes are contiguous across the workgroup.
+constexpr int kCQ = 2;
 __global__ void __launch_bounds__(256) copy_rows_t8(const char* X, int64_t ld_bytes, char* dst, int64_t n, int d,
-                                                    int fq) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[8][256];
+                                                    int nq) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kCQ][8][256];
   const int t = threadIdx.x;
-  const int64_t g = blockIdx.x / fq;
-  const int F = (int)(blockIdx.x - g * fq) * 256;
+  const int64_t g = blockIdx.x / nq;
+  const int F = (int)(blockIdx.x - g * nq) * (kCQ * 256);
   {
     const int r = t >> 5, q = t & 31;
     const int64_t tok = 8 * g + r;
-    const int f = F + 8 * q;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (tok < n && f < d) v = *reinterpret_cast<const u32x4*>(X + tok * ld_bytes + (int64_t)f * 2);
-    *reinterpret_cast<u32x4*>(&tile[r][8 * q]) = v;
+    u32x4 v[kCQ];
+#pragma unroll
+    for (int k = 0; k < kCQ; ++k) {
+      const int f = F + k * 256 + 8 * q;
+      v[k] = (tok < n && f < d) ? *reinterpret_cast<const u32x4*>(X + tok * ld_bytes + (int64_t)f * 2)
+                                : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kCQ; ++k) *reinterpret_cast<u32x4*>(&tile[k][r][8 * q]) = v[k];
   }
   __syncthreads();
-  const int f = F + t;
-  if (f < d) {
-    u32x4 c;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) c[p] = (uint32_t)tile[2 * p][t] | ((uint32_t)tile[2 * p + 1][t] << 16);
-    *reinterpret_cast<u32x4*>(dst + (g * d + f) * 16) = c;
+  for (int k = 0; k < kCQ; ++k) {
+    const int f = F + k * 256 + t;
+    if (f < d) {
+      u32x4 c;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) c[p] = (uint32_t)tile[k][2 * p][t] | ((uint32_t)tile[k][2 * p + 1][t] << 16);
+      *reinterpret_cast<u32x4*>(dst + (g * d + f) * 16) = c;
+    }
   }
 }
 
@@ -98,14 +108,18 @@ __global__ void __launch_bounds__(256) copy_rows_t8_elem(const uint16_t* X, int6
 }
 
 // Transposed staging copy of gathered rows for grouped updates: workgroup
-// (block, F) finds its group by the block prefix, then moves as
-// copy_rows_t8 does, with each token's row looked up in rows (or taken in
-// order).  Rows are 16-byte aligned (checked by the caller).
+// (block, quarter pair) finds its group by the block prefix, then moves
+// tokens 8 block .. +7 of features F .. F + kGQ * 256 - 1 as copy_rows_t8
+// does, with each token's row looked up in rows (or taken in order); the
+// loads of all its quarters are issued before the first is written.  Rows
+// are 16-byte aligned (checked by the caller).
+constexpr int kGQ = 4;
 __global__ void __launch_bounds__(256) gather_rows_t8(GatherParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[8][256];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kGQ][8][256];
   const int t = threadIdx.x;
-  const int64_t gb = blockIdx.x / P.fq;
-  const int F = (int)(blockIdx.x - gb * P.fq) * 256;
+  const int nq = (P.fq + kGQ - 1) / kGQ;
+  const int64_t gb = blockIdx.x / nq;
+  const int F0 = (int)(blockIdx.x - gb * nq) * (kGQ * 256);
   int lo = 0, hi = P.ngroups;  // last group g with blk_prefix[g] <= gb
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -117,29 +131,39 @@ __global__ void __launch_bounds__(256) gather_rows_t8(GatherParams P) {
   {
     const int r = t >> 5, q = t & 31;
     const int64_t tok = 8 * b + r;
-    const int f = F + 8 * q;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (tok < P.cnt[g] && f < P.d) {
+    const bool valid = tok < P.cnt[g];
+    int64_t row = 0;
+    if (valid) {
       const int64_t pos = P.beg[g] + tok;
-      const int64_t row = P.rows ? (int64_t)P.rows[pos] : pos;
-      v = *reinterpret_cast<const u32x4*>(static_cast<const char*>(P.X) + row * P.ld * 2 + (int64_t)f * 2);
+      row = P.rows ? (int64_t)P.rows[pos] : pos;
     }
-    *reinterpret_cast<u32x4*>(&tile[r][8 * q]) = v;
+    const char* src = static_cast<const char*>(P.X) + row * P.ld * 2;
+    u32x4 v[kGQ];
+#pragma unroll
+    for (int k = 0; k < kGQ; ++k) {
+      const int f = F0 + k * 256 + 8 * q;
+      v[k] = (valid && f < P.d) ? *reinterpret_cast<const u32x4*>(src + (int64_t)f * 2) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kGQ; ++k) *reinterpret_cast<u32x4*>(&tile[k][r][8 * q]) = v[k];
   }
   __syncthreads();
-  const int f = F + t;
-  if (f < P.d) {
-    u32x4 c;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) c[p] = (uint32_t)tile[2 * p][t] | ((uint32_t)tile[2 * p + 1][t] << 16);
-    *reinterpret_cast<u32x4*>(static_cast<char*>(P.dst) + ((P.blk[g] + b) * P.d + f) * 16) = c;
+  for (int k = 0; k < kGQ; ++k) {
+    const int f = F0 + k * 256 + t;
+    if (f < P.d) {
+      u32x4 c;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) c[p] = (uint32_t)tile[k][2 * p][t] | ((uint32_t)tile[k][2 * p + 1][t] << 16);
+      *reinterpret_cast<u32x4*>(static_cast<char*>(P.dst) + ((P.blk[g] + b) * P.d + f) * 16) = c;
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_gather_rows_t8(const GatherParams& P, hipStream_t stream) {
-  const int64_t wgs = P.blk_prefix[P.ngroups] * P.fq;
+  const int64_t wgs = P.blk_prefix[P.ngroups] * ((P.fq + kGQ - 1) / kGQ);
   if (wgs <= 0) return hipSuccess;
   if (wgs >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gather_rows_t8, dim3((unsigned)wgs), dim3(256), 0, stream, P);
@@ -152,11 +176,11 @@ hipError_t launch_copy_rows_t8(const void* X, int64_t ld, int64_t n, int64_t d, 
   const int64_t blocks8 = (n + 7) / 8;
   const bool vec = (reinterpret_cast<uintptr_t>(X) & 15u) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0 &&
                    ((ld * 2) & 15) == 0;
-  const int64_t fq = (d + 255) / 256;
-  const int64_t wgs = blocks8 * fq;
+  const int64_t nq = (d + kCQ * 256 - 1) / (kCQ * 256);
+  const int64_t wgs = blocks8 * nq;
   if (vec && wgs < ((int64_t)1 << 31)) {
     hipLaunchKernelGGL(copy_rows_t8, dim3((unsigned)wgs), dim3(256), 0, stream, static_cast<const char*>(X), ld * 2,
-                       static_cast<char*>(dst), n, (int)d, (int)fq);
+                       static_cast<char*>(dst), n, (int)d, (int)nq);
   } else {
     const int64_t elems = blocks8 * 8 * d;
     int64_t blocks = (elems + 255) / 256;

@@ -368,16 +368,14 @@ __device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParam
   };
 
   if constexpr (Grouped) {
-    // Whole tiles of several Hessians (groups sorted by token count, largest
-    // first; item = group * ntiles + tile), dealt to the workgroups in rounds
-    // of 256 in snake order (forward, then backward) so that each
-    // workgroup's share is about even; within a round the 32 workgroups of
-    // an XCD take consecutive tiles of one group.
+    // Whole tiles of several Hessians (item = group * ntiles + tile); the
+    // host deals them out (longest first, each to the least-loaded
+    // workgroup) and lists each workgroup's items in G->sched.
     const int bid = blockIdx.x;
-    const int q = (bid & 7) * 32 + (bid >> 3);
-    for (int r = 0;; ++r) {
-      const int item = r * 256 + ((r & 1) ? 255 - q : q);
-      if (item >= G->nitems) break;
+    const int i0 = __builtin_amdgcn_readfirstlane(G->sched[bid]);
+    const int i1 = __builtin_amdgcn_readfirstlane(G->sched[bid + 1]);
+    for (int ii = i0; ii < i1; ++ii) {
+      const int item = __builtin_amdgcn_readfirstlane(G->sched[ii]);
       const int g = item / P.ntiles, t = item - g * P.ntiles;
       const int64_t ng = G->n[g];
       const int k1 = (int)((ng + kKI - 1) / kKI);

@@ -82,9 +82,7 @@ const char* hess_last_error(void);
  * d % 8 == 0 a small tile-order table.  Such handles also make sure the
  * device's shared 256-tile workspace holds (512 + ntiles % 256) slots of
  * 256 KiB, ntiles = nb (nb + 1) / 2 with nb = ceil(d / 256) (162 MiB at
- * d = 4096), and, for d >= 1,024, that the device has the 512 MiB buffer in
- * which hess_add_batch_grouped gathers rows; both live until the process
- * ends.  N = 0.
+ * d = 4096); that buffer lives until the process ends.  N = 0.
  *   d         number of input features (Hessian width), 1 <= d <= 65536.
  *   in_dtype  HESS_BF16 or HESS_F32: the element type of every X later given
  *             to hess_add_batch (Model-Optimizer PR 3002, hessian_input_dtype).
@@ -192,10 +190,9 @@ int hess_flush(hess_t h, hess_stream_t stream);
 int hess_set_staging(int enable);
 
 /* Test hook, process-wide: cap (bytes, > 0) on the rows gathered per
- * 256-tile grouped launch (hess_add_batch_grouped gathers the groups' rows
- * into a 512 MiB per-device buffer in 8-token blocks and fills it as often as
- * needed, splitting groups that do not fit); 0 (default) = the whole buffer.
- * EINVAL for a negative value. */
+ * 256-tile grouped launch (hess_add_batch_grouped fills its gather buffer as
+ * often as needed, splitting groups that do not fit); 0 (default) = the
+ * whole buffer.  EINVAL for a negative value. */
 int hess_set_group_chunk(int64_t bytes);
 
 /* S = 0, N = 0 (enqueued on stream); also re-arms a consumed handle. */
@@ -276,12 +273,15 @@ int hess_local_blocks_ex(const void* X, int in_dtype, int64_t n_tokens, int64_t 
  * All row indices must be in [0, T) where T is the caller's row count; the
  * library cannot check device contents.
  * bf16 handles with d % 8 == 0, d >= 1,024 and 16-byte aligned rows take
- * 256-tiles: the groups' rows are first gathered into a per-device 512 MiB
- * buffer (allocated by hess_create with the 256-tile workspace) in the
- * transposed staging layout, then one launch adds whole upper tiles of every
- * group; groups beyond one buffer-full take further fills (see
- * hess_set_group_chunk).  Other handles take 128-tiles with rows gathered
- * by the kernel.
+ * 256-tiles: the groups' rows are first gathered into a per-device buffer in
+ * the transposed staging layout (8-row blocks per group), then one launch
+ * adds whole upper tiles of every group.  The first such call on a device,
+ * and any later one with more rows, allocates that buffer (after a device
+ * synchronize if it replaces a smaller one): sum over groups of
+ * ceil(rows / 8) * 8 * d * 2 bytes, at most 4 GiB; rows beyond it take
+ * further fills (see hess_set_group_chunk).  The buffer lives until the
+ * process ends.  Other handles take 128-tiles with rows gathered by the
+ * kernel.
  */
 int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld,
                            const int32_t* row_idx, const int64_t* offsets, hess_stream_t stream);
