@@ -169,7 +169,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--extras", default="all",
-                    help="comma-separated subset of d4096_ragged,d4096_single,moe,local (default all)")
+                    help="comma-separated subset of d4096_ragged,d4096_single,moe,local,imatrix (default all; "
+                         "imatrix runs with local)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--print-kernel-sha", action="store_true",
                     help="print the sha256 of the SYRK kernel sources and exit")
@@ -274,7 +275,8 @@ def main():
 def run_extras(torch, hs, W, args):
     extra = {}
     steps = max(3, args.steps // 2)
-    want = set(args.extras.split(",")) if args.extras != "all" else {"d4096_ragged", "d4096_single", "moe", "local"}
+    want = set(args.extras.split(",")) if args.extras != "all" else {"d4096_ragged", "d4096_single", "moe", "local",
+                                                                    "imatrix"}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # d=4096 ragged (bf16 and fp32), dead columns 1%
     for dt, tdt in (() if "d4096_ragged" not in want else (("bf16", torch.bfloat16), ("f32", torch.float32))):
@@ -376,6 +378,24 @@ def run_extras(torch, hs, W, args):
         byts = 32768 * 4096 * 2 + 256 * 256 * 4 * 2
         extra["local_32768x4096"] = {"ms_per_update": round(per, 4), "GBps": round(byts / per / 1e6, 1),
                                      "hbm_frac": round(byts / (per * 1e-3) / HBM, 4), "pages_rtx_pro_6000_ms": 0.40}
+        if "imatrix" in want:
+            # imatrix per-column sums of squares over the same 16 cold buffers
+            log("imatrix")
+            m = hs.ImatrixStat(4096, torch.bfloat16)
+            for xx in xs[:2]:
+                m.add_batch(xx)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                for xx in xs:
+                    m.add_batch(xx)
+            e1.record()
+            torch.cuda.synchronize()
+            per = e0.elapsed_time(e1) / (reps * 16)
+            byts = 32768 * 4096 * 2 + 4096 * 4 * 2
+            extra["imatrix_32768x4096"] = {"ms_per_update": round(per, 4), "GBps": round(byts / per / 1e6, 1),
+                                           "hbm_frac": round(byts / (per * 1e-3) / HBM, 4)}
+            m.close()
         del xs
     torch.cuda.empty_cache()
     return extra

@@ -95,6 +95,11 @@ def _load():
         "hess_local_blocks": (c_int, [vp, i64, i64, c_int, vp]),
         "hess_local_blocks_ex": (c_int, [vp, c_int, i64, i64, i64, c_int, vp, c_int, vp]),
         "hess_add_batch_grouped": (c_int, [ctypes.POINTER(vp), c_int, vp, i64, vp, ctypes.POINTER(i64), vp]),
+        "hess_imatrix_create": (vp, [i64, c_int]),
+        "hess_imatrix_destroy": (c_int, [vp]),
+        "hess_imatrix_add_batch": (c_int, [vp, vp, i64, i64, vp]),
+        "hess_imatrix_read": (c_int, [vp, vp, ctypes.POINTER(i64), vp]),
+        "hess_imatrix_reset": (c_int, [vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -284,6 +289,47 @@ def local_blocks(x: torch.Tensor, out: torch.Tensor | None = None, accumulate: b
     _check(_load().hess_local_blocks_ex(ptr, _dtype_code(x.dtype), n, d, ld, block, out.data_ptr(),
                                         1 if accumulate else 0, _stream(stream)))
     return out
+
+
+class ImatrixStat:
+    """Per-column float32 sums of squares of a layer's inputs (the imatrix statistic)."""
+
+    def __init__(self, d: int, dtype=torch.bfloat16):
+        self.d = int(d)
+        self.dtype = dtype
+        self._h = _load().hess_imatrix_create(self.d, _dtype_code(dtype))
+        if not self._h:
+            raise HessError(-1, _load().hess_last_error().decode(errors="replace"))
+
+    def add_batch(self, x: torch.Tensor, stream=None) -> None:
+        if not x.is_cuda:
+            raise ValueError("activations must be on the GPU")
+        if x.dtype != self.dtype:
+            raise ValueError(f"expected {self.dtype} activations, got {x.dtype}")
+        x2, n, ld = _as_rows(x, self.d)
+        _check(_load().hess_imatrix_add_batch(self._h, x2.data_ptr() if n > 0 else None, n, ld, _stream(stream)))
+
+    def read(self, out: torch.Tensor | None = None, stream=None):
+        """(sums, tokens): the float32 per-column sums and the token count."""
+        if out is None:
+            out = torch.empty(self.d, dtype=torch.float32, device="cuda")
+        n = ctypes.c_int64()
+        _check(_load().hess_imatrix_read(self._h, out.data_ptr(), ctypes.byref(n), _stream(stream)))
+        return out, int(n.value)
+
+    def reset(self, stream=None) -> None:
+        _check(_load().hess_imatrix_reset(self._h, _stream(stream)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _check(_load().hess_imatrix_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def add_batch_grouped(hessians, x: torch.Tensor, offsets, row_idx: torch.Tensor | None = None, stream=None) -> None:

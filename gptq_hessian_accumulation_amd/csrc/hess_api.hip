@@ -59,6 +59,17 @@ struct hess_s {
   int ntiles256 = 0;
 };
 
+struct hess_imx_s {
+  int64_t d = 0;
+  int dtype = HESS_BF16;
+  float* acc = nullptr;      // d floats: the running per-column sums of squares
+  float* part = nullptr;     // (kImxSplits + 32) x d floats: one batch's split partials and their run sums
+  int64_t N = 0;
+  bool has_stream = false;
+  hipStream_t last = nullptr;
+  hipEvent_t ev = nullptr;
+};
+
 namespace {
 
 // Stream-K workspace of the 256-tile path, one per device, shared by every
@@ -180,6 +191,20 @@ int64_t stage_tokens(int64_t d, int es, int64_t bytes) {
 // below 4 d^2, i.e. n < 2 d / esize.
 bool stage_pays(const hess_s* h, int64_t n) {
   return g_staging && h->stage && n <= h->stage_cap && n * esize(h->dtype) < 2 * h->d;
+}
+
+constexpr int64_t kImxSplits = 1024;  // row splits of one imatrix batch (partials per column)
+
+// Calls on an imatrix handle from a new stream wait for the previous stream's work.
+int imx_order_stream(hess_imx_t m, hipStream_t s) {
+  if (m->has_stream && m->last != s) {
+    hipError_t e = hipEventRecord(m->ev, m->last);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, m->ev, 0);
+    if (e != hipSuccess) return hip_fail(e, "imatrix stream ordering");
+  }
+  m->has_stream = true;
+  m->last = s;
+  return HESS_OK;
 }
 
 // Timing events around one SYRK pass (hess_set_timing).
@@ -909,6 +934,93 @@ int hess_local_blocks_ex(const void* X, int in_dtype, int64_t n_tokens, int64_t 
 
 int hess_local_blocks(const void* X, int64_t n_tokens, int64_t d, int block, float* out) {
   return hess_local_blocks_ex(X, HESS_BF16, n_tokens, d, d, block, out, 1, nullptr);
+}
+
+// ---- imatrix statistic: per-column float32 sums of squares ----
+
+hess_imx_t hess_imatrix_create(int64_t d, int in_dtype) {
+  if (d < 1 || d > ((int64_t)1 << 24)) {
+    fail(HESS_EINVAL, "d = %lld outside [1, 2^24]", (long long)d);
+    return nullptr;
+  }
+  if (in_dtype != HESS_BF16 && in_dtype != HESS_F32) {
+    fail(HESS_EINVAL, "unknown input dtype %d", in_dtype);
+    return nullptr;
+  }
+  hess_imx_t m = new (std::nothrow) hess_imx_s();
+  if (!m) {
+    fail(HESS_ENOMEM, "host allocation failed");
+    return nullptr;
+  }
+  m->d = d;
+  m->dtype = in_dtype;
+  hipError_t e = hipMalloc(&m->acc, (size_t)d * sizeof(float));
+  if (e == hipSuccess) e = hipMalloc(&m->part, (size_t)(kImxSplits + 32) * d * sizeof(float));
+  if (e == hipSuccess) e = hipMemset(m->acc, 0, (size_t)d * sizeof(float));
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    const int code = (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) ? HESS_ENOMEM : HESS_EHIP;
+    fail(code, "hess_imatrix_create(d=%lld): %s", (long long)d, hipGetErrorString(e));
+    (void)hipGetLastError();
+    if (m->acc) (void)hipFree(m->acc);
+    if (m->part) (void)hipFree(m->part);
+    if (m->ev) (void)hipEventDestroy(m->ev);
+    delete m;
+    return nullptr;
+  }
+  return m;
+}
+
+int hess_imatrix_destroy(hess_imx_t m) {
+  if (!m) return fail(HESS_EINVAL, "null handle");
+  hipError_t e = hipSuccess;
+  if (m->has_stream) e = hipStreamSynchronize(m->last);
+  (void)hipFree(m->acc);
+  (void)hipFree(m->part);
+  (void)hipEventDestroy(m->ev);
+  delete m;
+  return e == hipSuccess ? HESS_OK : hip_fail(e, "hess_imatrix_destroy");
+}
+
+int hess_imatrix_add_batch(hess_imx_t m, const void* X, int64_t n_tokens, int64_t ld, hess_stream_t stream) {
+  if (!m) return fail(HESS_EINVAL, "null handle");
+  if (n_tokens < 0) return fail(HESS_EINVAL, "n_tokens = %lld < 0", (long long)n_tokens);
+  if (ld < m->d) return fail(HESS_EINVAL, "ld = %lld < d = %lld", (long long)ld, (long long)m->d);
+  if (n_tokens == 0) return HESS_OK;
+  if (!X) return fail(HESS_EINVAL, "X is NULL with n_tokens > 0");
+  if (reinterpret_cast<uintptr_t>(X) % esize(m->dtype) != 0) return fail(HESS_EALIGN, "X not element-aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = imx_order_stream(m, s);
+  if (rc != HESS_OK) return rc;
+  const bool vec = vec_ok(X, ld, m->d, esize(m->dtype));
+  hipError_t e = launch_imatrix(X, m->dtype, n_tokens, (int)m->d, ld, vec, m->part, (int)kImxSplits, m->acc, s);
+  if (e != hipSuccess) return hip_fail(e, "imatrix launch");
+  m->N += n_tokens;
+  return HESS_OK;
+}
+
+int hess_imatrix_read(hess_imx_t m, float* out, int64_t* n_out, hess_stream_t stream) {
+  if (!m) return fail(HESS_EINVAL, "null handle");
+  if (!out) return fail(HESS_EINVAL, "out is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = imx_order_stream(m, s);
+  if (rc != HESS_OK) return rc;
+  hipError_t e = hipMemcpyAsync(out, m->acc, (size_t)m->d * sizeof(float), hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "imatrix read copy");
+  if (n_out) *n_out = m->N;
+  return HESS_OK;
+}
+
+int hess_imatrix_reset(hess_imx_t m, hess_stream_t stream) {
+  if (!m) return fail(HESS_EINVAL, "null handle");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = imx_order_stream(m, s);
+  if (rc != HESS_OK) return rc;
+  hipError_t e = launch_zero(m->acc, m->d, s);
+  if (e != hipSuccess) return hip_fail(e, "imatrix reset launch");
+  m->N = 0;
+  return HESS_OK;
 }
 
 }  // extern "C"

@@ -116,6 +116,12 @@ struct GatherParams {
 };
 hipError_t launch_gather_rows_t8(const GatherParams& P, hipStream_t stream);
 
+// acc[j] += sum_t X[t][j]^2 (float32), j < d; part holds (max_splits + 32) x d
+// floats: split partial sums, then sums of runs of 32 splits.  vec: X 16-byte aligned, ld * esize % 16 == 0
+// and d a multiple of 16 / esize.
+hipError_t launch_imatrix(const void* X, int in_dtype, int64_t n, int d, int64_t ld, bool vec, float* part,
+                          int max_splits, float* acc, hipStream_t stream);
+
 int syrk_tile_edge();
 hipError_t launch_syrk(const SyrkParams& P, int in_dtype, bool vec, int grid, hipStream_t stream);
 hipError_t launch_syrk_reduce(float* S, int64_t lds, const float* ws, int d, int nb, int full_tiles, int tail_tiles,

@@ -43,6 +43,7 @@ extern "C" {
 #define HESS_ABI_VERSION 1
 
 typedef struct hess_s* hess_t;
+typedef struct hess_imx_s* hess_imx_t;
 typedef void* hess_stream_t; /* a hipStream_t */
 
 /* Input element types.  bf16 products are exact in float32 and summed in
@@ -285,6 +286,35 @@ int hess_local_blocks_ex(const void* X, int in_dtype, int64_t n_tokens, int64_t 
  */
 int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld,
                            const int32_t* row_idx, const int64_t* offsets, hess_stream_t stream);
+
+/*
+ * imatrix statistic -- per-column float32 sums of squares of a layer's
+ * inputs, acc[j] = sum over every token of X[t][j]^2.  The imatrix method
+ * keeps this float32 statistic instead of a Gram matrix (NVIDIA
+ * Model-Optimizer PR 3002 page, "What does this PR do?": a per-column sum of
+ * squares, not a GEMM).  One streaming read of each batch.
+ *
+ * hess_imatrix_create -- an empty statistic of width d (1 <= d <= 2^24) for
+ *   inputs of in_dtype (HESS_BF16 or HESS_F32) on the current device: d
+ *   floats plus 1,024 x d floats of per-batch partial sums, allocated and
+ *   zeroed once.  NULL on error (EINVAL / ENOMEM / EHIP).
+ *   (1,056 x d floats of workspace in all: partials and their run sums.)
+ * hess_imatrix_add_batch -- acc += column sums of squares of X (device,
+ *   n_tokens x d row-major, row stride ld >= d, element-aligned), N +=
+ *   n_tokens; n_tokens = 0 is a no-op.  Each batch is summed in float32 over
+ *   up to 1,024 row runs whose partials are added in a fixed order.  Never
+ *   allocates.  EINVAL / EALIGN / EHIP.
+ * hess_imatrix_read -- copy acc (d floats) to the device buffer out,
+ *   enqueued on stream; *n_out (host, may be NULL) = N, the tokens seen.
+ * hess_imatrix_reset -- acc = 0, N = 0 (enqueued on stream).
+ * hess_imatrix_destroy -- free the handle after draining its last stream.
+ * A call on a different stream than the previous one waits for it (event).
+ */
+hess_imx_t hess_imatrix_create(int64_t d, int in_dtype);
+int hess_imatrix_add_batch(hess_imx_t m, const void* X, int64_t n_tokens, int64_t ld, hess_stream_t stream);
+int hess_imatrix_read(hess_imx_t m, float* out, int64_t* n_out, hess_stream_t stream);
+int hess_imatrix_reset(hess_imx_t m, hess_stream_t stream);
+int hess_imatrix_destroy(hess_imx_t m);
 
 #ifdef __cplusplus
 }

@@ -20,4 +20,5 @@ from .hess_oracle import (  # noqa: F401
     grouped_grams,
     local_blocks,
     materialize,
+    column_sum_squares,
 )

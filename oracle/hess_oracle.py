@@ -26,6 +26,8 @@ What it computes, and where the pages define it
 * ``grouped_grams``: one independent (S_e, N_e) per routed expert over the
   rows routed to it (Model-Optimizer PR 3002 page, "What does this PR do?":
   the option applies to every GPTQ Hessian, fused MoE experts included).
+* ``column_sum_squares``: the imatrix statistic, a per-column sum of squares
+  of the inputs (Model-Optimizer PR 3002 page, "What does this PR do?").
 
 Readings where the pages leave a step open (each is also listed in the
 design notes):
@@ -59,6 +61,7 @@ __all__ = [
     "grouped_grams",
     "gram_entries",
     "gram_exact_fraction",
+    "column_sum_squares",
 ]
 
 
@@ -189,6 +192,24 @@ def gram_entries(batches, in_dtype: str, rows: np.ndarray, cols: np.ndarray) -> 
         if Xd.shape[0] == 0:
             continue
         acc += np.einsum("tk,tk->k", Xd[:, rows], Xd[:, cols])
+    return acc
+
+
+def column_sum_squares(batches, in_dtype: str) -> np.ndarray:
+    """The imatrix statistic: per-column sum over every token of x_j^2.
+
+    The imatrix method keeps a float32 per-column sum of squares of the layer
+    inputs instead of a Gram matrix (NVIDIA Model-Optimizer PR 3002 page,
+    "What does this PR do?").  Here it is the float64 sum of the exact
+    squares of the stored values.
+    """
+    acc = None
+    for X in batches:
+        Xd = exact_float64(X, in_dtype)
+        if acc is None:
+            acc = np.zeros(Xd.shape[1], dtype=np.float64)
+        for t in range(Xd.shape[0]):
+            acc += Xd[t] * Xd[t]
     return acc
 
 

@@ -266,7 +266,25 @@ def pin_gram_entries(O, seed=13):
         assert abs(got[k] - float(S_exact[rows[k]][cols[k]])) <= 1e-14 * max(1, abs(float(S_exact[rows[k]][cols[k]])))
 
 
+def pin_imatrix(O, seed=14):
+    """Per-column sums of squares equal exact rational sums, over batches of both dtypes."""
+    rng = np.random.default_rng(seed)
+    d = 6
+    batches = [rng.standard_normal((n, d)).astype(np.float32) for n in (3, 0, 5, 1)]
+    got = O.column_sum_squares(batches, "f32")
+    rows = [r for b in batches for r in b.tolist()]
+    for j in range(d):
+        exact = sum(Fraction(float(r[j])) ** 2 for r in rows)
+        assert abs(got[j] - float(exact)) <= 1e-15 * float(exact) + 1e-300, (j, got[j], float(exact))
+    # bf16 inputs are decoded exactly: 0x3F80 = 1.0, 0xC040 = -3.0, 0x3F81 = 1 + 2^-7
+    bits = np.array([[0x3F80, 0xC040, 0x3F81], [0x0000, 0x3F80, 0xC040]], dtype=np.uint16)
+    got = O.column_sum_squares([bits], "bf16")
+    want = [1.0, 9.0 + 1.0, (1 + 2.0 ** -7) ** 2 + 9.0]
+    assert np.array_equal(got, np.array(want)), (got, want)
+
+
 ALL_PINS = [
+    pin_imatrix,
     pin_bruteforce_fraction,
     pin_orientation_hand,
     pin_worked_example,

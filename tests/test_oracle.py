@@ -35,6 +35,7 @@ def _ns(**over):
         decode_bf16=HO.decode_bf16,
         exact_float64=HO.exact_float64,
         gram_entries=HO.gram_entries,
+        column_sum_squares=HO.column_sum_squares,
     )
     base.update(over)
     return types.SimpleNamespace(**base)
@@ -169,7 +170,22 @@ def _entries_swapped(batches, in_dtype, rows, cols):
     return HO.gram_entries(batches, in_dtype, rows, (np.asarray(cols) + 1) % 9)  # wrong column index
 
 
+def _imx_not_squared(batches, in_dtype):
+    return sum(HO.exact_float64(X, in_dtype).sum(axis=0) for X in batches if len(X))  # mistake: sums x, not x^2
+
+
+def _imx_skips_last_row(batches, in_dtype):
+    return HO.column_sum_squares([X[:-1] if len(X) else X for X in batches], in_dtype)  # mistake: drops a token
+
+
+def _imx_shifted(batches, in_dtype):
+    return np.roll(HO.column_sum_squares(batches, in_dtype), 1)  # mistake: column index off by one
+
+
 MUTANTS = {
+    "imatrix_not_squared": _ns(column_sum_squares=_imx_not_squared),
+    "imatrix_skips_last_row": _ns(column_sum_squares=_imx_skips_last_row),
+    "imatrix_shifted": _ns(column_sum_squares=_imx_shifted),
     "counts_batches": _ns(GramAccumulator=_acc_class(add=_add_counts_batches)),
     "overwrites_sum": _ns(GramAccumulator=_acc_class(add=_add_overwrites)),
     "transposed_operand": _ns(GramAccumulator=_acc_class(add=_add_transposed)),

@@ -628,3 +628,60 @@ def test_kernel_timing_counts_launches():
     launches, tokens, ms = h.timing()
     assert (launches, tokens) == (1, 106)
     h.close()
+
+
+# ------------------------------------------------------------- imatrix --
+
+def _imatrix_check(d, sizes, dtype, seed, strided=False):
+    rng = np.random.default_rng(seed)
+    wl = W.ragged_case(d, sizes, seed=seed, dtype=dtype, dead_frac=0.0)
+    m = hs.ImatrixStat(d, torch_dtype(dtype))
+    for b in wl.batches:
+        xb = to_device(b, dtype)
+        if strided and xb.shape[0] > 0:
+            wide = torch.zeros((xb.shape[0], d + 3), dtype=xb.dtype, device=xb.device)
+            wide[:, :d] = xb
+            xb = wide[:, :d]
+        m.add_batch(xb)
+    got, n = m.read()
+    torch.cuda.synchronize()
+    ref = O.column_sum_squares(wl.batches, dtype)
+    assert n == sum(sizes)
+    got = got.double().cpu().numpy()
+    # every term is positive: a float32 sum of k terms is within k * 2^-24 of the column's value;
+    # here k <= rows per split + splits + batches < 850
+    rel = np.abs(got - ref) / np.maximum(ref, 1e-30)
+    assert rel.max() <= 5e-5, rel.max()
+    m.close()
+    return rng
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+@pytest.mark.parametrize("d", [8, 17, 1032, 4096])
+def test_imatrix_parity(d, dtype):
+    """Per-column float32 sums of squares against the oracle: vector and element paths,
+    ragged batches including empty and 1-token ones."""
+    _say(f"imatrix d={d} {dtype}")
+    _imatrix_check(d, [1, 0, 700, 33, 4000], dtype, seed=600 + d)
+
+
+def test_imatrix_strided_rows_and_reset():
+    _say("imatrix strided rows, reset")
+    _imatrix_check(1032, [300, 41], W.BF16, seed=610, strided=True)
+    m = hs.ImatrixStat(64, torch.float32)
+    x = torch.randn(100, 64, device="cuda")
+    m.add_batch(x)
+    m.reset()
+    m.add_batch(x[:10])
+    got, n = m.read()
+    torch.cuda.synchronize()
+    assert n == 10
+    ref = (x[:10].double() ** 2).sum(0).cpu().numpy()
+    assert np.max(np.abs(got.double().cpu().numpy() - ref) / ref) <= 5e-5
+    m.close()
+
+
+def test_imatrix_full_size():
+    """32,768 tokens x 4,096 features bf16 (the local-blocks workload's shape) against the oracle."""
+    _say("imatrix full size 32768x4096")
+    _imatrix_check(4096, [32768], W.BF16, seed=620)
