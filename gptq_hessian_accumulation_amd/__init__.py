@@ -95,6 +95,7 @@ def _load():
         "hess_local_blocks": (c_int, [vp, i64, i64, c_int, vp]),
         "hess_local_blocks_ex": (c_int, [vp, c_int, i64, i64, i64, c_int, vp, c_int, vp]),
         "hess_add_batch_grouped": (c_int, [ctypes.POINTER(vp), c_int, vp, i64, vp, ctypes.POINTER(i64), vp]),
+        "hess_adopt": (c_int, [vp, vp, vp]),
         "hess_imatrix_create": (vp, [i64, c_int]),
         "hess_imatrix_destroy": (c_int, [vp]),
         "hess_imatrix_add_batch": (c_int, [vp, vp, i64, i64, vp]),
@@ -245,6 +246,10 @@ class Hessian:
 
     def reset(self, stream=None) -> None:
         _check(_load().hess_reset(self._h, _stream(stream)))
+
+    def adopt_from(self, leader: "Hessian", stream=None) -> None:
+        """Replace this Hessian's statistics with a private copy of leader's (sum and token count)."""
+        _check(_load().hess_adopt(self._h, leader._h, _stream(stream)))
 
     def set_timing(self, on: bool) -> None:
         """Bracket every SYRK launch of this handle with HIP events on its stream."""

@@ -856,6 +856,26 @@ int hess_flush(hess_t h, hess_stream_t stream) {
   return flush_stage(h, s);
 }
 
+int hess_adopt(hess_t dst, hess_t src, hess_stream_t stream) {
+  if (!dst || !src) return fail(HESS_EINVAL, "null handle");
+  if (dst == src) return HESS_OK;
+  if (dst->d != src->d) return fail(HESS_EINVAL, "width mismatch: %lld vs %lld", (long long)dst->d, (long long)src->d);
+  if (src->consumed) return fail(HESS_ESTATE, "source was materialized in place; hess_reset it first");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = order_stream(src, s);
+  if (rc != HESS_OK) return rc;
+  rc = order_stream(dst, s);
+  if (rc != HESS_OK) return rc;
+  rc = flush_stage(src, s);  // the source's sum is complete
+  if (rc != HESS_OK) return rc;
+  hipError_t e = hipMemcpyAsync(dst->S, src->S, (size_t)src->d * src->d * sizeof(float), hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "adopt copy");
+  dst->stage_n = dst->stage_real = 0;  // the follower's own partials are dropped
+  dst->N = src->N;
+  dst->consumed = false;
+  return HESS_OK;
+}
+
 int hess_set_group_chunk(int64_t bytes) {
   if (bytes < 0) return fail(HESS_EINVAL, "group chunk must be >= 0");
   g_group_chunk = bytes;

@@ -117,6 +117,22 @@ hess_t hess_create_ex(int64_t d, int in_dtype, int64_t staging_bytes);
 int hess_destroy(hess_t h);
 
 /*
+ * hess_adopt -- dst takes a private copy of src's statistics: its Gram sum
+ * becomes a copy of src's (after src's staged rows are folded in) and its
+ * token count src's N; whatever dst held is dropped.  A follower that shares
+ * a leader's inputs adopts the leader's Hessian as an independent float32
+ * copy with the leader's sample count (GPTQModel PR 3052, "Shared-input
+ * Hessian dedup: plan metadata, E2E validation, and telemetry", What Changed
+ * > Phase 2 (looper Hessian dedup): adopt_hessian_from copies H and nsamples
+ * and clears the follower's partials; updating one afterwards leaves the
+ * other unchanged).
+ * dst == src is a no-op.  EINVAL: null handle or different d (the pages'
+ * column mismatch); ESTATE: src was materialized in place.  Enqueued on
+ * stream (both handles are ordered onto it).  Never allocates.
+ */
+int hess_adopt(hess_t dst, hess_t src, hess_stream_t stream);
+
+/*
  * hess_add_batch -- S += X^T X and N += n_tokens, in place.
  *
  * One calibration batch (GPTQModel PR 2979, What Changed: add_batch computes

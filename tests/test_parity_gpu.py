@@ -685,3 +685,44 @@ def test_imatrix_full_size():
     """32,768 tokens x 4,096 features bf16 (the local-blocks workload's shape) against the oracle."""
     _say("imatrix full size 32768x4096")
     _imatrix_check(4096, [32768], W.BF16, seed=620)
+
+
+# --------------------------------------------------------------- adopt --
+
+def test_adopt_is_private_copy():
+    """A follower adopts the leader's sum and token count (staged rows included), then diverges
+    without touching the leader; bad widths and consumed leaders are refused."""
+    _say("adopt")
+    d = 1032
+    wl = W.ragged_case(d, [5, 700, 3000, 17], seed=700, dtype=W.BF16, dead_frac=0.02)
+    more = W.ragged_case(d, [400, 9], seed=701, dtype=W.BF16)
+    leader, follower = hs.Hessian(d, torch.bfloat16), hs.Hessian(d, torch.bfloat16)
+    for b in wl.batches:
+        leader.add_batch(to_device(b, W.BF16))
+    follower.add_batch(to_device(more.batches[0], W.BF16))   # dropped by the adopt
+    follower.adopt_from(leader)
+    assert follower.nsamples == leader.nsamples == wl.total_tokens
+    A, _, _ = leader.materialize(0.01)
+    B, _, _ = follower.materialize(0.01)
+    torch.cuda.synchronize()
+    assert torch.equal(A, B)
+    for b in more.batches:
+        follower.add_batch(to_device(b, W.BF16))
+    A2, _, _ = leader.materialize(0.01)
+    torch.cuda.synchronize()
+    assert torch.equal(A, A2), "the leader changed"
+    both = W.Workload(d=d, dtype=W.BF16, batches=list(wl.batches) + list(more.batches))
+    H, dead, dmp = follower.materialize(0.01)
+    Hr, deadr, dmpr, Nr = run_oracle(both, 0.01, True)
+    assert follower.nsamples == Nr
+    assert np.array_equal(dead.cpu().numpy(), deadr)
+    assert agreement(H.cpu().numpy(), Hr) <= TOL[W.BF16]
+    follower.adopt_from(follower)   # no-op
+    other = hs.Hessian(d + 8, torch.bfloat16)
+    with pytest.raises(hs.HessError):
+        other.adopt_from(leader)
+    leader.materialize_in_place()
+    with pytest.raises(hs.HessError):
+        follower.adopt_from(leader)
+    for h in (leader, follower, other):
+        h.close()
