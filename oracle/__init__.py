@@ -21,4 +21,6 @@ from .hess_oracle import (  # noqa: F401
     local_blocks,
     materialize,
     column_sum_squares,
+    round_to_bf16,
+    staged_values,
 )

@@ -28,6 +28,14 @@ What it computes, and where the pages define it
   the option applies to every GPTQ Hessian, fused MoE experts included).
 * ``column_sum_squares``: the imatrix statistic, a per-column sum of squares
   of the inputs (Model-Optimizer PR 3002 page, "What does this PR do?").
+* Staging dtype: activations are first put into the accumulator's staging
+  type, then multiplied (GPTQModel PR 3052, "Shared-input Hessian dedup",
+  review finding P2: an fp16 activation of 1 + 2^-10 stays exact when staged
+  in fp32 and becomes 1.0 when staged in bf16; Model-Optimizer PR 3002 page,
+  "What does this PR do?": ``hessian_input_dtype`` bfloat16 versus the
+  float32 default).  ``round_to_bf16`` is IEEE round-to-nearest-even onto the
+  bf16 value set; fp16 and bf16 values are float32 values, so fp32 staging
+  changes nothing.
 
 Readings where the pages leave a step open (each is also listed in the
 design notes):
@@ -41,7 +49,8 @@ design notes):
 * local blocks are unscaled and accumulate across calls.
 
 The input decoding is exact: bf16 values are given as their uint16 bit
-patterns and widened bit-for-bit; float32 values widen exactly to float64.
+patterns and widened bit-for-bit; float32 and float16 values widen exactly to
+float64.
 Products of two such values are exact in float64 (<= 48 significant bits)
 and the sums carry only float64 rounding, about 1e-16 relative per add.
 """
@@ -62,6 +71,8 @@ __all__ = [
     "gram_entries",
     "gram_exact_fraction",
     "column_sum_squares",
+    "round_to_bf16",
+    "staged_values",
 ]
 
 
@@ -80,16 +91,62 @@ def decode_bf16(bits: np.ndarray) -> np.ndarray:
 def exact_float64(X: np.ndarray, in_dtype: str) -> np.ndarray:
     """The stored input values as float64, exactly.
 
-    ``in_dtype`` is ``"bf16"`` (X holds uint16 bit patterns) or ``"f32"``.
+    ``in_dtype`` is ``"bf16"`` (X holds uint16 bit patterns), ``"f32"`` or
+    ``"f16"`` (numpy float16).
     """
     if in_dtype == "bf16":
         return decode_bf16(X)
-    if in_dtype == "f32":
+    if in_dtype in ("f32", "f16"):
         X = np.asarray(X)
-        if X.dtype != np.float32:
-            raise TypeError("f32 input must be a float32 array")
+        want = np.float32 if in_dtype == "f32" else np.float16
+        if X.dtype != want:
+            raise TypeError(f"{in_dtype} input must be a {np.dtype(want).name} array")
         return X.astype(np.float64)
     raise ValueError(f"unknown input dtype {in_dtype!r}")
+
+
+# bf16: 8 significant bits, exponents as float32 (normal numbers from 2^-126,
+# subnormal spacing 2^-133), largest finite (2 - 2^-7) 2^127.
+_BF16_MIN_QUANTUM = 2.0 ** -133
+_BF16_OVERFLOW = (2.0 - 2.0 ** -8) * 2.0 ** 127  # halfway to 2^128: from here on, inf
+
+
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """Round float64 values (each exactly a float32 value) to the nearest bf16
+    value, ties to the even significand; results as float64.
+
+    The spacing of bf16 numbers in [2^e, 2^(e+1)) is 2^(e-7), and 2^-133 below
+    2^-126.  Dividing by that spacing is exact (a power of two), ``rint``
+    rounds half to even, and multiplying back is exact.  Magnitudes at or
+    beyond the midpoint between the largest finite bf16 and 2^128 become
+    infinite (the tie rounds to the even significand, which is the overflow).
+    NaN stays NaN and infinities stay infinite.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    out = v.copy()
+    fin = np.isfinite(v) & (v != 0.0)
+    a = np.abs(v[fin])
+    _, e = np.frexp(a)              # a = m 2^e with m in [0.5, 1): a in [2^(e-1), 2^e)
+    q = np.maximum(np.ldexp(1.0, e - 1 - 7), _BF16_MIN_QUANTUM)
+    r = np.rint(a / q) * q
+    r[a >= _BF16_OVERFLOW] = np.inf
+    out[fin] = np.copysign(r, v[fin])
+    return out
+
+
+def staged_values(X: np.ndarray, in_dtype: str, staging: str | None) -> np.ndarray:
+    """The float64 values a batch contributes once put into the staging type.
+
+    ``staging`` is ``None`` (the stored type), ``"f32"`` (fp16, bf16 and
+    float32 values are all float32 values: unchanged) or ``"bf16"`` (rounded
+    to nearest even).
+    """
+    Xd = exact_float64(X, in_dtype)
+    if staging is None or staging == "f32" or (staging == "bf16" and in_dtype == "bf16"):
+        return Xd
+    if staging == "bf16":
+        return round_to_bf16(Xd)
+    raise ValueError(f"unknown staging dtype {staging!r}")
 
 
 class GramAccumulator:
@@ -97,17 +154,20 @@ class GramAccumulator:
 
     ``add_batch`` takes one calibration batch, tokens x features; an empty
     batch changes nothing (GPTQModel PR 2981, Validation: empty batches).
+    ``staging`` (``None``, ``"f32"`` or ``"bf16"``) is the type every batch is
+    put into before its products are formed.
     """
 
-    def __init__(self, d: int):
+    def __init__(self, d: int, staging: str | None = None):
         if d < 1:
             raise ValueError("d must be positive")
         self.d = int(d)
+        self.staging = staging
         self.S = np.zeros((self.d, self.d), dtype=np.float64)
         self.N = 0
 
     def add_batch(self, X: np.ndarray, in_dtype: str) -> None:
-        Xd = exact_float64(X, in_dtype)
+        Xd = staged_values(X, in_dtype, self.staging)
         if Xd.ndim != 2 or Xd.shape[1] != self.d:
             raise ValueError(f"batch must be (tokens, {self.d})")
         n = Xd.shape[0]

@@ -92,6 +92,68 @@ def pin_worked_example(O):
     assert H[0, 0] == g["expected_diag_bf16_input"]
 
 
+def pin_worked_example_f16_staging(O):
+    """The same example with fp16 activations and the staging type chosen per accumulator."""
+    g = _load("worked_example_staging.json")
+    f = g["f16_staging"]
+    x = np.asarray(g["tokens"], dtype=np.float16)
+    assert float(x[0, 0]) == g["tokens"][0][0]  # exact in fp16
+    for staging, want in (("f32", f["expected_diag_f32_staging"]), (None, f["expected_diag_f32_staging"]),
+                          ("bf16", f["expected_diag_bf16_staging"])):
+        acc = O.GramAccumulator(1, staging=staging)
+        acc.add_batch(x, "f16")
+        H, _, _ = acc.materialize(0.0, neutralize=False)
+        assert H[0, 0] == want, (staging, H[0, 0])
+
+
+def _bf16_by_bits(x32: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even float32 -> bf16 by integer arithmetic on the bit
+    patterns (drop the low 16 bits, round half to even; NaN kept NaN), a
+    second derivation independent of the oracle's."""
+    u = x32.view(np.uint32).astype(np.uint64)
+    low = u & 0xFFFF
+    hi = u >> 16
+    up = (low > 0x8000) | ((low == 0x8000) & ((hi & 1) == 1))
+    hi = hi + up.astype(np.uint64)
+    out = (hi << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    out[np.isnan(x32)] = np.nan
+    return out
+
+
+def pin_bf16_rounding(O, seed=11):
+    """Rounding to bf16 agrees with torch's CPU conversion and with an integer derivation on
+    random bit patterns (all exponents, subnormals, ties, overflow), and with hand values."""
+    import torch
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 2 ** 16, size=20_000, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    near_max = np.uint32(0x7F7F0000) + rng.integers(0, 2 ** 16, size=2_000, dtype=np.uint64).astype(np.uint32)
+    x32 = np.concatenate([bits, ties, near_max, np.array([0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 0x00008000,
+                                                           0x00018000, 0x80000000], dtype=np.uint32)]).view(np.float32)
+    got = O.round_to_bf16(x32.astype(np.float64))
+    ref_t = torch.from_numpy(x32.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    ref_b = _bf16_by_bits(x32)
+    for ref in (ref_t, ref_b):
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], ref[~nan])
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # hand values: ties go to the even significand; fp16's largest value rounds up to 2^16
+    hand = {1 + 2.0 ** -8: 1.0, 1 + 3 * 2.0 ** -8: 1 + 2.0 ** -6, 1 + 2.0 ** -7: 1 + 2.0 ** -7,
+            65504.0: 65536.0, -(1 + 2.0 ** -10): -1.0, 2.0 ** -134: 0.0}
+    for v, want in hand.items():
+        assert O.round_to_bf16(np.array([v]))[0] == want, (v, want)
+    # staged values of every fp16 bit pattern: fp32 staging keeps them, bf16 staging rounds them
+    h = np.arange(2 ** 16, dtype=np.uint32).astype(np.uint16).view(np.float16).reshape(1, -1)
+    f32 = O.staged_values(h, "f16", "f32")
+    exact = h.astype(np.float32)
+    fin = np.isfinite(exact)
+    assert np.array_equal(f32[fin], exact[fin].astype(np.float64))
+    b = O.staged_values(h, "f16", "bf16")
+    rb = torch.from_numpy(exact.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(b[fin], rb[fin])
+
+
 def pin_neutralize_damp_hand(O):
     g = _load("neutralize_damp_hand.json")
     X = np.asarray(g["X"], dtype=np.float32)
@@ -288,6 +350,8 @@ ALL_PINS = [
     pin_bruteforce_fraction,
     pin_orientation_hand,
     pin_worked_example,
+    pin_worked_example_f16_staging,
+    pin_bf16_rounding,
     pin_neutralize_damp_hand,
     pin_multi_batch_is_concatenation,
     pin_empty_batch_noop,

@@ -36,6 +36,8 @@ def _ns(**over):
         exact_float64=HO.exact_float64,
         gram_entries=HO.gram_entries,
         column_sum_squares=HO.column_sum_squares,
+        round_to_bf16=HO.round_to_bf16,
+        staged_values=HO.staged_values,
     )
     base.update(over)
     return types.SimpleNamespace(**base)
@@ -182,7 +184,65 @@ def _imx_shifted(batches, in_dtype):
     return np.roll(HO.column_sum_squares(batches, in_dtype), 1)  # mistake: column index off by one
 
 
+def _round_truncates(v):
+    v = np.asarray(v, dtype=np.float64)
+    x32 = v.astype(np.float32)
+    return ((x32.view(np.uint32) >> 16) << 16).view(np.float32).astype(np.float64)  # mistake: rounds toward zero
+
+
+def _round_half_away(v):
+    v = np.asarray(v, dtype=np.float64)
+    out = v.copy()
+    fin = np.isfinite(v) & (v != 0)
+    a = np.abs(v[fin])
+    _, e = np.frexp(a)
+    q = np.maximum(np.ldexp(1.0, e - 8), 2.0 ** -133)
+    out[fin] = np.copysign(np.floor(a / q + 0.5) * q, v[fin])  # mistake: ties away from zero
+    return out
+
+
+def _round_keeps_8_fraction_bits(v):
+    v = np.asarray(v, dtype=np.float64)
+    out = v.copy()
+    fin = np.isfinite(v) & (v != 0)
+    a = np.abs(v[fin])
+    _, e = np.frexp(a)
+    q = np.ldexp(1.0, e - 9)  # mistake: one bit too many
+    out[fin] = np.copysign(np.rint(a / q) * q, v[fin])
+    return out
+
+
+def _staging_mutant(rounder):
+    def staged(X, in_dtype, staging):
+        Xd = HO.exact_float64(X, in_dtype)
+        return rounder(Xd) if staging == "bf16" else Xd
+
+    class Acc(HO.GramAccumulator):
+        def add_batch(self, X, in_dtype):
+            Xd = staged(X, in_dtype, self.staging)
+            if Xd.shape[0] == 0:
+                return
+            self.S += Xd.T @ Xd
+            self.N += Xd.shape[0]
+    return dict(GramAccumulator=Acc, round_to_bf16=rounder, staged_values=staged)
+
+
+def _staging_ignored():
+    class Acc(HO.GramAccumulator):
+        def add_batch(self, X, in_dtype):
+            Xd = HO.exact_float64(X, in_dtype)  # mistake: never rounds to the staging type
+            if Xd.shape[0] == 0:
+                return
+            self.S += Xd.T @ Xd
+            self.N += Xd.shape[0]
+    return dict(GramAccumulator=Acc, staged_values=lambda X, t, s: HO.exact_float64(X, t))
+
+
 MUTANTS = {
+    "bf16_round_truncates": _ns(**_staging_mutant(_round_truncates)),
+    "bf16_round_half_away": _ns(**_staging_mutant(_round_half_away)),
+    "bf16_round_9_bits": _ns(**_staging_mutant(_round_keeps_8_fraction_bits)),
+    "staging_ignored": _ns(**_staging_ignored()),
     "imatrix_not_squared": _ns(column_sum_squares=_imx_not_squared),
     "imatrix_skips_last_row": _ns(column_sum_squares=_imx_skips_last_row),
     "imatrix_shifted": _ns(column_sum_squares=_imx_shifted),
