@@ -41,6 +41,7 @@ _HEADER = os.path.join(os.path.dirname(_PKG), "include", "hess.h")
 
 HESS_BF16 = 0
 HESS_F32 = 1
+HESS_F16 = 2
 HESS_NO_NEUTRALIZE = 1
 
 _STATUS = {0: "HESS_OK", -1: "HESS_EINVAL", -2: "HESS_ENOMEM", -3: "HESS_EHIP", -4: "HESS_ESTATE",
@@ -80,6 +81,7 @@ def _load():
         "hess_create_ex": (vp, [i64, c_int, i64]),
         "hess_destroy": (c_int, [vp]),
         "hess_add_batch": (c_int, [vp, vp, i64, i64, vp]),
+        "hess_add_batch_cast": (c_int, [vp, vp, c_int, i64, i64, vp]),
         "hess_materialize": (c_int, [vp, ctypes.c_float, vp]),
         "hess_materialize_ex": (c_int, [vp, ctypes.c_float, ctypes.c_uint, vp, vp, vp, vp]),
         "hess_reset": (c_int, [vp, vp]),
@@ -137,6 +139,12 @@ def _dtype_code(dtype) -> int:
     raise TypeError(f"unsupported activation dtype {dtype}; use torch.bfloat16 or torch.float32")
 
 
+def _act_code(dtype) -> int:
+    if dtype == torch.float16:
+        return HESS_F16
+    return _dtype_code(dtype)
+
+
 def _as_rows(x: torch.Tensor, d: int):
     """(tokens, d) view of x with unit feature stride; returns (tensor, n, ld)."""
     if x.shape[-1] != d:
@@ -166,10 +174,13 @@ def set_tile_override(edge: int) -> None:
 class Hessian:
     """One calibration-Hessian accumulator of width ``d`` on the current GPU.
 
-    ``dtype`` is the activation element type every batch will have
-    (``torch.bfloat16`` or ``torch.float32``); the Hessian is always float32.
-    ``staging_bytes`` sizes the buffer that collects short batches (default:
-    512 MiB for bf16 at d >= 1024, else 64 MiB; 0 disables staging).
+    ``dtype`` is the staging dtype (``torch.bfloat16`` or ``torch.float32``):
+    the type the products are formed in.  Batches of that type are read as
+    they are; float16, bfloat16 or float32 batches of another type are
+    converted on their way into the staging buffer (rounded to nearest even
+    when narrowing).  The Hessian is always float32.  ``staging_bytes`` sizes
+    the buffer that collects short batches (default: 512 MiB for bf16 at
+    d >= 1024, else 64 MiB; 0 disables staging and conversion).
     """
 
     def __init__(self, d: int, dtype=torch.bfloat16, staging_bytes: int | None = None):
@@ -191,11 +202,13 @@ class Hessian:
         """S += X^T X, N += tokens; leading dimensions of x are flattened to tokens."""
         if not x.is_cuda:
             raise ValueError("activations must be on the GPU")
-        if x.dtype != self.dtype:
-            raise TypeError(f"activations are {x.dtype}, this Hessian takes {self.dtype}")
+        code = _act_code(x.dtype)
         x2, n, ld = _as_rows(x, self.d)
         ptr = x2.data_ptr() if n > 0 else None
-        _check(_load().hess_add_batch(self._h, ptr, n, ld, _stream(stream)))
+        if code == self._code:
+            _check(_load().hess_add_batch(self._h, ptr, n, ld, _stream(stream)))
+        else:
+            _check(_load().hess_add_batch_cast(self._h, ptr, code, n, ld, _stream(stream)))
 
     def materialize(self, damp_percent: float = 0.01, out: torch.Tensor | None = None, neutralize: bool = True,
                     stream=None):

@@ -595,7 +595,7 @@ hess_t hess_create_ex(int64_t d, int in_dtype, int64_t staging_bytes) {
     return nullptr;
   }
   if (in_dtype != HESS_BF16 && in_dtype != HESS_F32) {
-    fail(HESS_EINVAL, "unknown input dtype %d", in_dtype);
+    fail(HESS_EINVAL, "staging dtype %d is not HESS_BF16 or HESS_F32", in_dtype);
     return nullptr;
   }
   if (staging_bytes < 0 || staging_bytes > ((int64_t)16 << 30)) {
@@ -732,6 +732,47 @@ int hess_add_batch(hess_t h, const void* X, int64_t n_tokens, int64_t ld, hess_s
   return HESS_OK;
 }
 
+int hess_add_batch_cast(hess_t h, const void* X, int x_dtype, int64_t n_tokens, int64_t ld, hess_stream_t stream) {
+  if (!h) return fail(HESS_EINVAL, "null handle");
+  if (x_dtype != HESS_BF16 && x_dtype != HESS_F32 && x_dtype != HESS_F16)
+    return fail(HESS_EINVAL, "unknown activation dtype %d", x_dtype);
+  if (x_dtype == h->dtype) return hess_add_batch(h, X, n_tokens, ld, stream);
+  if (h->consumed) return fail(HESS_ESTATE, "handle was materialized in place; hess_reset it first");
+  if (n_tokens < 0) return fail(HESS_EINVAL, "n_tokens = %lld < 0", (long long)n_tokens);
+  if (ld < h->d) return fail(HESS_EINVAL, "ld = %lld < d = %lld", (long long)ld, (long long)h->d);
+  if (n_tokens == 0) return HESS_OK;
+  if (!X) return fail(HESS_EINVAL, "X is NULL with n_tokens > 0");
+  const int xes = x_dtype == HESS_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(X) % xes != 0) return fail(HESS_EALIGN, "X not element-aligned");
+  if (!h->stage) return fail(HESS_EINVAL, "converting activations needs the handle's staging buffer (staging_bytes > 0)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = order_stream(h, s);
+  if (rc != HESS_OK) return rc;
+  // the rows go through the staging buffer, converted on the copy, in pieces
+  // that fit; a full buffer is folded into S first (8-row blocks in the
+  // transposed layout keep the buffer's fill a multiple of 8)
+  const int64_t unit = h->stage_t8 ? 8 : 1;
+  for (int64_t off = 0; off < n_tokens;) {
+    if (h->stage_cap - h->stage_n < unit) {
+      rc = flush_stage(h, s);
+      if (rc != HESS_OK) return rc;
+    }
+    const int64_t space = h->stage_cap - h->stage_n;
+    int64_t take = n_tokens - off < space ? n_tokens - off : space;
+    if (take < n_tokens - off) take = take / unit * unit;
+    const int64_t rows = (take + unit - 1) / unit * unit;
+    char* dst = static_cast<char*>(h->stage) + h->stage_n * h->stage_ld * esize(h->dtype);
+    hipError_t e = launch_cast_rows(static_cast<const char*>(X) + off * ld * xes, x_dtype, ld, take, h->d, dst,
+                                    h->dtype, h->stage_ld, h->stage_t8, s);
+    if (e != hipSuccess) return hip_fail(e, "converting staging copy launch");
+    h->stage_n += rows;
+    h->stage_real += take;
+    off += take;
+  }
+  h->N += n_tokens;
+  return HESS_OK;
+}
+
 int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld, const int32_t* row_idx,
                            const int64_t* offsets, hess_stream_t stream) {
   if (!hs || n_groups < 1) return fail(HESS_EINVAL, "need at least one handle");
@@ -860,6 +901,11 @@ int hess_adopt(hess_t dst, hess_t src, hess_stream_t stream) {
   if (!dst || !src) return fail(HESS_EINVAL, "null handle");
   if (dst == src) return HESS_OK;
   if (dst->d != src->d) return fail(HESS_EINVAL, "width mismatch: %lld vs %lld", (long long)dst->d, (long long)src->d);
+  // the staging type and the staging buffer (the chunking of the sum) decide
+  // what the sum holds and its rounding order: only equal settings share
+  if (dst->dtype != src->dtype || dst->stage_cap != src->stage_cap || dst->stage_t8 != src->stage_t8)
+    return fail(HESS_EINVAL, "accumulation settings differ (staging dtype %d vs %d, staging rows %lld vs %lld)",
+                dst->dtype, src->dtype, (long long)dst->stage_cap, (long long)src->stage_cap);
   if (src->consumed) return fail(HESS_ESTATE, "source was materialized in place; hess_reset it first");
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = order_stream(src, s);

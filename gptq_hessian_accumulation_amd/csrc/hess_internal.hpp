@@ -142,6 +142,14 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 // bytes), blocks of d chunks; rows n .. round_up(n, 8) - 1 are written as zeros.
 hipError_t launch_copy_rows_t8(const void* X, int64_t ld, int64_t n, int64_t d, void* dst, hipStream_t stream);
 
+// Converting staging copy: n rows of X (element type x_dtype: 0 bf16, 1
+// float32, 2 fp16; row stride ld elements) into dst of type dst_dtype (0
+// bf16, 1 float32), either row-major with row stride dld or (t8, bf16 only)
+// in the transposed 8-token layout of launch_copy_rows_t8.  Narrowing rounds
+// to nearest even; widening is exact.  Same-type pairs are not handled here.
+hipError_t launch_cast_rows(const void* X, int x_dtype, int64_t ld, int64_t n, int64_t d, void* dst, int dst_dtype,
+                            int64_t dld, bool t8, hipStream_t stream);
+
 // Copy n rows of d elements (esize bytes each) from X (row stride ld) to dst (row stride dld).
 hipError_t launch_copy_rows(const void* X, int64_t ld, int esize, int64_t n, int64_t d, void* dst, int64_t dld,
                             hipStream_t stream);

@@ -16,6 +16,13 @@
 // consecutive tokens of one feature (the k-run of one matrix-core operand
 // lane), with every batch padded by zero rows to a multiple of 8 tokens.
 // Zero rows add nothing to the Gram sum.
+//
+// Activations of another type than the handle's staging type are converted
+// by the copy: fp16 and bf16 widen exactly to float32, float32 and fp16 are
+// rounded to the nearest bf16 (ties to even).  This is the staging dtype of
+// GPTQModel PR 3052 ("Shared-input Hessian dedup", review finding P2) and
+// Model-Optimizer's hessian_input_dtype (PR 3002 page, "What does this PR
+// do?").
 
 #include "hess_device.hpp"
 #include "hess_internal.hpp"
@@ -59,15 +66,55 @@ __global__ void __launch_bounds__(256) copy_rows_elem(const E* X, int64_t ld, E*
   }
 }
 
+// Element types of the rows a staging copy reads (the public dtype codes).
+constexpr int kSrcBF16 = 0, kSrcF32 = 1, kSrcF16 = 2;
+
+// Exact widening of one stored element to float32.
+template <int SRC>
+__device__ __forceinline__ float load_f32(const void* X, int64_t i) {
+  if constexpr (SRC == kSrcF32) return static_cast<const float*>(X)[i];
+  else if constexpr (SRC == kSrcF16) return (float)static_cast<const _Float16*>(X)[i];
+  else return bf16_bits_to_f32(static_cast<const uint16_t*>(X)[i]);
+}
+
+// Eight consecutive elements at p (16-byte aligned) as eight bf16 values in
+// four dwords (element 2k in the low half of dword k), rounded to nearest even.
+template <int SRC>
+__device__ __forceinline__ u32x4 load8_bf16(const char* p) {
+  if constexpr (SRC == kSrcBF16) {
+    return *reinterpret_cast<const u32x4*>(p);
+  } else if constexpr (SRC == kSrcF32) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p), b = *reinterpret_cast<const u32x4*>(p + 16);
+    u32x4 o;
+    o[0] = f32_to_bf16_bits(__uint_as_float(a[0])) | (f32_to_bf16_bits(__uint_as_float(a[1])) << 16);
+    o[1] = f32_to_bf16_bits(__uint_as_float(a[2])) | (f32_to_bf16_bits(__uint_as_float(a[3])) << 16);
+    o[2] = f32_to_bf16_bits(__uint_as_float(b[0])) | (f32_to_bf16_bits(__uint_as_float(b[1])) << 16);
+    o[3] = f32_to_bf16_bits(__uint_as_float(b[2])) | (f32_to_bf16_bits(__uint_as_float(b[3])) << 16);
+    return o;
+  } else {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(a[k] & 0xFFFFu));
+      const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(a[k] >> 16));
+      o[k] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    }
+    return o;
+  }
+}
+
 // Transposed staging copy, 16-byte aligned rows: workgroup (g, F) moves
 // tokens 8g..8g+7 (zeros past n) of features F .. F + kCQ * 256 - 1.  Its
 // 256 threads read the 8 rows' pieces into LDS with 16-byte loads (all
 // quarters' loads in flight at once), then thread t gathers each quarter's
 // feature F + 256 k + t over the 8 tokens and writes them as one chunk, so
 // that both the reads and the writes are contiguous across the workgroup.
+// Rows of fp16 or float32 are rounded to bf16 on the way.
 constexpr int kCQ = 2;
-__global__ void __launch_bounds__(256) copy_rows_t8(const char* X, int64_t ld_bytes, char* dst, int64_t n, int d,
-                                                    int nq) {
+template <int SRC>
+__device__ __forceinline__ void t8_body(const char* X, int64_t ld_bytes, char* dst, int64_t n, int d, int nq) {
+  constexpr int xes = SRC == kSrcF32 ? 4 : 2;
   __shared__ __attribute__((aligned(16))) uint16_t tile[kCQ][8][256];
   const int t = threadIdx.x;
   const int64_t g = blockIdx.x / nq;
@@ -79,8 +126,7 @@ __global__ void __launch_bounds__(256) copy_rows_t8(const char* X, int64_t ld_by
 #pragma unroll
     for (int k = 0; k < kCQ; ++k) {
       const int f = F + k * 256 + 8 * q;
-      v[k] = (tok < n && f < d) ? *reinterpret_cast<const u32x4*>(X + tok * ld_bytes + (int64_t)f * 2)
-                                : u32x4{0u, 0u, 0u, 0u};
+      v[k] = (tok < n && f < d) ? load8_bf16<SRC>(X + tok * ld_bytes + (int64_t)f * xes) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int k = 0; k < kCQ; ++k) *reinterpret_cast<u32x4*>(&tile[k][r][8 * q]) = v[k];
@@ -98,12 +144,66 @@ __global__ void __launch_bounds__(256) copy_rows_t8(const char* X, int64_t ld_by
   }
 }
 
+__global__ void __launch_bounds__(256) copy_rows_t8(const char* X, int64_t ld_bytes, char* dst, int64_t n, int d,
+                                                    int nq) {
+  t8_body<kSrcBF16>(X, ld_bytes, dst, n, d, nq);
+}
+
+template <int SRC>
+__global__ void __launch_bounds__(256) cast_rows_t8(const char* X, int64_t ld_bytes, char* dst, int64_t n, int d,
+                                                    int nq) {
+  t8_body<SRC>(X, ld_bytes, dst, n, d, nq);
+}
+
 // Transposed staging copy, any alignment: one element per thread.
 __global__ void __launch_bounds__(256) copy_rows_t8_elem(const uint16_t* X, int64_t ld, uint16_t* dst, int64_t n,
                                                          int64_t d, int64_t total) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i / d, f = i - t * d;
     dst[((t >> 3) * d + f) * 8 + (t & 7)] = t < n ? X[t * ld + f] : (uint16_t)0;
+  }
+}
+
+template <int SRC>
+__global__ void __launch_bounds__(256) cast_rows_t8_elem(const void* X, int64_t ld, uint16_t* dst, int64_t n,
+                                                         int64_t d, int64_t total) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / d, f = i - t * d;
+    dst[((t >> 3) * d + f) * 8 + (t & 7)] = t < n ? (uint16_t)f32_to_bf16_bits(load_f32<SRC>(X, t * ld + f)) : 0;
+  }
+}
+
+// Row-major converting copy into a bf16 (DST = 0) or float32 (DST = 1)
+// staging buffer.  vec: eight elements per thread (d % 8 == 0, rows and
+// destination 16-byte aligned); otherwise one element per thread.
+template <int SRC, int DST, bool VEC>
+__global__ void __launch_bounds__(256) cast_rows(const void* X, int64_t ld, void* dst, int64_t dld, int64_t n,
+                                                 int64_t d) {
+  constexpr int xes = SRC == kSrcF32 ? 4 : 2;
+  const int64_t per_row = VEC ? d / 8 : d;
+  const int64_t total = n * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / per_row, c = i - r * per_row;
+    if constexpr (VEC) {
+      if constexpr (DST == 0) {
+        const char* p = static_cast<const char*>(X) + (r * ld + 8 * c) * xes;
+        *reinterpret_cast<u32x4*>(static_cast<char*>(dst) + (r * dld + 8 * c) * 2) = load8_bf16<SRC>(p);
+      } else {
+        float* o = static_cast<float*>(dst) + r * dld + 8 * c;
+        f32x4 a, b;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          a[k] = load_f32<SRC>(X, r * ld + 8 * c + k);
+          b[k] = load_f32<SRC>(X, r * ld + 8 * c + 4 + k);
+        }
+        *reinterpret_cast<f32x4*>(o) = a;
+        *reinterpret_cast<f32x4*>(o + 4) = b;
+      }
+    } else {
+      const float v = load_f32<SRC>(X, r * ld + c);
+      if constexpr (DST == 0) static_cast<uint16_t*>(dst)[r * dld + c] = (uint16_t)f32_to_bf16_bits(v);
+      else static_cast<float*>(dst)[r * dld + c] = v;
+    }
   }
 }
 
@@ -189,6 +289,69 @@ hipError_t launch_copy_rows_t8(const void* X, int64_t ld, int64_t n, int64_t d, 
                        static_cast<const uint16_t*>(X), ld, static_cast<uint16_t*>(dst), n, d, elems);
   }
   return hipGetLastError();
+}
+
+namespace {
+
+int grid_for(int64_t items) {
+  int64_t blocks = (items + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  return (int)(blocks > 0 ? blocks : 1);
+}
+
+template <int SRC>
+hipError_t cast_t8(const void* X, int64_t ld, int64_t n, int64_t d, void* dst, hipStream_t stream) {
+  constexpr int xes = SRC == kSrcF32 ? 4 : 2;
+  const int64_t blocks8 = (n + 7) / 8;
+  const bool vec = (reinterpret_cast<uintptr_t>(X) & 15u) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0 &&
+                   ((ld * xes) & 15) == 0;
+  const int64_t nq = (d + kCQ * 256 - 1) / (kCQ * 256);
+  const int64_t wgs = blocks8 * nq;
+  if (vec && wgs < ((int64_t)1 << 31)) {
+    hipLaunchKernelGGL(cast_rows_t8<SRC>, dim3((unsigned)wgs), dim3(256), 0, stream, static_cast<const char*>(X),
+                       ld * xes, static_cast<char*>(dst), n, (int)d, (int)nq);
+  } else {
+    const int64_t elems = blocks8 * 8 * d;
+    hipLaunchKernelGGL(cast_rows_t8_elem<SRC>, dim3(grid_for(elems)), dim3(256), 0, stream, X, ld,
+                       static_cast<uint16_t*>(dst), n, d, elems);
+  }
+  return hipGetLastError();
+}
+
+template <int SRC, int DST>
+hipError_t cast_rm(const void* X, int64_t ld, int64_t n, int64_t d, void* dst, int64_t dld, hipStream_t stream) {
+  constexpr int xes = SRC == kSrcF32 ? 4 : 2;
+  constexpr int des = DST == 0 ? 2 : 4;
+  const bool vec = d % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(dst) & 15u) == 0 && ((ld * xes) & 15) == 0 && ((dld * des) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL((cast_rows<SRC, DST, true>), dim3(grid_for(n * (d / 8))), dim3(256), 0, stream, X, ld, dst,
+                       dld, n, d);
+  else
+    hipLaunchKernelGGL((cast_rows<SRC, DST, false>), dim3(grid_for(n * d)), dim3(256), 0, stream, X, ld, dst, dld,
+                       n, d);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cast_rows(const void* X, int x_dtype, int64_t ld, int64_t n, int64_t d, void* dst, int dst_dtype,
+                            int64_t dld, bool t8, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (t8) {
+    if (dst_dtype != kSrcBF16 || d % 8 != 0) return hipErrorInvalidValue;
+    if (x_dtype == kSrcF32) return cast_t8<kSrcF32>(X, ld, n, d, dst, stream);
+    if (x_dtype == kSrcF16) return cast_t8<kSrcF16>(X, ld, n, d, dst, stream);
+    return hipErrorInvalidValue;
+  }
+  if (dst_dtype == kSrcBF16) {
+    if (x_dtype == kSrcF32) return cast_rm<kSrcF32, 0>(X, ld, n, d, dst, dld, stream);
+    if (x_dtype == kSrcF16) return cast_rm<kSrcF16, 0>(X, ld, n, d, dst, dld, stream);
+  } else if (dst_dtype == kSrcF32) {
+    if (x_dtype == kSrcBF16) return cast_rm<kSrcBF16, 1>(X, ld, n, d, dst, dld, stream);
+    if (x_dtype == kSrcF16) return cast_rm<kSrcF16, 1>(X, ld, n, d, dst, dld, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_copy_rows(const void* X, int64_t ld, int esize, int64_t n, int64_t d, void* dst, int64_t dld,

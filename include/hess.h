@@ -46,10 +46,12 @@ typedef struct hess_s* hess_t;
 typedef struct hess_imx_s* hess_imx_t;
 typedef void* hess_stream_t; /* a hipStream_t */
 
-/* Input element types.  bf16 products are exact in float32 and summed in
- * float32 (Model-Optimizer PR 3002 page, "What does this PR do?": bfloat16
- * in, float32 out).  float32 inputs are multiplied to float32 accuracy. */
-enum hess_dtype { HESS_BF16 = 0, HESS_F32 = 1 };
+/* Element types.  A handle's staging dtype (HESS_BF16 or HESS_F32) is the
+ * type its products are formed in: bf16 products are exact in float32 and
+ * summed in float32 (Model-Optimizer PR 3002 page, "What does this PR do?":
+ * bfloat16 in, float32 out); float32 inputs are multiplied to float32
+ * accuracy.  Activations may also be HESS_F16 (hess_add_batch_cast only). */
+enum hess_dtype { HESS_BF16 = 0, HESS_F32 = 1, HESS_F16 = 2 };
 
 enum hess_status {
   HESS_OK = 0,
@@ -85,8 +87,11 @@ const char* hess_last_error(void);
  * 256 KiB, ntiles = nb (nb + 1) / 2 with nb = ceil(d / 256) (162 MiB at
  * d = 4096); that buffer lives until the process ends.  N = 0.
  *   d         number of input features (Hessian width), 1 <= d <= 65536.
- *   in_dtype  HESS_BF16 or HESS_F32: the element type of every X later given
- *             to hess_add_batch (Model-Optimizer PR 3002, hessian_input_dtype).
+ *   in_dtype  HESS_BF16 or HESS_F32: the staging dtype, i.e. the element
+ *             type of every X given to hess_add_batch and the type that
+ *             hess_add_batch_cast converts other activations to
+ *             (Model-Optimizer PR 3002, hessian_input_dtype; GPTQModel PR
+ *             3052, the staging_dtype accumulation setting).
  * Returns NULL on error (EINVAL / ENOMEM / EHIP; see hess_last_error()).
  * The handle owns its device memory until hess_destroy().
  */
@@ -126,8 +131,11 @@ int hess_destroy(hess_t h);
  * > Phase 2 (looper Hessian dedup): adopt_hessian_from copies H and nsamples
  * and clears the follower's partials; updating one afterwards leaves the
  * other unchanged).
- * dst == src is a no-op.  EINVAL: null handle or different d (the pages'
- * column mismatch); ESTATE: src was materialized in place.  Enqueued on
+ * dst == src is a no-op.  EINVAL: null handle, different d (the pages'
+ * column mismatch) or different accumulation settings: staging dtype or
+ * staging buffer (its rows and layout fix how the sum is chunked), which the
+ * same page's review (finding P2 and its fix) requires to match before a
+ * Hessian is shared.  ESTATE: src was materialized in place.  Enqueued on
  * stream (both handles are ordered onto it).  Never allocates.
  */
 int hess_adopt(hess_t dst, hess_t src, hess_stream_t stream);
@@ -152,6 +160,27 @@ int hess_adopt(hess_t dst, hess_t src, hess_stream_t stream);
  * nothing is enqueued and N is unchanged.
  */
 int hess_add_batch(hess_t h, const void* X, int64_t n_tokens, int64_t ld, hess_stream_t stream);
+
+/*
+ * hess_add_batch_cast -- hess_add_batch for activations of any element type:
+ * X is first put into the handle's staging dtype, then accumulated.
+ *
+ * fp16 and bf16 widen exactly to float32; float32 and fp16 round to the
+ * nearest bf16, ties to even.  The staging dtype therefore decides the
+ * result: one fp16 token of value 1 + 2^-10 gives a scaled diagonal of
+ * 2 + 2^-8 + 2^-19 with float32 staging and exactly 2 with bf16 staging
+ * (GPTQModel PR 3052, "Shared-input Hessian dedup", review finding P2;
+ * Model-Optimizer PR 3002 page, "What does this PR do?": the bfloat16
+ * hessian_input_dtype against the float32 default).
+ *   x_dtype   HESS_F16, HESS_BF16 or HESS_F32.  Equal to the staging dtype:
+ *             exactly hess_add_batch.  Otherwise the rows pass through the
+ *             staging buffer, converted on the copy, in pieces that fit (a
+ *             full buffer is folded into S first), so the handle needs a
+ *             staging buffer (EINVAL with staging_bytes 0).
+ *   other arguments and errors as hess_add_batch; X aligned to x_dtype's size.
+ * Never allocates.
+ */
+int hess_add_batch_cast(hess_t h, const void* X, int x_dtype, int64_t n_tokens, int64_t ld, hess_stream_t stream);
 
 /*
  * hess_materialize -- H_out = neutralize_dead(S * 2/N) + damp * I, where

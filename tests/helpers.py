@@ -17,11 +17,13 @@ TOL = {W.BF16: 5e-5, W.F32: 1e-5}
 def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     if dtype == W.BF16:
         return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == W.F16:
+        return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float16)).to(device)
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
 
 
 def torch_dtype(dtype: str):
-    return torch.bfloat16 if dtype == W.BF16 else torch.float32
+    return {W.BF16: torch.bfloat16, W.F32: torch.float32, W.F16: torch.float16}[dtype]
 
 
 def agreement(H: np.ndarray, H_ref: np.ndarray) -> float:

@@ -726,3 +726,141 @@ def test_adopt_is_private_copy():
         follower.adopt_from(leader)
     for h in (leader, follower, other):
         h.close()
+
+
+# ------------------------------------------------- staging dtype (casts) --
+
+def test_cast_worked_example_bitwise():
+    """The pages' fp16 example: one token 1 + 2^-10 gives a scaled diagonal of
+    2.003908157348633 staged in float32 and exactly 2.0 staged in bf16."""
+    _say("cast worked example")
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example_staging.json")))
+    f = g["f16_staging"]
+    x = torch.tensor(g["tokens"], dtype=torch.float16, device="cuda")
+    for staging, want in ((torch.float32, f["expected_diag_f32_staging"]),
+                          (torch.bfloat16, f["expected_diag_bf16_staging"])):
+        for d in (1, 1024):   # row-major staging; transposed bf16 staging at d = 1,024 under the 256 override
+            hs.set_tile_override(256 if d == 1024 else 0)
+            h = hs.Hessian(d, staging)
+            xx = torch.zeros((1, d), dtype=torch.float16, device="cuda")
+            xx[0, 0] = x[0, 0]
+            h.add_batch(xx)
+            H, _, _ = h.materialize(0.0, neutralize=False)
+            assert float(H[0, 0].cpu()) == want, (staging, d, float(H[0, 0].cpu()))
+            h.close()
+
+
+def _diag_batch(vals: np.ndarray, dtype: str) -> np.ndarray:
+    """Tokens t < len(vals): token t holds vals[t] at feature t, zeros elsewhere."""
+    n = vals.shape[0]
+    X = np.zeros((n, n), dtype=vals.dtype)
+    X[np.arange(n), np.arange(n)] = vals
+    return X
+
+
+@pytest.mark.parametrize("staging,src,t8", [(W.BF16, W.F16, False), (W.BF16, W.F16, True),
+                                             (W.BF16, W.F32, False), (W.BF16, W.F32, True),
+                                             (W.F32, W.F16, False), (W.F32, W.BF16, False)])
+def test_cast_rounding_bit_exact(staging, src, t8):
+    """The conversion itself, value by value: a batch of one-hot tokens puts each converted value's
+    square, a single exact product, on the diagonal of S.  f16 sources: every finite fp16 value;
+    f32 sources: random bit patterns with exponents in [-60, 60], ties, and values that round up
+    into the next binade."""
+    _say(f"cast rounding staging={staging} src={src} t8={t8}")
+    d = 2048
+    if src == W.F16:
+        allv = np.arange(2 ** 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+        allv = allv[np.isfinite(allv)]
+    elif src == W.F32:
+        rng = np.random.default_rng(17)
+        m = rng.integers(0, 2 ** 23, size=3 * d, dtype=np.int64)
+        e = rng.integers(127 - 60, 127 + 61, size=3 * d, dtype=np.int64)
+        sg = rng.integers(0, 2, size=3 * d, dtype=np.int64)
+        u = (sg << 31) | (e << 23) | m
+        u[d:2 * d] = (u[d:2 * d] & ~0xFFFF) | 0x8000      # exact ties
+        u[2 * d:2 * d + 256] |= 0x7FFFFF                   # all-ones fraction: rounds into the next binade
+        allv = u.astype(np.uint32).view(np.float32)
+    else:
+        rng = np.random.default_rng(18)
+        allv = W.encode(rng.standard_normal(2 * d).astype(np.float32) * 8, W.BF16)
+    hs.set_tile_override(256 if t8 else 128)
+    h = hs.Hessian(d, torch_dtype(staging))
+    want = np.zeros(d, dtype=np.float64)
+    got = np.zeros(d, dtype=np.float64)
+    for s0 in range(0, allv.shape[0], d):
+        vals = allv[s0:s0 + d]
+        k = vals.shape[0]
+        X = _diag_batch(vals, src)
+        if k < d:
+            X = np.concatenate([X, np.zeros((k, d - k), dtype=X.dtype)], axis=1)
+        h.reset()
+        h.add_batch(to_device(X, src))
+        h.flush()
+        S = h.state_tensor()
+        torch.cuda.synchronize()
+        got = torch.diagonal(S).cpu().numpy().astype(np.float64)[:k]
+        v = O.staged_values(X[np.arange(k), np.arange(k)].reshape(1, -1), src, staging)[0]
+        want = v * v
+        assert np.array_equal(got, want), (s0, np.flatnonzero(got != want)[:8], got[got != want][:4],
+                                           want[got != want][:4])
+    h.close()
+
+
+@pytest.mark.parametrize("staging,src,d,sbytes,override", [
+    (W.BF16, W.F16, 1032, None, 256),        # transposed staging, 256-tile flushes
+    (W.BF16, W.F32, 1032, 2 << 20, 256),     # small buffer: long batches split over many flushes
+    (W.BF16, W.F16, 520, None, 0),           # row-major bf16 staging
+    (W.BF16, W.F32, 17, None, 0),            # odd width: element copies
+    (W.F32, W.F16, 264, None, 0),
+    (W.F32, W.BF16, 100, 1 << 20, 0),        # width not a multiple of 8, small buffer
+])
+def test_cast_parity(staging, src, d, sbytes, override):
+    """Ragged batches (long ones included) of another type than the staging dtype, against the
+    oracle that rounds into the staging dtype first; plain batches mixed in."""
+    _say(f"cast parity staging={staging} src={src} d={d} sbytes={sbytes} override={override}")
+    hs.set_tile_override(override)
+    rng = np.random.default_rng(900 + d)
+    sc = W.column_scales(rng, d)
+    sizes = [5, 700, 3000, 1, 17, 2500, 64]
+    h = hs.Hessian(d, torch_dtype(staging), staging_bytes=sbytes)
+    acc = O.GramAccumulator(d, staging=staging)
+    for i, n in enumerate(sizes):
+        t = staging if i == 3 else src   # one batch already in the staging dtype
+        X = W.encode(W.normal_rows(rng, n, d, sc), t)
+        h.add_batch(to_device(X, t))
+        acc.add_batch(X, t)
+    assert h.nsamples == acc.N == sum(sizes)
+    for damp, neut in ((0.0, False), (0.01, True)):
+        H, dead, dmp = h.materialize(damp, neutralize=neut)
+        Hr, deadr, dmpr = acc.materialize(damp, neut)
+        torch.cuda.synchronize()
+        assert np.array_equal(dead.cpu().numpy(), deadr)
+        err = agreement(H.cpu().numpy(), Hr)
+        assert err <= TOL[staging], err
+    h.close()
+
+
+def test_cast_errors_and_adopt_settings():
+    """Conversion needs a staging buffer; adopt refuses handles whose staging dtype or staging
+    buffer differ (the accumulation settings) and accepts equal ones."""
+    _say("cast errors / adopt settings")
+    x = torch.ones((4, 64), dtype=torch.float16, device="cuda")
+    h0 = hs.Hessian(64, torch.bfloat16, staging_bytes=0)
+    with pytest.raises(hs.HessError):
+        h0.add_batch(x)
+    with pytest.raises(TypeError):
+        h0.add_batch(x.double())
+    a = hs.Hessian(64, torch.bfloat16)
+    b = hs.Hessian(64, torch.float32)
+    c = hs.Hessian(64, torch.bfloat16, staging_bytes=1 << 20)
+    e = hs.Hessian(64, torch.bfloat16)
+    a.add_batch(x)
+    with pytest.raises(hs.HessError):
+        b.adopt_from(a)
+    with pytest.raises(hs.HessError):
+        c.adopt_from(a)
+    e.adopt_from(a)
+    assert e.nsamples == 4
+    for hh in (h0, a, b, c, e):
+        hh.close()

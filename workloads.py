@@ -29,6 +29,7 @@ import numpy as np
 
 BF16 = "bf16"
 F32 = "f32"
+F16 = "f16"
 
 
 # ----------------------------------------------------------------------------
@@ -73,11 +74,13 @@ def normal_rows(rng: np.random.Generator, n: int, d: int, scales=None) -> np.nda
 
 
 def encode(x: np.ndarray, dtype: str) -> np.ndarray:
-    """float32 activations in the requested storage format (bf16 -> uint16 bits)."""
+    """float32 activations in the requested storage format (bf16 -> uint16 bits, f16 -> numpy float16)."""
     if dtype == BF16:
         return to_bf16_bits(x)
     if dtype == F32:
         return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == F16:
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16)
     raise ValueError(dtype)
 
 
