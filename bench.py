@@ -169,8 +169,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--extras", default="all",
-                    help="comma-separated subset of d4096_ragged,d4096_single,moe,local,imatrix (default all; "
-                         "imatrix runs with local)")
+                    help="comma-separated subset of d4096_ragged,d4096_single,moe,local,imatrix,f16_staging "
+                         "(default all; imatrix runs with local)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--print-kernel-sha", action="store_true",
                     help="print the sha256 of the SYRK kernel sources and exit")
@@ -276,8 +276,20 @@ def run_extras(torch, hs, W, args):
     extra = {}
     steps = max(3, args.steps // 2)
     want = set(args.extras.split(",")) if args.extras != "all" else {"d4096_ragged", "d4096_single", "moe", "local",
-                                                                    "imatrix"}
+                                                                    "imatrix", "f16_staging"}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if "f16_staging" in want:
+        # the d=2560 ragged workload with fp16 activations, staged in bf16:
+        # each batch is rounded to bf16 by the staging copy
+        log("d=2560 ragged, fp16 activations staged in bf16")
+        buf, views, sizes = ragged_setup(torch, W, 2560, seed=1, dtype="f16")
+        N = int(sizes.sum())
+        ms, _, _, _ = time_hessian(torch, hs, 2560, views, steps, 1, torch.bfloat16)
+        fl = syrk_flops(2560, N)
+        extra["d2560_ragged_f16_in_bf16_staging"] = {"ms": round(ms, 3), "tflops": round(fl / ms / 1e9, 1),
+                                                     "mfma_util": round(fl / (ms * 1e-3) / P_BF16, 4),
+                                                     "tokens": N}
+        del buf, views
     # d=4096 ragged (bf16 and fp32), dead columns 1%
     for dt, tdt in (() if "d4096_ragged" not in want else (("bf16", torch.bfloat16), ("f32", torch.float32))):
         log(f"d=4096 ragged {dt}")

@@ -23,4 +23,5 @@ from .hess_oracle import (  # noqa: F401
     column_sum_squares,
     round_to_bf16,
     staged_values,
+    chol_inverse_upper,
 )

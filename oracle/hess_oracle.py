@@ -28,6 +28,13 @@ What it computes, and where the pages define it
   the option applies to every GPTQ Hessian, fused MoE experts included).
 * ``column_sum_squares``: the imatrix statistic, a per-column sum of squares
   of the inputs (Model-Optimizer PR 3002 page, "What does this PR do?").
+* ``chol_inverse_upper``: the upper-triangular Cholesky factor of the inverse
+  of the damped Hessian, the quantization pass's step 4 (GPTQModel wiki
+  "QQQ", Concepts > Quadratic error compensation): U upper triangular with a
+  positive diagonal and U^T U = H^-1, which fixes U uniquely.  A damped H
+  that is not positive definite is a factorization error; there is no
+  automatic damping retry (wiki "QQQ", Pitfalls and the Quantizer API
+  notes on damp_auto_increment).
 * Staging dtype: activations are first put into the accumulator's staging
   type, then multiplied (GPTQModel PR 3052, "Shared-input Hessian dedup",
   review finding P2: an fp16 activation of 1 + 2^-10 stays exact when staged
@@ -73,6 +80,7 @@ __all__ = [
     "column_sum_squares",
     "round_to_bf16",
     "staged_values",
+    "chol_inverse_upper",
 ]
 
 
@@ -290,3 +298,19 @@ def gram_exact_fraction(rows_of_values) -> list:
             for j in range(d):
                 S[i][j] += r[i] * r[j]
     return S
+
+
+def chol_inverse_upper(H: np.ndarray) -> np.ndarray:
+    """Upper-triangular U, positive diagonal, with U^T U = H^-1 (float64).
+
+    H is the damped Hessian (symmetric).  The definition is applied as
+    written: invert H, then take the Cholesky factor of the inverse; numpy's
+    factor is the lower L with L L^T = H^-1, so U = L^T.  Raises
+    ``numpy.linalg.LinAlgError`` when H (hence H^-1) is not positive
+    definite.
+    """
+    H = np.asarray(H, dtype=np.float64)
+    np.linalg.cholesky(H)            # H itself must be positive definite
+    Hinv = np.linalg.inv(H)
+    L = np.linalg.cholesky(Hinv)     # reads the lower triangle of H^-1
+    return L.T.copy()

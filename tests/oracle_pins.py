@@ -345,7 +345,71 @@ def pin_imatrix(O, seed=14):
     assert np.array_equal(got, np.array(want)), (got, want)
 
 
+def _frac_inverse(M):
+    """Exact inverse of a small rational matrix by Gauss-Jordan elimination on Fractions."""
+    n = len(M)
+    A = [[Fraction(M[i][j]) for j in range(n)] + [Fraction(int(i == j)) for j in range(n)] for i in range(n)]
+    for c in range(n):
+        p = next(r for r in range(c, n) if A[r][c] != 0)
+        A[c], A[p] = A[p], A[c]
+        piv = A[c][c]
+        A[c] = [v / piv for v in A[c]]
+        for r in range(n):
+            if r != c and A[r][c] != 0:
+                f = A[r][c]
+                A[r] = [a - f * b for a, b in zip(A[r], A[c])]
+    return [row[n:] for row in A]
+
+
+def pin_chol_inverse_upper(O, seed=21):
+    """U upper with positive diagonal and U^T U = H^-1: closed forms (diagonal, 2 x 2), a factor
+    known by construction, exact rational inverses, the usual three-call library route, and the
+    not-positive-definite error."""
+    import torch
+    # diagonal H: U = diag(1 / sqrt(h))
+    h = np.array([4.0, 0.25, 9.0, 2.0])
+    U = O.chol_inverse_upper(np.diag(h))
+    assert np.allclose(U, np.diag(1 / np.sqrt(h)), rtol=1e-15, atol=0)
+    # 2 x 2 [[a, b], [b, c]]: u11 = sqrt(c / det), u12 = -b / sqrt(c det), u22 = 1 / sqrt(c)
+    a, b, c = 4.0, 2.0, 3.0
+    det = a * c - b * b
+    U = O.chol_inverse_upper(np.array([[a, b], [b, c]]))
+    want = np.array([[np.sqrt(c / det), -b / np.sqrt(c * det)], [0.0, 1 / np.sqrt(c)]])
+    assert np.allclose(U, want, rtol=1e-15, atol=1e-16), (U, want)
+    # H = V V^T with V upper, positive diagonal  =>  U = V^-1 (a unique factor)
+    rng = np.random.default_rng(seed)
+    d = 12
+    V = np.triu(rng.standard_normal((d, d)) * 0.3, 1) + np.diag(rng.uniform(0.5, 2.0, d))
+    U = O.chol_inverse_upper(V @ V.T)
+    Vinv = np.linalg.solve(V, np.eye(d))
+    assert np.allclose(U, Vinv, rtol=1e-11, atol=1e-12)
+    assert np.array_equal(U, np.triu(U)) and (np.diag(U) > 0).all()
+    # exact rational inverse at d = 4: U^T U matches it
+    M = [[6, 2, 1, 0], [2, 5, 2, 1], [1, 2, 4, 1], [0, 1, 1, 3]]
+    Minv = np.array([[float(v) for v in row] for row in _frac_inverse(M)])
+    U = O.chol_inverse_upper(np.array(M, dtype=np.float64))
+    assert np.allclose(U.T @ U, Minv, rtol=0, atol=1e-15)
+    # the library route: upper Cholesky of the inverse formed from the lower Cholesky of H
+    X = rng.standard_normal((200, 40))
+    H = 2.0 / 200 * X.T @ X
+    H += 0.01 * np.mean(np.diag(H)) * np.eye(40)
+    Ht = torch.from_numpy(H)
+    Ut = torch.linalg.cholesky(torch.cholesky_inverse(torch.linalg.cholesky(Ht)), upper=True).numpy()
+    U = O.chol_inverse_upper(H)
+    assert np.allclose(U, Ut, rtol=1e-10, atol=1e-12)
+    assert np.allclose(U.T @ U @ H, np.eye(40), atol=1e-10)
+    # not positive definite: an error, no silent result
+    for bad in (np.array([[1.0, 2.0], [2.0, 1.0]]), np.zeros((3, 3)), np.diag([1.0, -1e-3, 2.0])):
+        try:
+            O.chol_inverse_upper(bad)
+        except np.linalg.LinAlgError:
+            pass
+        else:
+            raise AssertionError("non-positive-definite input accepted")
+
+
 ALL_PINS = [
+    pin_chol_inverse_upper,
     pin_imatrix,
     pin_bruteforce_fraction,
     pin_orientation_hand,

@@ -38,6 +38,7 @@ def _ns(**over):
         column_sum_squares=HO.column_sum_squares,
         round_to_bf16=HO.round_to_bf16,
         staged_values=HO.staged_values,
+        chol_inverse_upper=HO.chol_inverse_upper,
     )
     base.update(over)
     return types.SimpleNamespace(**base)
@@ -238,7 +239,23 @@ def _staging_ignored():
     return dict(GramAccumulator=Acc, staged_values=lambda X, t, s: HO.exact_float64(X, t))
 
 
+def _chol_lower_returned(H):
+    return np.linalg.cholesky(np.linalg.inv(np.asarray(H, dtype=np.float64)))  # mistake: the lower factor
+
+
+def _chol_of_h(H):
+    return np.linalg.cholesky(np.asarray(H, dtype=np.float64)).T.copy()  # mistake: factor of H, not of H^-1
+
+
+def _chol_inverse_of_factor(H):
+    L = np.linalg.cholesky(np.asarray(H, dtype=np.float64))
+    return np.linalg.inv(L).T.copy()  # mistake: U = L^-T gives U^T U = (L^T L)^-1, not (L L^T)^-1
+
+
 MUTANTS = {
+    "chol_lower_factor": _ns(chol_inverse_upper=_chol_lower_returned),
+    "chol_of_h": _ns(chol_inverse_upper=_chol_of_h),
+    "chol_inverse_of_h_factor": _ns(chol_inverse_upper=_chol_inverse_of_factor),
     "bf16_round_truncates": _ns(**_staging_mutant(_round_truncates)),
     "bf16_round_half_away": _ns(**_staging_mutant(_round_half_away)),
     "bf16_round_9_bits": _ns(**_staging_mutant(_round_keeps_8_fraction_bits)),

@@ -169,12 +169,14 @@ def torch_column_scales(gen, d: int, device):
 
 
 def torch_rows(gen, n: int, d: int, scales, dtype: str, device, out=None):
-    """(n, d) activations N(0,1)*scales drawn on ``device``; bf16 or float32."""
+    """(n, d) activations N(0,1)*scales drawn on ``device``; bf16, fp16 or float32."""
     import torch
     x = torch.randn((n, d), generator=gen, device=device, dtype=torch.float32)
     x.mul_(scales[None, :])
     if dtype == BF16:
         x = x.to(torch.bfloat16)
+    elif dtype == F16:
+        x = x.to(torch.float16)
     if out is not None:
         out.copy_(x)
         return out
