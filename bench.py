@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 P_BF16 = 2.5e15        # MI355X dense bf16 matrix peak, FLOP/s
 P_F32_MFMA = 157.3e12  # MI355X fp32 matrix peak, FLOP/s
+P_F64 = 78.6e12        # MI355X fp64 peak (matrix and vector), FLOP/s
 HBM = 8.0e12           # MI355X HBM3E peak, bytes/s
 METRIC = "ms per Hessian & TFLOP/s (MFMA util %) at d=2560/4096, ragged batches"
 PAGES_MS = {2560: 11.0, 4096: 15.0}  # the pages' GB300 bf16-in numbers for ~360 ragged batches
@@ -169,7 +170,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--extras", default="all",
-                    help="comma-separated subset of d4096_ragged,d4096_single,moe,local,imatrix,f16_staging "
+                    help="comma-separated subset of d4096_ragged,d4096_single,moe,local,imatrix,f16_staging,chol "
                          "(default all; imatrix runs with local)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--print-kernel-sha", action="store_true",
@@ -276,8 +277,34 @@ def run_extras(torch, hs, W, args):
     extra = {}
     steps = max(3, args.steps // 2)
     want = set(args.extras.split(",")) if args.extras != "all" else {"d4096_ragged", "d4096_single", "moe", "local",
-                                                                    "imatrix", "f16_staging"}
+                                                                    "imatrix", "f16_staging", "chol"}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if "chol" in want:
+        # upper Cholesky factor of the inverse damped Hessian, float64 inside:
+        # 2 d^3 / 3 flops (factor d^3 / 3 + triangular inverse d^3 / 3)
+        for dc in (2560, 4096):
+            log(f"Cholesky of the inverse, d={dc}")
+            gen = W.torch_generator(5, "cuda")
+            sc = W.torch_column_scales(gen, dc, "cuda")
+            x = W.torch_rows(gen, 2 * dc, dc, sc, "f32", "cuda")
+            H = (x.T @ x) * (2.0 / (2 * dc))
+            H += 0.01 * H.diagonal().mean() * torch.eye(dc, device="cuda")
+            U = torch.empty_like(H)
+            ws = torch.empty(hs._load().hess_chol_inverse_workspace(dc), dtype=torch.uint8, device="cuda")
+            for _ in range(2):
+                hs.chol_inverse_upper(H, out=U, workspace=ws, check=False)
+            torch.cuda.synchronize()
+            reps = max(3, steps)
+            e0.record()
+            for _ in range(reps):
+                hs.chol_inverse_upper(H, out=U, workspace=ws, check=False)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            fl = 2.0 * dc ** 3 / 3.0
+            extra[f"chol_inverse_upper_d{dc}"] = {"ms": round(ms, 4), "tflops_f64": round(fl / ms / 1e9, 2),
+                                                  "f64_util": round(fl / (ms * 1e-3) / P_F64, 4)}
+            del x, H, U, ws
     if "f16_staging" in want:
         # the d=2560 ragged workload with fp16 activations, staged in bf16:
         # each batch is rounded to bf16 by the staging copy

@@ -29,6 +29,7 @@ __all__ = [
     "HessError",
     "local_blocks",
     "add_batch_grouped",
+    "chol_inverse_upper",
     "set_tile_override",
     "set_staging",
     "library_path",
@@ -45,7 +46,7 @@ HESS_F16 = 2
 HESS_NO_NEUTRALIZE = 1
 
 _STATUS = {0: "HESS_OK", -1: "HESS_EINVAL", -2: "HESS_ENOMEM", -3: "HESS_EHIP", -4: "HESS_ESTATE",
-           -5: "HESS_EALIGN"}
+           -5: "HESS_EALIGN", -6: "HESS_ENOTPD"}
 
 
 class HessError(RuntimeError):
@@ -98,6 +99,8 @@ def _load():
         "hess_local_blocks_ex": (c_int, [vp, c_int, i64, i64, i64, c_int, vp, c_int, vp]),
         "hess_add_batch_grouped": (c_int, [ctypes.POINTER(vp), c_int, vp, i64, vp, ctypes.POINTER(i64), vp]),
         "hess_adopt": (c_int, [vp, vp, vp]),
+        "hess_chol_inverse_workspace": (i64, [i64]),
+        "hess_chol_inverse_upper": (c_int, [vp, i64, i64, vp, i64, vp, i64, vp, vp]),
         "hess_imatrix_create": (vp, [i64, c_int]),
         "hess_imatrix_destroy": (c_int, [vp]),
         "hess_imatrix_add_batch": (c_int, [vp, vp, i64, i64, vp]),
@@ -306,6 +309,41 @@ def local_blocks(x: torch.Tensor, out: torch.Tensor | None = None, accumulate: b
     ptr = x2.data_ptr() if n > 0 else None
     _check(_load().hess_local_blocks_ex(ptr, _dtype_code(x.dtype), n, d, ld, block, out.data_ptr(),
                                         1 if accumulate else 0, _stream(stream)))
+    return out
+
+
+def chol_inverse_upper(H: torch.Tensor, out: torch.Tensor | None = None, check: bool = True,
+                       workspace: torch.Tensor | None = None, stream=None):
+    """U (float32, upper triangular, positive diagonal) with U^T U = H^-1, for a damped Hessian H.
+
+    Only H's upper triangle is read; ``out`` may be H itself.  With ``check``
+    the call waits for the result and raises HessError(HESS_ENOTPD) when H
+    is not positive definite; otherwise it returns ``(U, info)`` with info a
+    device int32 tensor (0, or 1 + the failing column).
+    """
+    if not H.is_cuda or H.dtype != torch.float32 or H.dim() != 2 or H.shape[0] != H.shape[1]:
+        raise ValueError("H must be a square float32 GPU tensor")
+    if H.stride(1) != 1:
+        raise ValueError("H must have unit column stride")
+    lib = _load()
+    d = H.shape[0]
+    if out is None:
+        out = torch.empty((d, d), dtype=torch.float32, device=H.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (d, d) or out.stride(1) != 1:
+        raise ValueError("out must be a float32 (d, d) GPU tensor with unit column stride")
+    need = int(lib.hess_chol_inverse_workspace(d))
+    if need < 0:
+        raise HessError(-1, f"width {d} not supported")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=H.device)
+    info = torch.empty(1, dtype=torch.int32, device=H.device)
+    _check(lib.hess_chol_inverse_upper(H.data_ptr(), d, H.stride(0), out.data_ptr(), out.stride(0),
+                                       workspace.data_ptr(), need, info.data_ptr(), _stream(stream)))
+    if not check:
+        return out, info
+    bad = int(info.item())
+    if bad:
+        raise HessError(-6, f"the damped Hessian is not positive definite (pivot of column {bad - 1} failed)")
     return out
 
 

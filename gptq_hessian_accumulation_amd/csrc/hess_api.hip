@@ -193,6 +193,7 @@ bool stage_pays(const hess_s* h, int64_t n) {
   return g_staging && h->stage && n <= h->stage_cap && n * esize(h->dtype) < 2 * h->d;
 }
 
+constexpr int64_t kCholMaxD = 32768;  // largest width of hess_chol_inverse_upper (16 GiB of workspace)
 constexpr int64_t kImxSplits = 1024;  // row splits of one imatrix batch (partials per column)
 
 // Calls on an imatrix handle from a new stream wait for the previous stream's work.
@@ -566,6 +567,7 @@ const char* hess_strerror(int code) {
     case HESS_EHIP: return "HIP runtime error";
     case HESS_ESTATE: return "handle consumed by an in-place materialize";
     case HESS_EALIGN: return "misaligned input";
+    case HESS_ENOTPD: return "matrix not positive definite";
     default: return "unknown status";
   }
 }
@@ -920,6 +922,36 @@ int hess_adopt(hess_t dst, hess_t src, hess_stream_t stream) {
   dst->N = src->N;
   dst->consumed = false;
   return HESS_OK;
+}
+
+int64_t hess_chol_inverse_workspace(int64_t d) {
+  if (d < 1 || d > kCholMaxD) return -1;
+  const int64_t dp = chol_padded(d);
+  return (2 * dp * dp + dp * 64) * (int64_t)sizeof(double);
+}
+
+int hess_chol_inverse_upper(const float* H, int64_t d, int64_t ldh, float* U, int64_t ldu, void* work,
+                            int64_t work_bytes, int* info, hess_stream_t stream) {
+  if (d < 1 || d > kCholMaxD) return fail(HESS_EINVAL, "d = %lld outside [1, %lld]", (long long)d, (long long)kCholMaxD);
+  if (!H || !U || !work) return fail(HESS_EINVAL, "null H, U or workspace");
+  if (ldh < d || ldu < d) return fail(HESS_EINVAL, "row stride below d");
+  if ((reinterpret_cast<uintptr_t>(H) & 3u) || (reinterpret_cast<uintptr_t>(U) & 3u))
+    return fail(HESS_EALIGN, "H or U not float-aligned");
+  if (reinterpret_cast<uintptr_t>(work) & 15u) return fail(HESS_EALIGN, "workspace not 16-byte aligned");
+  const int64_t need = hess_chol_inverse_workspace(d);
+  if (work_bytes < need)
+    return fail(HESS_EINVAL, "workspace of %lld bytes, %lld needed", (long long)work_bytes, (long long)need);
+  // U may be H itself (same stride); any other overlap is refused
+  const uintptr_t h0 = reinterpret_cast<uintptr_t>(H), h1 = h0 + (uintptr_t)(((d - 1) * ldh + d) * 4);
+  const uintptr_t u0 = reinterpret_cast<uintptr_t>(U), u1 = u0 + (uintptr_t)(((d - 1) * ldu + d) * 4);
+  if (u0 < h1 && h0 < u1 && !(u0 == h0 && ldu == ldh)) return fail(HESS_EINVAL, "U overlaps H without being H");
+  const uintptr_t w0 = reinterpret_cast<uintptr_t>(work), w1 = w0 + (uintptr_t)need;
+  if ((w0 < h1 && h0 < w1) || (w0 < u1 && u0 < w1)) return fail(HESS_EINVAL, "workspace overlaps H or U");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t dp = chol_padded(d);
+  double* A = static_cast<double*>(work);
+  hipError_t e = launch_chol_inverse_upper(H, ldh, (int)d, U, ldu, A, A + dp * dp, A + 2 * dp * dp, info, s);
+  return e == hipSuccess ? HESS_OK : hip_fail(e, "Cholesky-of-inverse launch");
 }
 
 int hess_set_group_chunk(int64_t bytes) {

@@ -137,6 +137,15 @@ hipError_t launch_local_blocks(const void* X, int in_dtype, int64_t n, int d, in
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 
+// Upper Cholesky factor of the inverse: U (d x d float32, row stride ldu,
+// zeros below the diagonal) with U^T U = H^-1, from the upper triangle of H
+// (row stride ldh).  A and X are chol_padded(d)^2 float64 each, P is
+// chol_padded(d) x 64 float64; info (device, nullable) receives 0 or 1 + the
+// largest H column whose pivot failed.
+int64_t chol_padded(int64_t d);
+hipError_t launch_chol_inverse_upper(const float* H, int64_t ldh, int d, float* U, int64_t ldu, double* A, double* X,
+                                     double* P, int* info, hipStream_t stream);
+
 // Transposed staging copy (bf16): n rows of X (row stride ld) into 8-token
 // blocks at dst, chunk f of block b = tokens 8b..8b+7 of feature f (16
 // bytes), blocks of d chunks; rows n .. round_up(n, 8) - 1 are written as zeros.

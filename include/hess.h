@@ -59,7 +59,9 @@ enum hess_status {
   HESS_ENOMEM = -2, /* device allocation failed (hess_create only) */
   HESS_EHIP = -3,   /* a HIP runtime or launch error; see hess_last_error() */
   HESS_ESTATE = -4, /* handle consumed by an in-place materialize */
-  HESS_EALIGN = -5  /* X not aligned to its element size */
+  HESS_EALIGN = -5, /* X not aligned to its element size */
+  HESS_ENOTPD = -6  /* a matrix to factor is not positive definite (reported by
+                       bindings after reading hess_chol_inverse_upper's info) */
 };
 
 /* hess_materialize_ex flags */
@@ -331,6 +333,34 @@ int hess_local_blocks_ex(const void* X, int in_dtype, int64_t n_tokens, int64_t 
  */
 int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld,
                            const int32_t* row_idx, const int64_t* offsets, hess_stream_t stream);
+
+/*
+ * hess_chol_inverse_upper -- the upper Cholesky factor of the inverse of a
+ * damped Hessian: U upper triangular with a positive diagonal and
+ * U^T U = H^-1 (the quantization pass's step 4 after neutralization and
+ * damping: GPTQModel wiki "QQQ", Concepts > Quadratic error compensation).
+ *
+ * Computed in float64 (H widened exactly) by factoring the index-reversed H
+ * and inverting that factor, then rounded once to float32.
+ *   H      device float32, d x d, row stride ldh >= d; only its upper
+ *          triangle (j >= i) is read (hess_materialize's output qualifies).
+ *   U      device float32, d x d, row stride ldu >= d; every entry written
+ *          (zeros below the diagonal).  U may be H itself (same stride: in
+ *          place); no other overlap is allowed.
+ *   work   device workspace of hess_chol_inverse_workspace(d) bytes, 16-byte
+ *          aligned, owned by the caller, not overlapping H or U.
+ *   info   device int, nullable: set to 0, or on failure to 1 + the largest
+ *          column j of H whose pivot was not positive (H[j:, j:] is then not
+ *          positive definite).  The pages raise the factorization error and
+ *          retry nothing (wiki "QQQ", Pitfalls; damp_auto_increment is not
+ *          applied): a failed factorization leaves NaN in U and says so in
+ *          info, which the caller reads after the stream reaches this call.
+ *   1 <= d <= 32768.  Errors: EINVAL (bad sizes, null pointers, workspace too
+ *   small, overlaps), EALIGN, EHIP.  Enqueued on stream; allocates nothing.
+ */
+int64_t hess_chol_inverse_workspace(int64_t d); /* bytes, or -1 for a bad d */
+int hess_chol_inverse_upper(const float* H, int64_t d, int64_t ldh, float* U, int64_t ldu, void* work,
+                            int64_t work_bytes, int* info, hess_stream_t stream);
 
 /*
  * imatrix statistic -- per-column float32 sums of squares of a layer's

@@ -54,6 +54,28 @@ def test_invalid_arguments_rejected_without_gpu():
     assert b"staging_bytes" in lib.hess_last_error()
     offs = (ctypes.c_int64 * 2)(0, 1)
     assert lib.hess_add_batch_grouped(None, 1, None, 16, None, offs, None) == -1
+    # Cholesky of the inverse: workspace size rule and argument checks (no device work)
+    assert lib.hess_chol_inverse_workspace(0) == -1
+    assert lib.hess_chol_inverse_workspace(1) == (2 * 64 * 64 + 64 * 64) * 8
+    assert lib.hess_chol_inverse_workspace(65) == (2 * 128 * 128 + 128 * 64) * 8
+    p = lambda a: ctypes.c_void_p(a)  # noqa: E731  (fake, never dereferenced)
+    base = 1 << 40
+    need = lib.hess_chol_inverse_workspace(100)
+    assert lib.hess_chol_inverse_upper(p(base), 100, 100, p(base + (1 << 30)), 100, p(base + (2 << 30)), need - 1,
+                                       None, None) == -1
+    assert b"workspace" in lib.hess_last_error()
+    assert lib.hess_chol_inverse_upper(p(base), 100, 99, p(base + (1 << 30)), 100, p(base + (2 << 30)), need,
+                                       None, None) == -1
+    assert lib.hess_chol_inverse_upper(p(base), 100, 100, p(base + 400), 100, p(base + (2 << 30)), need,
+                                       None, None) == -1
+    assert b"overlaps" in lib.hess_last_error()
+    assert lib.hess_chol_inverse_upper(p(base), 100, 100, p(base + (1 << 30)), 100, p(base + 16), need,
+                                       None, None) == -1
+    assert lib.hess_chol_inverse_upper(p(base), 40000, 40000, p(base + (1 << 30)), 40000, p(base + (2 << 30)),
+                                       need, None, None) == -1
+    # the staging dtype of a handle is bf16 or f32; fp16 is an activation type only
+    assert not lib.hess_create(16, 2)
+    assert lib.hess_add_batch_cast(None, None, 2, 1, 16, None) == -1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
