@@ -24,4 +24,6 @@ from .hess_oracle import (  # noqa: F401
     round_to_bf16,
     staged_values,
     chol_inverse_upper,
+    quant_scale,
+    gptq_quantize,
 )

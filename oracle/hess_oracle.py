@@ -35,6 +35,18 @@ What it computes, and where the pages define it
   that is not positive definite is a factorization error; there is no
   automatic damping retry (wiki "QQQ", Pitfalls and the Quantizer API
   notes on damp_auto_increment).
+* ``gptq_quantize``: the quantization pass's step 5 (wiki "QQQ", Concepts >
+  Quadratic error compensation): columns are quantized in order and each
+  column's error, divided by the factor's diagonal entry, is propagated into
+  the columns not yet quantized through the row of the factor; the
+  quantizer is symmetric 4-bit, one per output row (group_size -1) or per
+  group of contiguous input columns (wiki "QQQ", Whole-row and grouped
+  weight quantization), with group parameters taken when a group is reached
+  (static_groups off, wiki "QQQ" configuration table); the loss is the
+  summed squared scaled error over the token count (wiki "QQQ",
+  Implementation internals > Quantizer API and results).  The pages process
+  128-column blocks; blocking changes only the order of the float64
+  additions, so the oracle propagates column by column.
 * Staging dtype: activations are first put into the accumulator's staging
   type, then multiplied (GPTQModel PR 3052, "Shared-input Hessian dedup",
   review finding P2: an fp16 activation of 1 + 2^-10 stays exact when staged
@@ -81,6 +93,8 @@ __all__ = [
     "round_to_bf16",
     "staged_values",
     "chol_inverse_upper",
+    "quant_scale",
+    "gptq_quantize",
 ]
 
 
@@ -314,3 +328,56 @@ def chol_inverse_upper(H: np.ndarray) -> np.ndarray:
     Hinv = np.linalg.inv(H)
     L = np.linalg.cholesky(Hinv)     # reads the lower triangle of H^-1
     return L.T.copy()
+
+
+def quant_scale(x: np.ndarray, bits: int = 4) -> np.ndarray:
+    """Symmetric quantizer step per row of x: 2 max|x| / (2^bits - 1).
+
+    Codes are q = clip(rint(w / scale) + 2^(bits-1), 0, 2^bits - 1), i.e.
+    signed values q - 2^(bits-1) in [-2^(bits-1), 2^(bits-1) - 1] around the
+    fixed centre, dequantized as scale (q - 2^(bits-1)).  A row that is all
+    zero takes max|x| = 1.
+    """
+    a = np.max(np.abs(np.asarray(x, dtype=np.float64)), axis=1)
+    a = np.where(a == 0.0, 1.0, a)
+    return 2.0 * a / float(2 ** bits - 1)
+
+
+def gptq_quantize(W: np.ndarray, U: np.ndarray, group_size: int = -1, bits: int = 4, dead=None,
+                  nsamples: int = 1):
+    """Error-propagating quantization of W (rows = outputs, columns = inputs).
+
+    U is the upper Cholesky factor of the inverse damped Hessian (only its
+    upper triangle is used).  Returns ``(Q, codes, scales, loss)``: Q the
+    dequantized weights (float64), codes uint8 in [0, 2^bits - 1], scales
+    (rows, groups) float64 (one column for group_size -1), loss the summed
+    squared scaled error over ``nsamples``.
+    """
+    W = np.array(W, dtype=np.float64)
+    U = np.triu(np.asarray(U, dtype=np.float64))
+    N, K = W.shape
+    if dead is not None:
+        W[:, np.asarray(dead, dtype=bool)] = 0.0   # the weight side of dead-column neutralization
+    maxq = 2 ** bits - 1
+    centre = 2 ** (bits - 1)
+    g = K if group_size in (-1, K) else int(group_size)
+    ngroups = -(-K // g)
+    scales = np.zeros((N, ngroups), dtype=np.float64)
+    codes = np.zeros((N, K), dtype=np.uint8)
+    Q = np.zeros((N, K), dtype=np.float64)
+    loss = 0.0
+    scale = None
+    for i in range(K):
+        if i % g == 0:
+            # parameters from the group's current (already error-updated) weights
+            scale = quant_scale(W[:, i:i + g], bits)
+            scales[:, i // g] = scale
+        w = W[:, i].copy()
+        q = np.clip(np.rint(w / scale) + centre, 0, maxq)
+        deq = scale * (q - centre)
+        err = (w - deq) / U[i, i]
+        W[:, i + 1:] -= np.outer(err, U[i, i + 1:])
+        codes[:, i] = q.astype(np.uint8)
+        Q[:, i] = deq
+        loss += float(np.sum(err * err))
+    return Q, codes, scales, loss / nsamples

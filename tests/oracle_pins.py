@@ -408,7 +408,73 @@ def pin_chol_inverse_upper(O, seed=21):
             raise AssertionError("non-positive-definite input accepted")
 
 
+def _obs_quantize(W, H, group, bits=4):
+    """GPTQ as optimal brain surgery, written independently of the oracle: at column i the
+    remaining weights F = i..K-1 move by -(w_i - deq_i) / [inv(H_FF)]_00 inv(H_FF)[0, :], with the
+    inverse of the remaining block recomputed by a library inverse at every step."""
+    W = np.array(W, dtype=np.float64)
+    N, K = W.shape
+    g = K if group in (-1, K) else group
+    Q = np.zeros_like(W)
+    codes = np.zeros((N, K), dtype=np.int64)
+    loss = 0.0
+    for i in range(K):
+        if i % g == 0:
+            a = np.max(np.abs(W[:, i:i + g]), axis=1)
+            scale = 2.0 * np.where(a == 0, 1.0, a) / (2 ** bits - 1)
+        Hinv = np.linalg.inv(H[i:, i:])
+        w = W[:, i].copy()
+        q = np.clip(np.rint(w / scale) + 2 ** (bits - 1), 0, 2 ** bits - 1)
+        deq = scale * (q - 2 ** (bits - 1))
+        W[:, i:] -= np.outer((w - deq) / Hinv[0, 0], Hinv[0, :])
+        loss += float(np.sum((w - deq) ** 2 / Hinv[0, 0]))
+        Q[:, i] = deq
+        codes[:, i] = q
+    return Q, codes, loss
+
+
+def pin_gptq_quantize(O, seed=31):
+    """Quantizer hand values; identity Hessian = plain rounding; the factor-row propagation equals
+    optimal-brain-surgery updates with explicit inverses (whole rows and groups); dead columns
+    quantize to zero and move nothing."""
+    g = _load("quantizer_hand.json")
+    row = np.asarray([g["row"]])
+    assert abs(O.quant_scale(row)[0] - g["scale"]) <= 1e-15
+    assert abs(O.quant_scale(np.zeros((1, 3)))[0] - g["zero_row_scale"]) <= 1e-15
+    Q, codes, scales, loss = O.gptq_quantize(row, np.eye(row.shape[1]))
+    assert codes[0].tolist() == g["codes"], codes
+    assert np.allclose(Q[0], g["dequantized"], rtol=0, atol=1e-15)
+    assert abs(loss - float(np.sum((row[0] - np.asarray(g["dequantized"])) ** 2))) <= 1e-14
+    rng = np.random.default_rng(seed)
+    for N, K, group in ((5, 6, -1), (4, 12, 4), (3, 9, 3), (6, 16, 8)):
+        X = rng.standard_normal((3 * K, K))
+        H = 2.0 / (3 * K) * X.T @ X
+        H += 0.01 * np.mean(np.diag(H)) * np.eye(K)
+        W = rng.standard_normal((N, K))
+        U = O.chol_inverse_upper(H)
+        Q, codes, scales, loss = O.gptq_quantize(W, U, group_size=group, nsamples=7)
+        Qr, codes_r, loss_r = _obs_quantize(W, H, group)
+        assert np.array_equal(codes, codes_r), (N, K, group)
+        assert np.allclose(Q, Qr, rtol=1e-12, atol=1e-12)
+        assert abs(loss * 7 - loss_r) <= 1e-10 * max(1.0, loss_r)
+        assert scales.shape == (N, 1 if group == -1 else -(-K // group))
+    # dead columns: zero weights, centre codes, no error to move
+    W = rng.standard_normal((4, 8))
+    X = rng.standard_normal((30, 8))
+    H = X.T @ X / 15 + 0.05 * np.eye(8)
+    U = O.chol_inverse_upper(H)
+    dead = np.zeros(8, dtype=bool)
+    dead[[2, 5]] = True
+    Q, codes, _, _ = O.gptq_quantize(W, U, dead=dead)
+    assert (codes[:, dead] == 8).all() and not Q[:, dead].any()
+    W2 = W.copy()
+    W2[:, dead] = 0.0
+    Q2, codes2, _, _ = O.gptq_quantize(W2, U)
+    assert np.array_equal(codes, codes2) and np.array_equal(Q, Q2)
+
+
 ALL_PINS = [
+    pin_gptq_quantize,
     pin_chol_inverse_upper,
     pin_imatrix,
     pin_bruteforce_fraction,

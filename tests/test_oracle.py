@@ -39,6 +39,8 @@ def _ns(**over):
         round_to_bf16=HO.round_to_bf16,
         staged_values=HO.staged_values,
         chol_inverse_upper=HO.chol_inverse_upper,
+        quant_scale=HO.quant_scale,
+        gptq_quantize=HO.gptq_quantize,
     )
     base.update(over)
     return types.SimpleNamespace(**base)
@@ -252,7 +254,47 @@ def _chol_inverse_of_factor(H):
     return np.linalg.inv(L).T.copy()  # mistake: U = L^-T gives U^T U = (L^T L)^-1, not (L L^T)^-1
 
 
+def _gptq_mutant(kind):
+    def run(W, U, group_size=-1, bits=4, dead=None, nsamples=1):
+        W = np.array(W, dtype=np.float64)
+        U = np.triu(np.asarray(U, dtype=np.float64))
+        N, K = W.shape
+        if dead is not None:
+            W[:, np.asarray(dead, dtype=bool)] = 0.0
+        W0 = W.copy()
+        g = K if group_size in (-1, K) else group_size
+        scales = np.zeros((N, -(-K // g)))
+        codes = np.zeros((N, K), dtype=np.uint8)
+        Q = np.zeros((N, K))
+        loss = 0.0
+        for i in range(K):
+            if i % g == 0:
+                src = W0 if kind == "static_groups" else W   # mistake: parameters from the untouched weights
+                a = np.max(np.abs(src[:, i:i + g]), axis=1)
+                a = np.where(a == 0, 1.0, a)
+                scale = a / 7.0 if kind == "scale_absmax_over_7" else 2 * a / 15.0  # mistake: other step
+                scales[:, i // g] = scale
+            w = W[:, i].copy()
+            x = w / scale
+            r = np.floor(x + 0.5) if kind == "ties_away" else np.rint(x)  # mistake: ties not to even
+            q = np.clip(r + 8, 0, 15)
+            deq = scale * (q - 8)
+            err = (w - deq) if kind == "no_diag_division" else (w - deq) / U[i, i]  # mistake: unscaled
+            if kind == "column_of_factor":
+                W[:, i + 1:] -= np.outer(err, U[i + 1:, i])   # mistake: the factor's column, not its row
+            else:
+                W[:, i + 1:] -= np.outer(err, U[i, i + 1:])
+            codes[:, i] = q
+            Q[:, i] = deq
+            loss += float(np.sum((w - deq) ** 2)) if kind == "loss_unscaled" else float(np.sum(err * err))
+        return Q, codes, scales, loss / nsamples
+    return run
+
+
 MUTANTS = {
+    **{f"gptq_{k}": _ns(gptq_quantize=_gptq_mutant(k)) for k in
+       ("static_groups", "scale_absmax_over_7", "ties_away", "no_diag_division", "column_of_factor",
+        "loss_unscaled")},
     "chol_lower_factor": _ns(chol_inverse_upper=_chol_lower_returned),
     "chol_of_h": _ns(chol_inverse_upper=_chol_of_h),
     "chol_inverse_of_h_factor": _ns(chol_inverse_upper=_chol_inverse_of_factor),
