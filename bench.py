@@ -170,7 +170,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--extras", default="all",
-                    help="comma-separated subset of d4096_ragged,d4096_single,moe,local,imatrix,f16_staging,chol "
+                    help="comma-separated subset of d4096_ragged,d4096_single,moe,local,imatrix,f16_staging,chol,quant "
                          "(default all; imatrix runs with local)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--print-kernel-sha", action="store_true",
@@ -277,8 +277,36 @@ def run_extras(torch, hs, W, args):
     extra = {}
     steps = max(3, args.steps // 2)
     want = set(args.extras.split(",")) if args.extras != "all" else {"d4096_ragged", "d4096_single", "moe", "local",
-                                                                    "imatrix", "f16_staging", "chol"}
+                                                                    "imatrix", "f16_staging", "chol", "quant"}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if "quant" in want:
+        # error-propagating 4-bit quantization of a 4096 x 4096 layer (groups of 128), float64
+        # inside: the propagation is rows * cols^2 flops (one multiply-add per remaining column)
+        log("block quantize 4096 x 4096")
+        dq = 4096
+        gen = W.torch_generator(6, "cuda")
+        sc = W.torch_column_scales(gen, dq, "cuda")
+        x = W.torch_rows(gen, 2 * dq, dq, sc, "f32", "cuda")
+        H = (x.T @ x) * (2.0 / (2 * dq))
+        H += 0.01 * H.diagonal().mean() * torch.eye(dq, device="cuda")
+        U = hs.chol_inverse_upper(H)
+        Wq = torch.randn((dq, dq), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+        ws = torch.empty(hs._load().hess_gptq_quantize_workspace(dq, dq), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(Wq)
+        for _ in range(2):
+            hs.gptq_quantize(Wq, U, group_size=128, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        reps = max(3, steps)
+        e0.record()
+        for _ in range(reps):
+            hs.gptq_quantize(Wq, U, group_size=128, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        fl = float(dq) * dq * dq
+        extra["gptq_quantize_4096x4096_g128"] = {"ms": round(ms, 4), "tflops_f64": round(fl / ms / 1e9, 2),
+                                                 "f64_util": round(fl / (ms * 1e-3) / P_F64, 4)}
+        del x, H, U, Wq, ws, out
     if "chol" in want:
         # upper Cholesky factor of the inverse damped Hessian, float64 inside:
         # 2 d^3 / 3 flops (factor d^3 / 3 + triangular inverse d^3 / 3)

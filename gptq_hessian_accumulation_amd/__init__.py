@@ -30,6 +30,7 @@ __all__ = [
     "local_blocks",
     "add_batch_grouped",
     "chol_inverse_upper",
+    "gptq_quantize",
     "set_tile_override",
     "set_staging",
     "library_path",
@@ -100,6 +101,9 @@ def _load():
         "hess_add_batch_grouped": (c_int, [ctypes.POINTER(vp), c_int, vp, i64, vp, ctypes.POINTER(i64), vp]),
         "hess_adopt": (c_int, [vp, vp, vp]),
         "hess_chol_inverse_workspace": (i64, [i64]),
+        "hess_gptq_quantize_workspace": (i64, [i64, i64]),
+        "hess_gptq_quantize": (c_int, [vp, i64, i64, i64, vp, i64, vp, c_int, vp, i64, vp, i64, vp, vp, i64, vp,
+                                       i64, vp]),
         "hess_chol_inverse_upper": (c_int, [vp, i64, i64, vp, i64, vp, i64, vp, vp]),
         "hess_imatrix_create": (vp, [i64, c_int]),
         "hess_imatrix_destroy": (c_int, [vp]),
@@ -345,6 +349,46 @@ def chol_inverse_upper(H: torch.Tensor, out: torch.Tensor | None = None, check: 
     if bad:
         raise HessError(-6, f"the damped Hessian is not positive definite (pivot of column {bad - 1} failed)")
     return out
+
+
+def gptq_quantize(W: torch.Tensor, U: torch.Tensor, group_size: int = -1, dead: torch.Tensor | None = None,
+                  nsamples: int = 1, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  stream=None):
+    """4-bit error-propagating quantization of W (outputs x inputs, float32) with the factor U.
+
+    Returns ``(Q, codes, scales, loss)``: dequantized float32 weights (``out`` may be W itself),
+    uint8 codes 0..15, float32 steps (rows x groups) and a float64 device scalar loss.
+    """
+    for name, t in (("W", W), ("U", U)):
+        if not t.is_cuda or t.dtype != torch.float32 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be a 2-D float32 GPU tensor with unit column stride")
+    rows, cols = W.shape
+    if tuple(U.shape) != (cols, cols):
+        raise ValueError("U must be (cols, cols)")
+    lib = _load()
+    dev = W.device
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    groups = 1 if group_size == -1 or group_size >= cols else -(-cols // group_size)
+    scales = torch.empty((rows, groups), dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float64, device=dev)
+    need = int(lib.hess_gptq_quantize_workspace(rows, cols))
+    if need < 0:
+        raise HessError(-1, f"shape {rows} x {cols} not supported")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    dptr = None
+    if dead is not None:
+        dead = dead.to(device=dev, dtype=torch.uint8).contiguous()
+        if dead.numel() != cols:
+            raise ValueError("dead must have one entry per column")
+        dptr = dead.data_ptr()
+    _check(lib.hess_gptq_quantize(W.data_ptr(), rows, cols, W.stride(0), U.data_ptr(), U.stride(0), dptr,
+                                  int(group_size), out.data_ptr(), out.stride(0), codes.data_ptr(), codes.stride(0),
+                                  scales.data_ptr(), loss.data_ptr(), int(nsamples), workspace.data_ptr(), need,
+                                  _stream(stream)))
+    return out, codes, scales, loss
 
 
 class ImatrixStat:

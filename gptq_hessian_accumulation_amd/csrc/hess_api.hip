@@ -193,6 +193,7 @@ bool stage_pays(const hess_s* h, int64_t n) {
   return g_staging && h->stage && n <= h->stage_cap && n * esize(h->dtype) < 2 * h->d;
 }
 
+constexpr int64_t kQuantMaxDim = 65536;  // largest rows / cols of hess_gptq_quantize
 constexpr int64_t kCholMaxD = 32768;  // largest width of hess_chol_inverse_upper (16 GiB of workspace)
 constexpr int64_t kImxSplits = 1024;  // row splits of one imatrix batch (partials per column)
 
@@ -952,6 +953,59 @@ int hess_chol_inverse_upper(const float* H, int64_t d, int64_t ldh, float* U, in
   double* A = static_cast<double*>(work);
   hipError_t e = launch_chol_inverse_upper(H, ldh, (int)d, U, ldu, A, A + dp * dp, A + 2 * dp * dp, info, s);
   return e == hipSuccess ? HESS_OK : hip_fail(e, "Cholesky-of-inverse launch");
+}
+
+int64_t hess_gptq_quantize_workspace(int64_t rows, int64_t cols) {
+  if (rows < 1 || rows > kQuantMaxDim || cols < 1 || cols > kQuantMaxDim) return -1;
+  return quant_workspace_doubles(rows, cols) * (int64_t)sizeof(double);
+}
+
+namespace {
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+}  // namespace
+
+int hess_gptq_quantize(const float* W, int64_t rows, int64_t cols, int64_t ldw, const float* U, int64_t ldu,
+                       const uint8_t* dead, int group_size, float* Q, int64_t ldq, uint8_t* codes, int64_t ldc,
+                       float* scales, double* loss, int64_t nsamples, void* work, int64_t work_bytes,
+                       hess_stream_t stream) {
+  if (rows < 1 || rows > kQuantMaxDim || cols < 1 || cols > kQuantMaxDim)
+    return fail(HESS_EINVAL, "rows = %lld, cols = %lld outside [1, %lld]", (long long)rows, (long long)cols,
+                (long long)kQuantMaxDim);
+  if (!W || !U || !Q || !codes || !scales || !work) return fail(HESS_EINVAL, "null W, U, Q, codes, scales or workspace");
+  if (ldw < cols || ldu < cols || ldq < cols || ldc < cols) return fail(HESS_EINVAL, "row stride below cols");
+  if (!(group_size == -1 || (group_size >= 1 && (group_size >= cols || 128 % group_size == 0))))
+    return fail(HESS_EINVAL, "group_size %d: -1, >= cols, or a divisor of 128", group_size);
+  if (loss && nsamples < 1) return fail(HESS_EINVAL, "nsamples = %lld < 1", (long long)nsamples);
+  if ((reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Q) |
+       reinterpret_cast<uintptr_t>(scales)) & 3u)
+    return fail(HESS_EALIGN, "W, U, Q or scales not float-aligned");
+  if ((reinterpret_cast<uintptr_t>(work) & 15u) || (reinterpret_cast<uintptr_t>(loss) & 7u))
+    return fail(HESS_EALIGN, "workspace not 16-byte or loss not 8-byte aligned");
+  const int64_t need = hess_gptq_quantize_workspace(rows, cols);
+  if (work_bytes < need)
+    return fail(HESS_EINVAL, "workspace of %lld bytes, %lld needed", (long long)work_bytes, (long long)need);
+  const int groups = (group_size <= 0 || group_size >= cols) ? 1 : (int)((cols + group_size - 1) / group_size);
+  const int64_t wb = ((rows - 1) * ldw + cols) * 4, ub = ((cols - 1) * ldu + cols) * 4;
+  const int64_t qb = ((rows - 1) * ldq + cols) * 4, cb = (rows - 1) * ldc + cols, sb = rows * groups * 4;
+  // Q may be W itself (same stride: the working copy is taken first); nothing else may overlap
+  if (overlaps(Q, qb, W, wb) && !(static_cast<const void*>(Q) == static_cast<const void*>(W) && ldq == ldw))
+    return fail(HESS_EINVAL, "Q overlaps W without being W");
+  const void* outs[3] = {Q, codes, scales};
+  const int64_t outb[3] = {qb, cb, sb};
+  for (int a = 0; a < 3; ++a) {
+    if (overlaps(outs[a], outb[a], U, ub) || overlaps(outs[a], outb[a], work, need))
+      return fail(HESS_EINVAL, "an output overlaps U or the workspace");
+    for (int b = a + 1; b < 3; ++b)
+      if (overlaps(outs[a], outb[a], outs[b], outb[b])) return fail(HESS_EINVAL, "outputs overlap");
+  }
+  if (overlaps(work, need, W, wb) || overlaps(work, need, U, ub)) return fail(HESS_EINVAL, "workspace overlaps W or U");
+  QuantParams P{W, ldw, (int)rows, (int)cols, U, ldu, dead, group_size, Q, ldq, codes, ldc, scales, loss,
+                nsamples, static_cast<double*>(work)};
+  hipError_t e = launch_gptq_quantize(P, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HESS_OK : hip_fail(e, "block-quantize launch");
 }
 
 int hess_set_group_chunk(int64_t bytes) {

@@ -137,6 +137,28 @@ hipError_t launch_local_blocks(const void* X, int in_dtype, int64_t n, int d, in
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 
+// Error-propagating 4-bit quantization of W (rows x cols) with the factor U.
+struct QuantParams {
+  const float* W;
+  int64_t ldw;
+  int rows;
+  int cols;
+  const float* U;
+  int64_t ldu;
+  const uint8_t* dead;  // nullable: columns to zero first
+  int group;            // <= 0 or >= cols: whole rows; else a divisor of 128
+  float* Q;
+  int64_t ldq;
+  uint8_t* codes;
+  int64_t ldc;
+  float* scales;        // rows x groups
+  double* loss;         // nullable
+  int64_t nsamples;
+  double* work;         // quant_workspace_doubles(rows, cols)
+};
+int64_t quant_workspace_doubles(int64_t rows, int64_t cols);
+hipError_t launch_gptq_quantize(const QuantParams& P, hipStream_t stream);
+
 // Upper Cholesky factor of the inverse: U (d x d float32, row stride ldu,
 // zeros below the diagonal) with U^T U = H^-1, from the upper triangle of H
 // (row stride ldh).  A and X are chol_padded(d)^2 float64 each, P is

@@ -335,6 +335,43 @@ int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld,
                            const int32_t* row_idx, const int64_t* offsets, hess_stream_t stream);
 
 /*
+ * hess_gptq_quantize -- error-propagating 4-bit quantization of a weight
+ * matrix with the upper Cholesky factor of the inverse damped Hessian (the
+ * quantization pass's step 5: GPTQModel wiki "QQQ", Concepts > Quadratic
+ * error compensation; 128-column blocks).
+ *
+ * Column i of W is quantized, its error divided by U[i][i] and propagated
+ * into the columns not yet quantized through row i of U.  Quantizer (wiki
+ * "QQQ", Whole-row and grouped weight quantization): symmetric, step
+ * 2 max|w| / 15 per row (group_size -1) or per group of contiguous columns
+ * taken when the group is reached; code clip(rint(w / step) + 8, 0, 15);
+ * value step (code - 8).  Computed in float64 (inputs widened exactly).
+ *   W       device float32, rows x cols (outputs x inputs), row stride ldw.
+ *   U       device float32, cols x cols, row stride ldu: the factor from
+ *           hess_chol_inverse_upper (only its upper triangle is read).
+ *   dead    device bytes, cols, nullable: nonzero columns are zeroed first
+ *           (the weight side of dead-column neutralization).
+ *   group_size  -1 (whole rows), a divisor of 128, or >= cols (whole rows).
+ *   Q       device float32 out, dequantized weights, row stride ldq; may be W
+ *           itself (same stride).
+ *   codes   device uint8 out, rows x cols, row stride ldc, values 0..15.
+ *   scales  device float32 out, rows x groups (groups = 1 for whole rows).
+ *   loss    device double out, nullable: sum over columns and rows of the
+ *           squared error divided by U[i][i], over nsamples (wiki "QQQ",
+ *           Implementation internals > Quantizer API and results).
+ *   work    device workspace of hess_gptq_quantize_workspace(rows, cols)
+ *           bytes, 16-byte aligned, owned by the caller.
+ *   1 <= rows, cols <= 65536.  Errors: EINVAL (sizes, strides, group size,
+ *   null pointers, overlaps, small workspace), EALIGN, EHIP.  Enqueued on
+ *   stream; allocates nothing.
+ */
+int64_t hess_gptq_quantize_workspace(int64_t rows, int64_t cols); /* bytes, or -1 for bad sizes */
+int hess_gptq_quantize(const float* W, int64_t rows, int64_t cols, int64_t ldw, const float* U, int64_t ldu,
+                       const uint8_t* dead, int group_size, float* Q, int64_t ldq, uint8_t* codes, int64_t ldc,
+                       float* scales, double* loss, int64_t nsamples, void* work, int64_t work_bytes,
+                       hess_stream_t stream);
+
+/*
  * hess_chol_inverse_upper -- the upper Cholesky factor of the inverse of a
  * damped Hessian: U upper triangular with a positive diagonal and
  * U^T U = H^-1 (the quantization pass's step 4 after neutralization and

@@ -344,7 +344,7 @@ def quant_scale(x: np.ndarray, bits: int = 4) -> np.ndarray:
 
 
 def gptq_quantize(W: np.ndarray, U: np.ndarray, group_size: int = -1, bits: int = 4, dead=None,
-                  nsamples: int = 1):
+                  nsamples: int = 1, follow=None, tie_tol: float = 0.0):
     """Error-propagating quantization of W (rows = outputs, columns = inputs).
 
     U is the upper Cholesky factor of the inverse damped Hessian (only its
@@ -352,6 +352,14 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, group_size: int = -1, bits: int 
     dequantized weights (float64), codes uint8 in [0, 2^bits - 1], scales
     (rows, groups) float64 (one column for group_size -1), loss the summed
     squared scaled error over ``nsamples``.
+
+    Rounding ties: the largest magnitude of a group sits at 7.5 steps, so
+    ties between two codes are part of the method, and a run whose float64
+    additions come in another order may round such a tie the other way.  Both
+    codes are then correct.  With ``follow`` (a code array of the same shape)
+    the oracle takes follow's code wherever w / step lies within ``tie_tol``
+    (relative) of a half-integer and follow's code is one of its two
+    neighbours; everything else is decided as above.
     """
     W = np.array(W, dtype=np.float64)
     U = np.triu(np.asarray(U, dtype=np.float64))
@@ -373,7 +381,14 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, group_size: int = -1, bits: int 
             scale = quant_scale(W[:, i:i + g], bits)
             scales[:, i // g] = scale
         w = W[:, i].copy()
-        q = np.clip(np.rint(w / scale) + centre, 0, maxq)
+        x = w / scale
+        q = np.clip(np.rint(x) + centre, 0, maxq)
+        if follow is not None:
+            tie = np.abs(x - np.floor(x) - 0.5) <= tie_tol * np.maximum(1.0, np.abs(x))
+            lo = np.clip(np.floor(x) + centre, 0, maxq)
+            hi = np.clip(np.ceil(x) + centre, 0, maxq)
+            f = np.asarray(follow)[:, i].astype(np.float64)
+            q = np.where(tie & ((f == lo) | (f == hi)), f, q)
         deq = scale * (q - centre)
         err = (w - deq) / U[i, i]
         W[:, i + 1:] -= np.outer(err, U[i, i + 1:])

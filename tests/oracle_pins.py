@@ -458,6 +458,18 @@ def pin_gptq_quantize(O, seed=31):
         assert np.allclose(Q, Qr, rtol=1e-12, atol=1e-12)
         assert abs(loss * 7 - loss_r) <= 1e-10 * max(1.0, loss_r)
         assert scales.shape == (N, 1 if group == -1 else -(-K // group))
+    # following one's own codes at ties changes nothing; codes that are not a neighbour are ignored
+    Q2, codes2, _, _ = O.gptq_quantize(W, U, group_size=group, nsamples=7, follow=codes, tie_tol=1e-12)
+    assert np.array_equal(codes2, codes) and np.array_equal(Q2, Q)
+    Q3, codes3, _, _ = O.gptq_quantize(W, U, group_size=group, nsamples=7, follow=np.full_like(codes, 200),
+                                       tie_tol=1e-12)
+    assert np.array_equal(codes3, codes)
+    # an exact tie: w / step = -7.5 rounds to the even -8 (code 0); following code 1 is allowed there
+    row = np.array([[-3.75, 1.0]])
+    _, c_tie, _, _ = O.gptq_quantize(row, np.eye(2))
+    assert c_tie[0, 0] == 0
+    _, c_f, _, _ = O.gptq_quantize(row, np.eye(2), follow=np.array([[1, 0]]), tie_tol=1e-12)
+    assert c_f[0, 0] == 1
     # dead columns: zero weights, centre codes, no error to move
     W = rng.standard_normal((4, 8))
     X = rng.standard_normal((30, 8))

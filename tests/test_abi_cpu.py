@@ -83,3 +83,24 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(hs, "_LIB_PATH", "/nonexistent/libhess.so")
     with pytest.raises(RuntimeError, match="not built"):
         hs._load()
+
+
+def test_quantize_arguments_rejected_without_gpu():
+    lib = hs._load()
+    p = lambda a: ctypes.c_void_p(a)  # noqa: E731  (fake, never dereferenced)
+    base = 1 << 40
+    assert lib.hess_gptq_quantize_workspace(0, 5) == -1
+    need = lib.hess_gptq_quantize_workspace(10, 200)
+    assert need == (64 * 256 + 64 * 128 + 10 + 10 * 2) * 8
+
+    def call(group=-1, ldw=200, work_bytes=None, q=None, n=10):
+        return lib.hess_gptq_quantize(p(base), n, 200, ldw, p(base + (1 << 30)), 200, None, group,
+                                      p(q if q is not None else base + (2 << 30)), 200, p(base + (3 << 30)), 200,
+                                      p(base + (4 << 30)), None, 1, p(base + (5 << 30)),
+                                      need if work_bytes is None else work_bytes, None)
+    assert call(group=48) == -1 and b"group_size" in lib.hess_last_error()
+    assert call(group=0) == -1
+    assert call(ldw=199) == -1
+    assert call(work_bytes=need - 8) == -1 and b"workspace" in lib.hess_last_error()
+    assert call(q=base + 64) == -1 and b"overlaps" in lib.hess_last_error()
+    assert call(n=70000) == -1
