@@ -17,14 +17,15 @@
 // that is all zero takes max|w| = 1.
 //
 // Arithmetic.  float64 working weights (W widened exactly, dead columns
-// zeroed), U widened exactly; the code and error decisions use the same
-// float64 divisions as a plain column-by-column implementation, so the codes
-// match it except at rounding ties closer than the float64 reordering of the
-// updates.  Outputs: dequantized weights and step sizes rounded to float32,
+// zeroed), U widened exactly; the code and error take reciprocals of the
+// step and of U's diagonal, an ulp or so from the quotients, like the
+// float64 reordering of the updates: a code can differ from a plain
+// column-by-column implementation only at a rounding tie, where both codes
+// are correct.  Outputs: dequantized weights and step sizes rounded to float32,
 // codes as bytes, the loss sum_i sum_r (err_ri)^2 / nsamples in float64.
 //
-// Kernels per 128-column block: q_rows (one wave per weight row: the serial
-// walk through the block's columns, lanes holding two columns each) and
+// Kernels per 128-column block: q_rows (16 lanes per weight row: the serial
+// walk through the block's columns, lanes holding eight columns each) and
 // q_gemm (64 x 64 tiles of W right of the block, float64 matrix cores, the
 // block's errors as A and U's rows as B).
 
@@ -89,63 +90,147 @@ __global__ void __launch_bounds__(256) q_rowscale(const double* __restrict__ Wd,
   }
 }
 
-// The serial walk through block [i1, i1 + nb) for one row per wave.  Lane l
-// holds the row's columns i1 + l and i1 + 64 + l.  group: 0 = whole row
-// (steps in step[]), else the group size (a divisor of 128).
+// The serial walk through block [i1, i1 + nb): 16 rows per workgroup, 4 per
+// wave, 16 lanes per row; lane j of a row holds columns i1 + j + 16 k
+// (k < 8).  The block's slice of U is staged in LDS with only its strict
+// upper part kept (zeros on and below the diagonal) and the reciprocals of its
+// diagonal beside it, so every update is unconditional and a column's
+// register keeps, after its own step, exactly the value it was quantized
+// from.  Every lane of a row also carries the value of the column being
+// quantized (wn) and of the next one as of the previous step (wn2): step i
+// takes the code and error of wn, applies err_i to all held columns and to
+// wn2 (the same fused multiply-add the owner applies, so the copies equal the
+// owner's register bit for bit), and fetches column i + 2 from its owner by a
+// lane shuffle that is not needed until the next step's error is known, so
+// the shuffle latency stays off the serial chain.  Code q = clip(rint(w / s),
+// -8, 7) + 8 with w / s taken as w times the reciprocal step; error
+// (w - s (q - 8)) / U[i][i] taken as w d - (s d)(q - 8) with d the reciprocal
+// diagonal: within an ulp or so of the quotients, which can change a code only
+// at a rounding tie.  The codes, values and errors are taken again from the
+// kept values after the walk, with the same arithmetic, and written out then.
+// group: 0 = whole row (steps in step[]), else the group size (a divisor of
+// 128, so a power of two); a group's step comes from its columns' values when
+// it is reached.
+constexpr int kRowsPerWg = 16;
+constexpr int kUbLd = kQB + 4;  // LDS row stride of the staged slice (floats)
+
+__device__ __forceinline__ double shfl16_max(double v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ double shfl16_sum(double v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// signed code in [-8, 7] and the scaled error of one weight
+__device__ __forceinline__ double q_code(double w, double inv_s) { return fmin(fmax(rint(w * inv_s), -8.0), 7.0); }
+__device__ __forceinline__ double q_err(double w, double q, double d, double sd) { return fma(-sd, q, w * d); }
+
+// GC: the group size when known at compile time (0 = whole rows), or -1 to
+// take it from group_rt; FULL: the block has all 128 columns.
+template <int GC, bool FULL>
 __global__ void __launch_bounds__(256) q_rows(double* __restrict__ Wd, int ldd, int N, int K, int i1,
-                                              const float* __restrict__ U, int64_t ldu, int group,
+                                              const float* __restrict__ U, int64_t ldu, int group_rt,
                                               const double* __restrict__ step, float* __restrict__ scales,
                                               int ngroups, double* __restrict__ Err, float* __restrict__ Q,
                                               int64_t ldq, uint8_t* __restrict__ codes, int64_t ldc,
                                               double* __restrict__ lossp, int nblk) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (r >= N) return;
-  const int nb = min(kQB, K - i1);
-  const int c0 = lane, c1 = lane + 64;
-  double* wrow = Wd + (int64_t)r * ldd + i1;
-  double w0 = c0 < nb ? wrow[c0] : 0.0;
-  double w1 = c1 < nb ? wrow[c1] : 0.0;
-  double s = group ? 0.0 : step[r];
-  double q0 = 0.0, q1 = 0.0, d0 = 0.0, d1 = 0.0, e0 = 0.0, e1 = 0.0;
-  double loss = 0.0;
-  for (int i = 0; i < nb; ++i) {
-    if (group && i % group == 0) {
-      // the group's step from its current weights
-      double m = fmax((c0 >= i && c0 < i + group && c0 < nb) ? fabs(w0) : 0.0,
-                      (c1 >= i && c1 < i + group && c1 < nb) ? fabs(w1) : 0.0);
-      m = wave_max(m);
-      s = quant_step(m);
-      if (lane == 0) scales[(int64_t)r * ngroups + (i1 + i) / group] = (float)s;
+  __shared__ float Ub[kQB * kUbLd];
+  __shared__ double invd[kQB];
+  const int group = GC >= 0 ? GC : group_rt;
+  const int nb = FULL ? kQB : min(kQB, K - i1);
+  {
+    // all of a thread's loads in flight before its first store: thread t takes
+    // column t % 128 of rows t / 128 + 2 q (q < 64)
+    const int cc = threadIdx.x & (kQB - 1), r0 = threadIdx.x >> 7;
+    float v[kQB / 2];
+#pragma unroll
+    for (int q = 0; q < kQB / 2; ++q) {
+      const int rr = r0 + 2 * q;
+      v[q] = (cc > rr && cc < nb) ? U[(int64_t)(i1 + rr) * ldu + i1 + cc] : 0.0f;
     }
-    const int o = i & 63;
-    const double w = readlane_f64(i < 64 ? w0 : w1, o);
-    const double q = fmin(fmax(rint(w / s) + 8.0, 0.0), 15.0);
-    const double dq = s * (q - 8.0);
-    const double uii = (double)U[(int64_t)(i1 + i) * ldu + i1 + i];
-    const double err = (w - dq) / uii;
-    loss = fma(err, err, loss);
-    const float* urow = U + (int64_t)(i1 + i) * ldu + i1;
-    if (c0 > i && c0 < nb) w0 = fma(-err, (double)urow[c0], w0);
-    if (c1 > i && c1 < nb) w1 = fma(-err, (double)urow[c1], w1);
-    const bool mine0 = i < 64 && lane == o, mine1 = i >= 64 && lane == o;
-    q0 = mine0 ? q : q0;
-    d0 = mine0 ? dq : d0;
-    e0 = mine0 ? err : e0;
-    q1 = mine1 ? q : q1;
-    d1 = mine1 ? dq : d1;
-    e1 = mine1 ? err : e1;
+#pragma unroll
+    for (int q = 0; q < kQB / 2; ++q) Ub[(r0 + 2 * q) * kUbLd + cc] = v[q];
   }
-  if (c0 < nb) {
-    Q[(int64_t)r * ldq + i1 + c0] = (float)d0;
-    codes[(int64_t)r * ldc + i1 + c0] = (uint8_t)q0;
+  if (threadIdx.x < kQB)
+    invd[threadIdx.x] = threadIdx.x < nb ? 1.0 / (double)U[(int64_t)(i1 + threadIdx.x) * ldu + i1 + threadIdx.x] : 0.0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, j = lane & 15;
+  const int slot = (threadIdx.x >> 6) * 4 + (lane >> 4);  // row slot in the workgroup
+  const int r = blockIdx.x * kRowsPerWg + slot;
+  const bool live = r < N;
+  const int base = lane & 48;
+  double wr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c = j + 16 * k;
+    wr[k] = (live && c < nb) ? Wd[(int64_t)r * ldd + i1 + c] : 0.0;
   }
-  if (c1 < nb) {
-    Q[(int64_t)r * ldq + i1 + c1] = (float)d1;
-    codes[(int64_t)r * ldc + i1 + c1] = (uint8_t)q1;
+  double s = (!group && live) ? step[r] : 1.0;
+  double inv_s = 1.0 / s;
+  double sk[8];  // the step of each held column's group
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sk[k] = s;
+  double wn = __shfl(wr[0], base | 0);   // column 0
+  double wn2 = __shfl(wr[0], base | 1);  // column 1
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = 16 * m + u;
+      if (i >= nb) continue;
+      if (group && (i & (group - 1)) == 0) {
+        // the group's step from its columns' current values
+        double a = 0.0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int c = j + 16 * k;
+          a = fmax(a, (c >= i && c < i + group && c < nb) ? fabs(wr[k]) : 0.0);
+        }
+        a = shfl16_max(a);
+        s = quant_step(a);
+        inv_s = 1.0 / s;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int c = j + 16 * k;
+          sk[k] = (c >= i && c < i + group) ? s : sk[k];
+        }
+        if (j == 0 && live) scales[(int64_t)r * ngroups + (i1 + i) / group] = (float)s;
+      }
+      const double d = invd[i];
+      const double err = q_err(wn, q_code(wn, inv_s), d, s * d);
+      const float* urow = Ub + i * kUbLd;
+      const double wnext = fma(-err, (double)urow[i + 1 < kQB ? i + 1 : i], wn2);
+#pragma unroll
+      for (int k = m; k < 8; ++k) wr[k] = fma(-err, (double)urow[j + 16 * k], wr[k]);
+      if (i + 2 < kQB) wn2 = __shfl(wr[(i + 2) >> 4], base | ((i + 2) & 15));
+      wn = wnext;
+    }
   }
-  Err[(int64_t)r * kQB + c0] = c0 < nb ? e0 : 0.0;
-  Err[(int64_t)r * kQB + c1] = c1 < nb ? e1 : 0.0;
-  if (lane == 0) lossp[(int64_t)r * nblk + i1 / kQB] = loss;
+  // codes, values and errors from the kept values, as in the walk
+  double loss = 0.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c = j + 16 * k;
+    double e = 0.0;
+    if (c < nb) {
+      const double sc = sk[k], w = wr[k], d = invd[c];
+      const double q = q_code(w, 1.0 / sc);
+      e = q_err(w, q, d, sc * d);
+      loss = fma(e, e, loss);
+      if (live) {
+        Q[(int64_t)r * ldq + i1 + c] = (float)(sc * q);
+        codes[(int64_t)r * ldc + i1 + c] = (uint8_t)(q + 8.0);
+      }
+    }
+    if (live) Err[(int64_t)r * kQB + c] = e;
+  }
+  loss = shfl16_sum(loss);
+  if (j == 0 && live) lossp[(int64_t)r * nblk + i1 / kQB] = loss;
 }
 
 // Wd[:, i2 + 64 tc .. ] -= Err (rowsP x 128) U[i1 .. i1 + 128, i2 + ..]: one
@@ -195,15 +280,24 @@ __global__ void __launch_bounds__(256) q_gemm(double* __restrict__ Wd, int ldd, 
 }
 
 // loss = sum of the per-row, per-block partials in a fixed order / nsamples.
-__global__ void __launch_bounds__(256) q_loss(const double* __restrict__ lossp, int64_t n, double inv_n,
-                                              double* __restrict__ loss) {
-  __shared__ double part[4];
-  double v = 0.0;
-  for (int64_t i = threadIdx.x; i < n; i += 256) v += lossp[i];
-  v = wave_sum(v);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+__global__ void __launch_bounds__(1024) q_loss(const double* __restrict__ lossp, int64_t n, double inv_n,
+                                               double* __restrict__ loss) {
+  __shared__ double part[16];
+  double v[4] = {0.0, 0.0, 0.0, 0.0};
+  int64_t i = threadIdx.x;
+  for (; i + 3 * 1024 < n; i += 4 * 1024) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] += lossp[i + u * 1024];
+  }
+  for (; i < n; i += 1024) v[0] += lossp[i];
+  double t = wave_sum((v[0] + v[1]) + (v[2] + v[3]));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = t;
   __syncthreads();
-  if (threadIdx.x == 0) *loss = ((part[0] + part[1]) + (part[2] + part[3])) * inv_n;
+  if (threadIdx.x == 0) {
+    double a = 0.0;
+    for (int w = 0; w < 16; ++w) a += part[w];
+    *loss = a * inv_n;
+  }
 }
 
 }  // namespace
@@ -230,8 +324,20 @@ hipError_t launch_gptq_quantize(const QuantParams& P, hipStream_t s) {
   if (!group) hipLaunchKernelGGL(q_rowscale, dim3((N + 3) / 4), dim3(256), 0, s, Wd, ldd, N, K, step, P.scales);
   for (int b = 0; b < nblk; ++b) {
     const int i1 = b * kQB, i2 = i1 + kQB;
-    hipLaunchKernelGGL(q_rows, dim3((N + 3) / 4), dim3(256), 0, s, Wd, ldd, N, K, i1, P.U, P.ldu, group, step,
-                       P.scales, ngroups, Err, P.Q, P.ldq, P.codes, P.ldc, lossp, nblk);
+    const bool full = i2 <= K;
+    auto rows_kernel = [&]() -> void (*)(double*, int, int, int, int, const float*, int64_t, int, const double*,
+                                         float*, int, double*, float*, int64_t, uint8_t*, int64_t, double*, int) {
+      if (!full) return q_rows<-1, false>;
+      switch (group) {
+        case 0: return q_rows<0, true>;
+        case 32: return q_rows<32, true>;
+        case 64: return q_rows<64, true>;
+        case 128: return q_rows<128, true>;
+        default: return q_rows<-1, true>;
+      }
+    };
+    hipLaunchKernelGGL(rows_kernel(), dim3((N + kRowsPerWg - 1) / kRowsPerWg), dim3(256), 0, s, Wd, ldd, N, K, i1,
+                       P.U, P.ldu, group, step, P.scales, ngroups, Err, P.Q, P.ldq, P.codes, P.ldc, lossp, nblk);
     if (i2 < K) {
       const int ntc = (ldd - i2 + kQT - 1) / kQT;
       const int64_t tiles = (int64_t)(rp / kQT) * ntc;
@@ -239,7 +345,7 @@ hipError_t launch_gptq_quantize(const QuantParams& P, hipStream_t s) {
     }
   }
   if (P.loss)
-    hipLaunchKernelGGL(q_loss, dim3(1), dim3(256), 0, s, lossp, (int64_t)N * nblk, 1.0 / (double)P.nsamples, P.loss);
+    hipLaunchKernelGGL(q_loss, dim3(1), dim3(1024), 0, s, lossp, (int64_t)N * nblk, 1.0 / (double)P.nsamples, P.loss);
   return hipGetLastError();
 }
 
