@@ -39,7 +39,7 @@ namespace {
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQB = 128;  // columns per block
-constexpr int kQT = 64;   // product tile edge
+constexpr int kQT = 64;   // row padding: the product's tile edge
 
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
@@ -136,7 +136,7 @@ template <int GC, bool FULL>
 __global__ void __launch_bounds__(256) q_rows(double* __restrict__ Wd, int ldd, int N, int K, int i1,
                                               const float* __restrict__ U, int64_t ldu, int group_rt,
                                               const double* __restrict__ step, float* __restrict__ scales,
-                                              int ngroups, double* __restrict__ Err, float* __restrict__ Q,
+                                              int ngroups, double* __restrict__ Err, int lde, float* __restrict__ Q,
                                               int64_t ldq, uint8_t* __restrict__ codes, int64_t ldc,
                                               double* __restrict__ lossp, int nblk) {
   __shared__ float Ub[kQB * kUbLd];
@@ -227,54 +227,56 @@ __global__ void __launch_bounds__(256) q_rows(double* __restrict__ Wd, int ldd, 
         codes[(int64_t)r * ldc + i1 + c] = (uint8_t)(q + 8.0);
       }
     }
-    if (live) Err[(int64_t)r * kQB + c] = e;
+    if (live) Err[(int64_t)r * lde + c] = e;
   }
   loss = shfl16_sum(loss);
   if (j == 0 && live) lossp[(int64_t)r * nblk + i1 / kQB] = loss;
 }
 
-// Wd[:, i2 + 64 tc .. ] -= Err (rowsP x 128) U[i1 .. i1 + 128, i2 + ..]: one
-// 64 x 64 tile per workgroup (rows 64 tr, columns i2 + 64 tc); wave w computes
-// rows 32 (w >> 1) .. +31 and columns 32 (w & 1) .. +31 as 2 x 2 blocks of
-// 16 x 16 (v_mfma_f64_16x16x4_f64: lane l supplies A[l%16][l/16] and
-// B[l/16][l%16]; register j of lane l holds D[l/16 + 4 j][l%16]).
-__global__ void __launch_bounds__(256) q_gemm(double* __restrict__ Wd, int ldd, int K, int i1, int i2, int ntc,
-                                              const float* __restrict__ U, int64_t ldu,
-                                              const double* __restrict__ Err) {
+// Wd[:, c] -= sum_k E[r][k] U[u0 + k][c] for the columns c_begin .. (ntc
+// tiles), k < kdim: one (32 WB) x (32 WB) tile per workgroup; wave w
+// computes rows 16 WB (w >> 1) .. and columns 16 WB (w & 1) .. of it as
+// WB x WB blocks of 16 x 16 (v_mfma_f64_16x16x4_f64: lane l supplies
+// A[l%16][l/16] and B[l/16][l%16]; register j of lane l holds
+// D[l/16 + 4 j][l%16]).  Rows of U at or past K read as zero.
+template <int WB>
+__global__ void __launch_bounds__(256) q_gemm(double* __restrict__ Wd, int ldd, int c_begin, int ntc,
+                                              const double* __restrict__ E, int lde, int kdim,
+                                              const float* __restrict__ U, int64_t ldu, int u0, int K) {
+  constexpr int TW = 16 * WB, TT = 2 * TW;
   const int tr = blockIdx.x / ntc, tc = blockIdx.x - tr * ntc;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int li = lane & 15, lk = lane >> 4;
-  const int row0 = kQT * tr + 32 * (w >> 1);
-  const int col0 = i2 + kQT * tc + 32 * (w & 1);
-  f64x4 acc[2][2];
+  const int row0 = TT * tr + TW * (w >> 1);
+  const int col0 = c_begin + TT * tc + TW * (w & 1);
+  f64x4 acc[WB][WB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < WB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < WB; ++cb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[rb][cb][j] = Wd[(int64_t)(row0 + 16 * rb + lk + 4 * j) * ldd + col0 + 16 * cb + li];
-  const int kmax = min(kQB, K - i1);
-#pragma unroll 4
-  for (int kk = 0; kk < kQB; kk += 4) {
-    double a[2], b[2];
+#pragma unroll 2
+  for (int kk = 0; kk < kdim; kk += 4) {
+    double a[WB], b[WB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) a[rb] = -Err[(int64_t)(row0 + 16 * rb + li) * kQB + kk + lk];
-    const int ur = kk + lk;
+    for (int rb = 0; rb < WB; ++rb) a[rb] = -E[(int64_t)(row0 + 16 * rb + li) * lde + kk + lk];
+    const int ur = u0 + kk + lk;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < WB; ++cb) {
       const int col = col0 + 16 * cb + li;
-      b[cb] = (ur < kmax && col < K) ? (double)U[(int64_t)(i1 + ur) * ldu + col] : 0.0;
+      b[cb] = (ur < K && col < K) ? (double)U[(int64_t)ur * ldu + col] : 0.0;
     }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < WB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < WB; ++cb)
         acc[rb][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
   }
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < WB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < WB; ++cb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) Wd[(int64_t)(row0 + 16 * rb + lk + 4 * j) * ldd + col0 + 16 * cb + li] = acc[rb][cb][j];
 }
@@ -310,23 +312,26 @@ int64_t quant_workspace_doubles(int64_t n, int64_t k) {
   return rp * ldd + rp * kQB + n + n * (ldd / kQB);
 }
 
+// After each 128-column block's walk, its errors reach every column to its
+// right through one product (k = 128, 64 x 64 tiles).
 hipError_t launch_gptq_quantize(const QuantParams& P, hipStream_t s) {
   const int N = P.rows, K = P.cols;
   const int rp = (int)quant_rows_padded(N), ldd = (int)quant_cols_padded(K);
   const int nblk = ldd / kQB;
   double* Wd = P.work;
-  double* Err = Wd + (int64_t)rp * ldd;
-  double* step = Err + (int64_t)rp * kQB;
+  double* E = Wd + (int64_t)rp * ldd;
+  double* step = E + (int64_t)rp * kQB;
   double* lossp = step + N;
   const int group = (P.group <= 0 || P.group >= K) ? 0 : P.group;
   const int ngroups = group ? (K + group - 1) / group : 1;
-  hipLaunchKernelGGL(q_load, dim3(rp), dim3(256), 0, s, P.W, P.ldw, N, K, P.dead, Wd, ldd, Err);
+  hipLaunchKernelGGL(q_load, dim3(rp), dim3(256), 0, s, P.W, P.ldw, N, K, P.dead, Wd, ldd, E);
   if (!group) hipLaunchKernelGGL(q_rowscale, dim3((N + 3) / 4), dim3(256), 0, s, Wd, ldd, N, K, step, P.scales);
-  for (int b = 0; b < nblk; ++b) {
-    const int i1 = b * kQB, i2 = i1 + kQB;
+  for (int i1 = 0; i1 < K; i1 += kQB) {
+    const int i2 = i1 + kQB;
     const bool full = i2 <= K;
     auto rows_kernel = [&]() -> void (*)(double*, int, int, int, int, const float*, int64_t, int, const double*,
-                                         float*, int, double*, float*, int64_t, uint8_t*, int64_t, double*, int) {
+                                         float*, int, double*, int, float*, int64_t, uint8_t*, int64_t, double*,
+                                         int) {
       if (!full) return q_rows<-1, false>;
       switch (group) {
         case 0: return q_rows<0, true>;
@@ -337,11 +342,11 @@ hipError_t launch_gptq_quantize(const QuantParams& P, hipStream_t s) {
       }
     };
     hipLaunchKernelGGL(rows_kernel(), dim3((N + kRowsPerWg - 1) / kRowsPerWg), dim3(256), 0, s, Wd, ldd, N, K, i1,
-                       P.U, P.ldu, group, step, P.scales, ngroups, Err, P.Q, P.ldq, P.codes, P.ldc, lossp, nblk);
+                       P.U, P.ldu, group, step, P.scales, ngroups, E, kQB, P.Q, P.ldq, P.codes, P.ldc, lossp, nblk);
     if (i2 < K) {
-      const int ntc = (ldd - i2 + kQT - 1) / kQT;
-      const int64_t tiles = (int64_t)(rp / kQT) * ntc;
-      hipLaunchKernelGGL(q_gemm, dim3((unsigned)tiles), dim3(256), 0, s, Wd, ldd, K, i1, i2, ntc, P.U, P.ldu, Err);
+      const int ntc = (ldd - i2) / 64;
+      hipLaunchKernelGGL(q_gemm<2>, dim3((unsigned)((rp / 64) * ntc)), dim3(256), 0, s, Wd, ldd, i2, ntc, E, kQB,
+                         kQB, P.U, P.ldu, i1, K);
     }
   }
   if (P.loss)
