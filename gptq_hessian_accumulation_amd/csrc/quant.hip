@@ -26,8 +26,8 @@
 //
 // Kernels per 128-column block: q_rows (16 lanes per weight row: the serial
 // walk through the block's columns, lanes holding eight columns each) and
-// q_gemm (64 x 64 tiles of W right of the block, float64 matrix cores, the
-// block's errors as A and U's rows as B).
+// q_gemm_lds (128 x 128 tiles of W right of the block, float64 matrix cores,
+// the block's errors as A and U's rows as B, both staged through LDS).
 
 #include "hess_device.hpp"
 #include "hess_internal.hpp"
@@ -39,7 +39,7 @@ namespace {
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQB = 128;  // columns per block
-constexpr int kQT = 64;   // row padding: the product's tile edge
+constexpr int kQT = 128;  // row padding: the product's tile edge
 
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
@@ -233,52 +233,97 @@ __global__ void __launch_bounds__(256) q_rows(double* __restrict__ Wd, int ldd, 
   if (j == 0 && live) lossp[(int64_t)r * nblk + i1 / kQB] = loss;
 }
 
-// Wd[:, c] -= sum_k E[r][k] U[u0 + k][c] for the columns c_begin .. (ntc
-// tiles), k < kdim: one (32 WB) x (32 WB) tile per workgroup; wave w
-// computes rows 16 WB (w >> 1) .. and columns 16 WB (w & 1) .. of it as
-// WB x WB blocks of 16 x 16 (v_mfma_f64_16x16x4_f64: lane l supplies
-// A[l%16][l/16] and B[l/16][l%16]; register j of lane l holds
-// D[l/16 + 4 j][l%16]).  Rows of U at or past K read as zero.
-template <int WB>
-__global__ void __launch_bounds__(256) q_gemm(double* __restrict__ Wd, int ldd, int c_begin, int ntc,
-                                              const double* __restrict__ E, int lde, int kdim,
-                                              const float* __restrict__ U, int64_t ldu, int u0, int K) {
-  constexpr int TW = 16 * WB, TT = 2 * TW;
+// Wd[rows, c_begin + ...] -= E (rows x 128) U[u0 .. u0 + 128, c_begin + ...]
+// with operands staged through LDS: one 128 x 128 tile of W per workgroup,
+// four waves of 64 x 64 (4 x 4 blocks of 16 x 16 on the float64 matrix
+// instruction, accumulators held for the whole k range).  k runs in chunks of
+// 16, double-buffered: the next chunk's global loads are issued before the
+// current chunk's products, and stored to the other LDS buffer after them.
+// E's chunk is 128 rows x 16 k (row-major, padded); U's is 16 rows x 128
+// columns, widened from float32 as it is stored.  Rows of U at or past K, and
+// columns past K, read as zero.
+constexpr int kGT = 128;          // tile edge
+constexpr int kGK = 16;           // k per chunk
+constexpr int kEL = kGK + 2;      // LDS row stride of the E chunk (doubles)
+constexpr int kUL = kGT + 2;      // LDS row stride of the U chunk (doubles)
+
+__global__ void __launch_bounds__(256) q_gemm_lds(double* __restrict__ Wd, int ldd, int c_begin, int ntc,
+                                                  const double* __restrict__ E, const float* __restrict__ U,
+                                                  int64_t ldu, int u0, int K) {
+  __shared__ __attribute__((aligned(16))) double Es[2][kGT * kEL];
+  __shared__ __attribute__((aligned(16))) double Us[2][kGK * kUL];
   const int tr = blockIdx.x / ntc, tc = blockIdx.x - tr * ntc;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int li = lane & 15, lk = lane >> 4;
-  const int row0 = TT * tr + TW * (w >> 1);
-  const int col0 = c_begin + TT * tc + TW * (w & 1);
-  f64x4 acc[WB][WB];
+  const int R0 = kGT * tr, C0 = c_begin + kGT * tc;
+  const int wr = 64 * (w >> 1), wc = 64 * (w & 1);
+  // global -> register loads of one chunk: E rows t / 2 (two threads per row, 8 k each),
+  // U rows t / 16 (16 threads per row, 8 columns each)
+  const int er = t >> 1, ek = (t & 1) * 8;
+  const int ur = t >> 4, uc = (t & 15) * 8;
+  f64x4 ev[2];          // 8 doubles of E
+  float uv[8];
+  auto load = [&](int kc) {
+    const double* src = E + (int64_t)(R0 + er) * kQB + kc + ek;
 #pragma unroll
-  for (int rb = 0; rb < WB; ++rb)
+    for (int q = 0; q < 2; ++q) ev[q] = *reinterpret_cast<const f64x4*>(src + 4 * q);
+    const int urow = u0 + kc + ur;
 #pragma unroll
-    for (int cb = 0; cb < WB; ++cb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[rb][cb][j] = Wd[(int64_t)(row0 + 16 * rb + lk + 4 * j) * ldd + col0 + 16 * cb + li];
-#pragma unroll 2
-  for (int kk = 0; kk < kdim; kk += 4) {
-    double a[WB], b[WB];
-#pragma unroll
-    for (int rb = 0; rb < WB; ++rb) a[rb] = -E[(int64_t)(row0 + 16 * rb + li) * lde + kk + lk];
-    const int ur = u0 + kk + lk;
-#pragma unroll
-    for (int cb = 0; cb < WB; ++cb) {
-      const int col = col0 + 16 * cb + li;
-      b[cb] = (ur < K && col < K) ? (double)U[(int64_t)ur * ldu + col] : 0.0;
+    for (int q = 0; q < 8; ++q) {
+      const int col = C0 + uc + q;
+      uv[q] = (urow < K && col < K) ? U[(int64_t)urow * ldu + col] : 0.0f;
     }
+  };
+  auto store = [&](int buf) {
+    double* e = Es[buf] + er * kEL + ek;
 #pragma unroll
-    for (int rb = 0; rb < WB; ++rb)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int cb = 0; cb < WB; ++cb)
-        acc[rb][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
+      for (int z = 0; z < 4; ++z) e[4 * q + z] = ev[q][z];
+    double* u = Us[buf] + ur * kUL + uc;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) u[q] = (double)uv[q];
+  };
+  f64x4 acc[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[rb][cb][j] = Wd[(int64_t)(R0 + wr + 16 * rb + lk + 4 * j) * ldd + C0 + wc + 16 * cb + li];
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kc = 0; kc < kQB; kc += kGK) {
+    const int buf = (kc / kGK) & 1;
+    const bool more = kc + kGK < kQB;
+    if (more) load(kc + kGK);
+    const double* Eb = Es[buf];
+    const double* Ubf = Us[buf];
+#pragma unroll
+    for (int kk = 0; kk < kGK; kk += 4) {
+      double a[4], b[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) a[rb] = -Eb[(wr + 16 * rb + li) * kEL + kk + lk];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) b[cb] = Ubf[(kk + lk) * kUL + wc + 16 * cb + li];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
   }
 #pragma unroll
-  for (int rb = 0; rb < WB; ++rb)
+  for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < WB; ++cb)
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Wd[(int64_t)(row0 + 16 * rb + lk + 4 * j) * ldd + col0 + 16 * cb + li] = acc[rb][cb][j];
+      for (int j = 0; j < 4; ++j)
+        Wd[(int64_t)(R0 + wr + 16 * rb + lk + 4 * j) * ldd + C0 + wc + 16 * cb + li] = acc[rb][cb][j];
 }
 
 // loss = sum of the per-row, per-block partials in a fixed order / nsamples.
@@ -313,7 +358,7 @@ int64_t quant_workspace_doubles(int64_t n, int64_t k) {
 }
 
 // After each 128-column block's walk, its errors reach every column to its
-// right through one product (k = 128, 64 x 64 tiles).
+// right through one product (k = 128, 128 x 128 tiles staged through LDS).
 hipError_t launch_gptq_quantize(const QuantParams& P, hipStream_t s) {
   const int N = P.rows, K = P.cols;
   const int rp = (int)quant_rows_padded(N), ldd = (int)quant_cols_padded(K);
@@ -344,9 +389,9 @@ hipError_t launch_gptq_quantize(const QuantParams& P, hipStream_t s) {
     hipLaunchKernelGGL(rows_kernel(), dim3((N + kRowsPerWg - 1) / kRowsPerWg), dim3(256), 0, s, Wd, ldd, N, K, i1,
                        P.U, P.ldu, group, step, P.scales, ngroups, E, kQB, P.Q, P.ldq, P.codes, P.ldc, lossp, nblk);
     if (i2 < K) {
-      const int ntc = (ldd - i2) / 64;
-      hipLaunchKernelGGL(q_gemm<2>, dim3((unsigned)((rp / 64) * ntc)), dim3(256), 0, s, Wd, ldd, i2, ntc, E, kQB,
-                         kQB, P.U, P.ldu, i1, K);
+      const int ntc = (ldd - i2) / kGT;
+      hipLaunchKernelGGL(q_gemm_lds, dim3((unsigned)((rp / kGT) * ntc)), dim3(256), 0, s, Wd, ldd, i2, ntc, E, P.U,
+                         P.ldu, i1, K);
     }
   }
   if (P.loss)

@@ -91,7 +91,7 @@ def test_quantize_arguments_rejected_without_gpu():
     base = 1 << 40
     assert lib.hess_gptq_quantize_workspace(0, 5) == -1
     need = lib.hess_gptq_quantize_workspace(10, 200)
-    assert need == (64 * 256 + 64 * 128 + 10 + 10 * 2) * 8
+    assert need == (128 * 256 + 128 * 128 + 10 + 10 * 2) * 8
 
     def call(group=-1, ldw=200, work_bytes=None, q=None, n=10):
         return lib.hess_gptq_quantize(p(base), n, 200, ldw, p(base + (1 << 30)), 200, None, group,
