@@ -183,8 +183,9 @@ __global__ void __launch_bounds__(256) chol_load(const float* __restrict__ H, in
 // j takes, from LDS, the column of T as it stands after steps 0 .. j-1
 // (colv[r] = T[r][j] for r >= j, zero above), the row Y[j][.] (rowv; zero
 // past j) and the pivot's square root l and reciprocal, all published by
-// their owners during step j-1, so each step needs one barrier.  Column j of
-// L (colv / l) goes straight to memory; the rank-one updates
+// their owners during step j-1, so each step needs one barrier and issues all
+// its LDS reads at once.  Column j of L (colv / l) is kept in LDS and written
+// out with the tile at the end; the rank-one updates
 // T[i][c] -= L[i][j] L[c][j] and Y[i][c] -= L[i][j] Y[j][c] / l are applied
 // to every owned entry without tests: the zeros in colv and rowv leave the
 // finished columns and the zero upper part of Y alone, and the entries of T
@@ -200,25 +201,24 @@ struct DiagLds {
   double colv[2][2 * kCB];  // entries past kCB stay zero (reads for shifted-out registers)
   double rowv[2][kCB];
   double pv[2][2];
+  double Lt[kCB * (kCB + 1)];  // the finished columns of L, written out at the end
 };
 
 // Square root and reciprocal square root of a pivot: the hardware estimate of
-// 1 / sqrt(p) refined by two Newton steps y <- y + y (1 - p y^2) / 2, then
-// l = p y with one correction l <- l + y (p - l^2) / 2: a short dependent
-// chain, accurate to a few float64 ulps (the result is rounded to float32).
-// A pivot that is not positive becomes NaN and is reported in *info.
-__device__ __forceinline__ void diag_pivot(double p, int col, int d, int* info, double* pv) {
-  if (!(p > 0.0)) {
-    if (info && col < d) atomicMax(info, d - col);
-    p = __builtin_nan("");
-  }
-  double y = __builtin_amdgcn_rsq(p);
+// 1 / sqrt(p) refined by one Newton step y <- y + y (1 - p y^2) / 2 (the
+// estimate's relative error squared, far below the float32 rounding of the
+// result), and l = p y.  A pivot that is not positive becomes NaN.  Every
+// thread evaluates it on its own candidate, without a branch, so that the
+// chain overlaps the thread's other updates; only the owner publishes it.
+__device__ __forceinline__ void pivot_root(double p, double& l, double& y) {
+  p = p > 0.0 ? p : __builtin_nan("");
+  y = __builtin_amdgcn_rsq(p);
   y = fma(0.5 * y, fma(-p * y, y, 1.0), y);
-  y = fma(0.5 * y, fma(-p * y, y, 1.0), y);
-  double l = p * y;
-  l = fma(0.5 * y, fma(-l, l, p), l);
-  pv[0] = l;
-  pv[1] = y;
+  l = p * y;
+}
+
+__device__ __forceinline__ void report_pivot(double p, int col, int d, int* info) {
+  if (!(p > 0.0) && info && col < d) atomicMax(info, d - col);
 }
 
 // The tile to factor is read from src (row stride lds: global memory, or the
@@ -249,7 +249,10 @@ __device__ __forceinline__ void diag_body(const double* src, int64_t lds, double
   if (i == 0) {
 #pragma unroll
     for (int m = 0; m < kPer; ++m) rowv[0][cls + kTPR * m] = Y[m];
-    if (cls == 0) diag_pivot(T[0], k * kCB, d, info, pv[0]);
+    if (cls == 0) {
+      report_pivot(T[0], k * kCB, d, info);
+      pivot_root(T[0], pv[0][0], pv[0][1]);
+    }
   }
   __syncthreads();
   for (int jb = 0; jb < kCB; jb += kTPR) {
@@ -258,29 +261,42 @@ __device__ __forceinline__ void diag_body(const double* src, int64_t lds, double
     for (int u = 0; u < kTPR; ++u) {
       const int j = jb + u;
       const int b = u & 1, nb = b ^ 1;
+      // every read of the step at once: one LDS latency
       const double l = pv[b][0], inv = pv[b][1];
-      const double lij = i > j ? colv[b][i] * inv : 0.0;
-      if (cls == u && i >= j) Ag[(int64_t)i * dp + j] = i == j ? l : lij;  // column j of L
+      const double ci = colv[b][i];
+      double cv[kPer], rv[kPer];
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        cv[m] = colv[b][cb + kTPR * m];
+        rv[m] = rowv[b][cls + kTPR * m];
+      }
+      const double lij = i > j ? ci * inv : 0.0;
       const double f = lij * inv;
 #pragma unroll
       for (int m = 0; m < kPer; ++m) {
-        T[m] = fma(-f, colv[b][cb + kTPR * m], T[m]);
-        Y[m] = fma(-f, rowv[b][cls + kTPR * m], Y[m]);
+        T[m] = fma(-f, cv[m], T[m]);
+        Y[m] = fma(-f, rv[m], Y[m]);
       }
-      if (i == j) {
+      const double ys = i == j ? inv : 1.0;  // row j of L^-1
 #pragma unroll
-        for (int m = 0; m < kPer; ++m) Y[m] *= inv;  // row j of L^-1
-      }
+      for (int m = 0; m < kPer; ++m) Y[m] *= ys;
+      if (cls == u && i >= j) S.Lt[i * (kCB + 1) + j] = i == j ? l : lij;  // column j of L
       const int c1 = j + 1;
       if (c1 < kCB) {
         // column c1 is T[0] of owner cls = u + 1, or T[1] of cls = 0 after the block's last step
         const bool owner = cls == (u + 1) % kTPR;
         const double next = (u + 1 < kTPR) ? T[0] : T[1];
+        double nl, ny;
+        pivot_root(next, nl, ny);
         if (owner) colv[nb][i] = i >= c1 ? next : 0.0;
         if (i == c1) {
 #pragma unroll
           for (int m = 0; m < kPer; ++m) rowv[nb][cls + kTPR * m] = Y[m];
-          if (owner) diag_pivot(next, k * kCB + c1, d, info, pv[nb]);
+          if (owner) {
+            report_pivot(next, k * kCB + c1, d, info);
+            pv[nb][0] = nl;
+            pv[nb][1] = ny;
+          }
         }
       }
       __syncthreads();
@@ -290,7 +306,11 @@ __device__ __forceinline__ void diag_body(const double* src, int64_t lds, double
     T[kPer - 1] = 0.0;
   }
 #pragma unroll
-  for (int m = 0; m < kPer; ++m) Xg[(int64_t)i * dp + cls + kTPR * m] = Y[m];
+  for (int m = 0; m < kPer; ++m) {
+    const int c = cls + kTPR * m;
+    Xg[(int64_t)i * dp + c] = Y[m];
+    Ag[(int64_t)i * dp + c] = c <= i ? S.Lt[i * (kCB + 1) + c] : 0.0;
+  }
 }
 
 __global__ void __launch_bounds__(kCB * kTPR) chol_diag(double* __restrict__ A, double* __restrict__ X, int dp, int k,
