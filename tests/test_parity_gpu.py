@@ -864,3 +864,43 @@ def test_cast_errors_and_adopt_settings():
     assert e.nsamples == 4
     for hh in (h0, a, b, c, e):
         hh.close()
+
+
+def test_new_entry_points_on_a_side_stream():
+    """Cast, adopt, the imatrix statistic, the Cholesky factor and the block quantize all run on a
+    non-default stream with their inputs produced on that stream, and agree with the oracle."""
+    _say("side stream: cast / adopt / imatrix / chol / quantize")
+    side = torch.cuda.Stream()
+    d = 264
+    rng = np.random.default_rng(77)
+    x16 = W.encode(W.normal_rows(rng, 900, d, W.column_scales(rng, d)), W.F16)
+    with torch.cuda.stream(side):
+        xd = torch.from_numpy(x16).to("cuda", non_blocking=False)
+        xd = xd * 1.0                     # produced on the side stream
+        h = hs.Hessian(d, torch.bfloat16)
+        h.add_batch(xd, stream=side)
+        f = hs.Hessian(d, torch.bfloat16)
+        f.adopt_from(h, stream=side)
+        m = hs.ImatrixStat(d, torch.bfloat16)
+        m.add_batch(xd.to(torch.bfloat16), stream=side)
+        H, dead, _ = f.materialize(0.01, stream=side)
+        U = hs.chol_inverse_upper(H, stream=side)
+        Wt = torch.randn((40, d), device="cuda", dtype=torch.float32) * 0.02
+        Q, codes, _, _ = hs.gptq_quantize(Wt, U, group_size=-1, stream=side)
+        sums, n = m.read(stream=side)
+    side.synchronize()
+    acc = O.GramAccumulator(d, staging="bf16")
+    acc.add_batch(x16, W.F16)
+    Hr, deadr, _ = acc.materialize(0.01)
+    assert f.nsamples == acc.N == 900
+    assert agreement(H.cpu().numpy(), Hr) <= TOL[W.BF16]
+    xb = W.to_bf16_bits(x16.astype(np.float32))
+    sr = O.column_sum_squares([xb], W.BF16)
+    assert n == 900 and np.all(np.abs(sums.cpu().numpy() - sr) <= 5e-5 * sr + 1e-30)
+    U32 = U.cpu().numpy()
+    assert np.allclose(U32, O.chol_inverse_upper(H.cpu().numpy().astype(np.float64)), rtol=1e-5, atol=1e-9)
+    Qr, cr, _, _ = O.gptq_quantize(Wt.cpu().numpy().astype(np.float64), U32.astype(np.float64),
+                                   follow=codes.cpu().numpy(), tie_tol=1e-12)
+    assert np.array_equal(codes.cpu().numpy(), cr)
+    for o in (h, f, m):
+        o.close()
