@@ -79,12 +79,14 @@ __device__ __forceinline__ float load_f32(const void* X, int64_t i) {
 
 // Eight consecutive elements at p (16-byte aligned) as eight bf16 values in
 // four dwords (element 2k in the low half of dword k), rounded to nearest even.
+// Activations are read once, so the loads are non-temporal.
 template <int SRC>
 __device__ __forceinline__ u32x4 load8_bf16(const char* p) {
   if constexpr (SRC == kSrcBF16) {
-    return *reinterpret_cast<const u32x4*>(p);
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   } else if constexpr (SRC == kSrcF32) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p), b = *reinterpret_cast<const u32x4*>(p + 16);
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 16));
     u32x4 o;
     o[0] = f32_to_bf16_bits(__uint_as_float(a[0])) | (f32_to_bf16_bits(__uint_as_float(a[1])) << 16);
     o[1] = f32_to_bf16_bits(__uint_as_float(a[2])) | (f32_to_bf16_bits(__uint_as_float(a[3])) << 16);
@@ -92,7 +94,7 @@ __device__ __forceinline__ u32x4 load8_bf16(const char* p) {
     o[3] = f32_to_bf16_bits(__uint_as_float(b[2])) | (f32_to_bf16_bits(__uint_as_float(b[3])) << 16);
     return o;
   } else {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     u32x4 o;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -110,6 +112,9 @@ __device__ __forceinline__ u32x4 load8_bf16(const char* p) {
 // quarters' loads in flight at once), then thread t gathers each quarter's
 // feature F + 256 k + t over the 8 tokens and writes them as one chunk, so
 // that both the reads and the writes are contiguous across the workgroup.
+// The staged rows are read back only by a later flush, long after the L2 has
+// turned over, so they are written non-temporally (measured 1.5-2% faster
+// per Hessian on the ragged d=2560 workload).
 // Rows of fp16 or float32 are rounded to bf16 on the way.
 constexpr int kCQ = 2;
 template <int SRC>
@@ -139,7 +144,7 @@ __device__ __forceinline__ void t8_body(const char* X, int64_t ld_bytes, char* d
       u32x4 c;
 #pragma unroll
       for (int p = 0; p < 4; ++p) c[p] = (uint32_t)tile[k][2 * p][t] | ((uint32_t)tile[k][2 * p + 1][t] << 16);
-      *reinterpret_cast<u32x4*>(dst + (g * d + f) * 16) = c;
+      __builtin_nontemporal_store(c, reinterpret_cast<u32x4*>(dst + (g * d + f) * 16));
     }
   }
 }
