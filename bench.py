@@ -170,7 +170,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--extras", default="all",
-                    help="comma-separated subset of d4096_ragged,d4096_single,moe,local,imatrix,f16_staging,chol,quant "
+                    help="comma-separated subset of d4096_ragged,d4096_single,moe,local,imatrix,f16_staging,chol,quant,"
+                         "thin "
                          "(default all; imatrix runs with local)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--print-kernel-sha", action="store_true",
@@ -277,7 +278,8 @@ def run_extras(torch, hs, W, args):
     extra = {}
     steps = max(3, args.steps // 2)
     want = set(args.extras.split(",")) if args.extras != "all" else {"d4096_ragged", "d4096_single", "moe", "local",
-                                                                    "imatrix", "f16_staging", "chol", "quant"}
+                                                                    "imatrix", "f16_staging", "chol", "quant",
+                                                                    "thin"}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if "quant" in want:
         # error-propagating 4-bit quantization of a 4096 x 4096 layer (groups of 128), float64
@@ -464,6 +466,42 @@ def run_extras(torch, hs, W, args):
                                            "hbm_frac": round(byts / (per * 1e-3) / HBM, 4)}
             m.close()
         del xs
+    if "thin" in want:
+        # thin batches added straight into S (a handle without staging): the 64-tile kernel, whose
+        # time is the read-modify-write of S's upper triangle (4 d (d + 1) bytes) plus the batch
+        # (2 n d bytes).  batch_us: 200 back-to-back calls between two events on the stream (the
+        # host's per-call cost, about 7 us from Python, bounds it when the kernel is shorter);
+        # kernel_us: the library's HIP events around each launch (their own cost included).
+        for dt in (4096, 2560):
+            log(f"thin batches straight into S, d={dt}")
+            gen = W.torch_generator(8, "cuda")
+            sc = W.torch_column_scales(gen, dt, "cuda")
+            xs = W.torch_rows(gen, 64 * 16, dt, sc, "bf16", "cuda")
+            h = hs.Hessian(dt, torch.bfloat16, staging_bytes=0)
+            res = {}
+            for n in (1, 64):
+                views = [xs[i * 64:i * 64 + n] for i in range(16)]
+                for v in views[:4]:
+                    h.add_batch(v)
+                torch.cuda.synchronize()
+                reps = 200
+                e0.record()
+                for i in range(reps):
+                    h.add_batch(views[i % 16])
+                e1.record()
+                torch.cuda.synchronize()
+                b_us = e0.elapsed_time(e1) * 1e3 / reps
+                h.set_timing(True)
+                for i in range(reps):
+                    h.add_batch(views[i % 16])
+                launches, _, kms = h.timing()
+                h.set_timing(False)
+                byts = 4.0 * dt * (dt + 1) + 2.0 * n * dt
+                res[f"n{n}"] = {"batch_us": round(b_us, 2), "kernel_us": round(kms * 1e3 / launches, 2),
+                                "GBps": round(byts / b_us / 1e3, 1), "hbm_frac": round(byts / (b_us * 1e-6) / HBM, 4)}
+            h.close()
+            extra[f"thin_direct_d{dt}"] = res
+            del xs
     torch.cuda.empty_cache()
     return extra
 

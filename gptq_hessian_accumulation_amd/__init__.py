@@ -174,7 +174,7 @@ def set_group_chunk(nbytes: int) -> None:
 
 
 def set_tile_override(edge: int) -> None:
-    """Force the SYRK tile edge (0 = automatic, 128 or 256); process-wide."""
+    """Force the SYRK tile edge (0 = automatic, 64, 128 or 256); process-wide."""
     _check(_load().hess_set_tile_override(int(edge)))
 
 

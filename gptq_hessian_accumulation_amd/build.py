@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhess.so")
 
-SOURCES = ["hess_api.hip", "chol.hip", "quant.hip", "syrk.hip", "syrk_big.hip", "materialize.hip", "local_blocks.hip", "stage.hip",
+SOURCES = ["hess_api.hip", "chol.hip", "quant.hip", "syrk.hip", "syrk_big.hip", "syrk_thin.hip", "materialize.hip", "local_blocks.hip", "stage.hip",
            "imatrix.hip"]
 
 HIPCC_FLAGS = [

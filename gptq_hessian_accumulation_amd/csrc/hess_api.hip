@@ -93,7 +93,7 @@ constexpr int kMaxDevices = 64;
 BigWorkspace g_big[kMaxDevices];
 
 thread_local char g_err[512] = "";
-int g_tile_override = 0;  // 0 = automatic; 128 forces the 128-edge SYRK tiles
+int g_tile_override = 0;  // 0 = automatic; 64, 128 or 256 force that SYRK tile edge where it applies
 int64_t g_group_chunk = 0; // test hook: cap on the gathered bytes per grouped launch (0 = scratch size)
 bool g_staging = true;    // thin-batch staging enabled (process-wide)
 
@@ -338,9 +338,33 @@ int run_big(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s, bool 
   return HESS_OK;
 }
 
+// Thin bf16 batches added straight into S take the 64-tile kernel, whose
+// time is the read-modify-write of S's upper triangle.
+constexpr int kThinTile = 64;
+bool use_thin(const hess_s* h, int64_t n, bool vec) {
+  if (h->dtype != HESS_BF16 || !vec || n > kSyrkThinMaxN) return false;
+  return g_tile_override == 0 || g_tile_override == kThinTile;
+}
+
+int run_thin(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (h->timing) {
+    e = timing_begin(h, s);
+    if (e != hipSuccess) return hip_fail(e, "timing event");
+  }
+  e = launch_syrk_thin(X, ld, n, (int)h->d, h->S, h->d, s);
+  if (e != hipSuccess) return hip_fail(e, "thin SYRK launch");
+  if (h->timing) {
+    e = timing_end(h, s, n);
+    if (e != hipSuccess) return hip_fail(e, "timing event");
+  }
+  return HESS_OK;
+}
+
 // One SYRK pass of n rows of X into S, on stream s (already ordered).
 int run_syrk(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s) {
   const bool vec = vec_ok(X, ld, h->d, esize(h->dtype));
+  if (use_thin(h, n, vec)) return run_thin(h, X, n, ld, s);
   if (use_big(h, n, vec)) return run_big(h, X, n, ld, s);
   const Plan pl = plan_single(h->d, n, h->ws != nullptr);
   SyrkParams P;
@@ -576,7 +600,8 @@ const char* hess_strerror(int code) {
 const char* hess_last_error(void) { return g_err; }
 
 int hess_set_tile_override(int edge) {
-  if (edge != 0 && edge != 128 && edge != 256) return fail(HESS_EINVAL, "tile override must be 0, 128 or 256");
+  if (edge != 0 && edge != 64 && edge != 128 && edge != 256)
+    return fail(HESS_EINVAL, "tile override must be 0, 64, 128 or 256");
   g_tile_override = edge;
   return HESS_OK;
 }

@@ -250,14 +250,16 @@ int hess_reset(hess_t h, hess_stream_t stream);
 int hess_token_count(hess_t h, int64_t* n_out);
 
 /* Tuning and test hook, process-wide: force the edge of the upper-triangle
- * tiles used by hess_add_batch (0 = automatic choice per call, 128, or 256).
- * 256-tiles apply to bf16 handles with d % 8 == 0 and 16-byte aligned rows;
- * other calls keep 128-tiles.  The automatic choice takes 256-tiles at
- * d >= 1,024 when a pass (one batch, or one staging flush) gives each of
- * the 256 workgroups at least 300 iterations of 32 tokens.  The setting at
- * hess_create also fixes a handle's staging layout: 256 makes it the
- * transposed one whenever the handle stages, 128 keeps rows (see
- * hess_create_ex). */
+ * tiles used by hess_add_batch (0 = automatic choice per call, 64, 128, or
+ * 256).  256-tiles apply to bf16 handles with d % 8 == 0 and 16-byte aligned
+ * rows; 64-tiles (the thin-batch kernel, whose time is the read-modify-write
+ * of S) to the same handles and rows for passes of at most 512 tokens;
+ * other calls keep 128-tiles.  The automatic choice takes 64-tiles for such
+ * passes of at most 512 tokens, and 256-tiles at d >= 1,024 when a pass
+ * (one batch, or one staging flush) gives each of the 256 workgroups at
+ * least 300 iterations of 32 tokens.  The setting at hess_create also fixes
+ * a handle's staging layout: 256 makes it the transposed one whenever the
+ * handle stages, 128 keeps rows (see hess_create_ex). */
 int hess_set_tile_override(int edge);
 
 /*

@@ -50,6 +50,7 @@ def test_invalid_arguments_rejected_without_gpu():
     assert lib.hess_local_blocks_ex(None, 0, 0, 32, 16, 16, ctypes.c_void_p(16), 1, None) == -1
     assert lib.hess_local_blocks_ex(None, 0, 5, 32, 32, 16, ctypes.c_void_p(16), 1, None) == -1
     assert lib.hess_set_tile_override(100) == -1
+    assert lib.hess_set_tile_override(64) == 0 and lib.hess_set_tile_override(0) == 0
     assert not lib.hess_create_ex(16, 0, -1)
     assert b"staging_bytes" in lib.hess_last_error()
     offs = (ctypes.c_int64 * 2)(0, 1)

@@ -97,12 +97,48 @@ def test_edge_widths(d, dtype):
     check_against_oracle(wl)
 
 
-@pytest.mark.parametrize("edge", [128, 256])
+@pytest.mark.parametrize("edge", [64, 128, 256])
 def test_forced_tile_edges(edge):
     _say(f"forced tile {edge}")
     hs.set_tile_override(edge)
     wl = W.ragged_case(1000, [300, 2000], seed=55, dtype=W.BF16)
     check_against_oracle(wl)
+
+
+@pytest.mark.parametrize("override", [0, 64])
+@pytest.mark.parametrize("d", [8, 64, 72, 264, 1000, 2056])
+def test_thin_tiles(d, override):
+    """Batches added straight into S: the 64-tile kernel up to 512 tokens (edge
+    and diagonal tiles, partial 32-token steps), the 128- or 256-tile kernels
+    from 513 on."""
+    _say(f"thin 64-tile d={d} override={override}")
+    hs.set_tile_override(override)
+    hs.set_staging(False)
+    wl = W.ragged_case(d, [1, 5, 31, 32, 33, 100, 0, 511, 512, 513], seed=900 + d, dtype=W.BF16, dead_frac=0.02)
+    check_against_oracle(wl)
+
+
+def test_thin_tiles_full_width_and_strided_rows():
+    """Width 4,096 with 64-token batches straight into S (the thin-batch
+    measurement's shape), one of them with a row stride wider than d."""
+    _say("thin 64-tile d=4096, strided rows")
+    hs.set_staging(False)
+    d = 4096
+    wl = W.ragged_case(d, [64, 1, 64, 200], seed=77, dtype=W.BF16, dead_frac=0.01)
+    h = hs.Hessian(d, torch.bfloat16)
+    for i, b in enumerate(wl.batches):
+        xb = to_device(b, wl.dtype)
+        if i == 2:
+            wide = torch.zeros((xb.shape[0], d + 8), dtype=xb.dtype, device=xb.device)
+            wide[:, :d] = xb
+            xb = wide[:, :d]
+        h.add_batch(xb)
+    H, dead, _ = h.materialize(0.01)
+    Hr, deadr, _, Nr = run_oracle(wl)
+    assert h.nsamples == Nr
+    assert np.array_equal(dead.cpu().numpy(), deadr)
+    assert agreement(H.cpu().numpy(), Hr) <= TOL[W.BF16]
+    h.close()
 
 
 @pytest.mark.parametrize("staging", [True, False])
