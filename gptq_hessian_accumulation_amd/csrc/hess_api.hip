@@ -606,11 +606,12 @@ int hess_set_tile_override(int edge) {
   return HESS_OK;
 }
 
-// Default staging: for bf16 at widths >= 1,024, 512 MiB, so that a flush
-// is long enough for the 256-tile kernel (104,448 tokens at 2,560: one ragged
-// calibration Hessian of ~375K tokens takes 4 passes; measured 3.8 ms per
-// Hessian against 4.8 ms with 64 MiB staging and 128-tile passes); 64 MiB
-// otherwise.
+// Default staging: for bf16 at widths >= 1,024, 1 GiB, so that a flush
+// is long enough for the 256-tile kernel (209,664 tokens at 2,560: one ragged
+// calibration Hessian of ~375K tokens takes 2 passes).  Measured per Hessian
+// on that workload: 4.8 ms with 64 MiB and 128-tile passes, 3.53 ms with
+// 512 MiB (4 passes), 3.38-3.44 ms with 1 GiB, 3.52 ms with 2 GiB (one pass);
+// 64 MiB otherwise.
 int64_t default_staging(int64_t d, int in_dtype) {
   return (in_dtype == HESS_BF16 && d >= 1024) ? HESS_STAGING_DEFAULT : ((int64_t)64 << 20);
 }

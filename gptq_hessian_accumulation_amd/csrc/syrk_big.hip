@@ -59,9 +59,10 @@
 //  * Diagonal tiles load one panel and leave the below-diagonal wave idle.
 //
 // A float32 accumulation chain here is one segment's iterations: at most a
-// batch, or one staged flush (104,448 tokens at width 2,560 with the default
-// 512 MiB staging, i.e. 3,264 additions); each addition brings in one
-// instruction's sum of 32 exact products.
+// batch's or one staged flush's share of a tile (at width 2,560 the default
+// 1 GiB staging holds 209,664 tokens, cut into 5 parts of 1,311 additions;
+// whole-tile flushes, at widths above 5,632, chain at most 2,974); each
+// addition brings in one instruction's sum of 32 exact products.
 
 #include "hess_device.hpp"
 #include "hess_internal.hpp"

@@ -101,15 +101,15 @@ hess_t hess_create(int64_t d, int in_dtype);
 
 /* Size of a handle's staging buffer for short batches that hess_create
  * picks for bf16 handles with d >= 1024 (bytes); other handles get 64 MiB. */
-#define HESS_STAGING_DEFAULT ((int64_t)512 << 20)
+#define HESS_STAGING_DEFAULT ((int64_t)1 << 30)
 
 /*
  * hess_create_ex -- hess_create with the staging buffer's size chosen by the
  * caller: staging_bytes in [0, 16 GiB]; 0 (or too small for 256 rows)
  * disables staging for the handle, e.g. for Hessians only ever updated by
- * hess_add_batch_grouped.  hess_create picks 512 MiB (HESS_STAGING_DEFAULT)
+ * hess_add_batch_grouped.  hess_create picks 1 GiB (HESS_STAGING_DEFAULT)
  * for bf16 handles with d >= 1024, so that a staged flush is long enough for
- * the 256-tile kernel (104,448 tokens at d = 2560), and 64 MiB otherwise.
+ * the 256-tile kernel (209,664 tokens at d = 2560), and 64 MiB otherwise.
  * A smaller buffer saves memory at the cost of more, shorter flushes.
  * When a full buffer's flush would take the 256-tile kernel (bf16, d % 8 ==
  * 0, d >= 1,024 and enough tokens; see hess_set_tile_override), the staged
@@ -223,7 +223,7 @@ int hess_materialize_ex(hess_t h, float damp_percent, unsigned flags, float* H_o
  *
  * A batch shorter than about 2*d/elem_size tokens is not given its own pass
  * over the d x d sum: hess_add_batch copies its rows into a staging buffer
- * allocated by hess_create (64 or 512 MiB, see hess_create_ex) and counts its tokens, and the staged
+ * allocated by hess_create (64 MiB or 1 GiB, see hess_create_ex) and counts its tokens, and the staged
  * rows are added to S in one pass when the buffer fills, by
  * hess_materialize*, or by this call.  The Gram sum of the concatenated rows
  * equals the sum of the batches' Grams (GPTQModel PR 2981, Validation: add_batch

@@ -243,11 +243,11 @@ def test_big_tiles_full_size_sampled(d, n):
 
 
 def test_transposed_staging_full_flush_sampled():
-    """One full default staging buffer at width 2,560 (104,448 tokens in 2,000-token batches,
-    the longest float32 chain a staged flush makes) against the oracle's exact sums."""
+    """One full default staging buffer at width 2,560 (209,664 tokens in 2,000-token batches,
+    the longest staged flush at this width) against the oracle's exact sums."""
     _say("transposed staging full flush d=2560")
     d = 2560
-    sizes = [2000] * 52 + [448]
+    sizes = [2000] * 104 + [1664]
     wl = W.ragged_case(d, sizes, seed=2560, dtype=W.BF16, dead_frac=0.0)
     h = hs.Hessian(d, torch.bfloat16)
     for b in wl.batches:
