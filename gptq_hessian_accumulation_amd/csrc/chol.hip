@@ -19,7 +19,9 @@
 // R^-1; P holds the current block column of L transposed, tile by tile.  For
 // each block column k:
 //   diag    one workgroup factors A_kk = L_kk L_kk^T and inverts L_kk in LDS
-//           and registers, writing L_kk into A_kk and L_kk^-1 into X_kk
+//           (four 16-column panels, each factored by one wave without
+//           barriers, then blocked updates and a blocked inverse on the
+//           matrix cores), writing L_kk into A_kk and L_kk^-1 into X_kk
 //           (for k > 0 inside the previous update launch: its first
 //           workgroup updates A_kk and factors it while the others update
 //           the rest);
@@ -177,32 +179,7 @@ __global__ void __launch_bounds__(256) chol_load(const float* __restrict__ H, in
   }
 }
 
-// Factor and invert the diagonal tile k.  512 threads: thread t owns row
-// i = t / 8 and the columns cls + 8 m (cls = t % 8, m < 8) of Y (becoming
-// L^-1, starting as the identity) and of T (the tile being factored).  Step
-// j takes, from LDS, the column of T as it stands after steps 0 .. j-1
-// (colv[r] = T[r][j] for r >= j, zero above), the row Y[j][.] (rowv; zero
-// past j) and the pivot's square root l and reciprocal, all published by
-// their owners during step j-1, so each step needs one barrier and issues all
-// its LDS reads at once.  Column j of L (colv / l) is kept in LDS and written
-// out with the tile at the end; the rank-one updates
-// T[i][c] -= L[i][j] L[c][j] and Y[i][c] -= L[i][j] Y[j][c] / l are applied
-// to every owned entry without tests: the zeros in colv and rowv leave the
-// finished columns and the zero upper part of Y alone, and the entries of T
-// above the diagonal or left of column j are never read again.  After every
-// 8 steps the T registers shift down by one, dropping a finished column, so
-// that the column of the next pivot always sits in a fixed register.  The
-// owner of T[j+1][j+1] takes the next pivot's square root one step ahead of
-// its use.
-constexpr int kTPR = 8;               // threads per tile row (workgroup of kCB * kTPR)
-constexpr int kPer = kCB / kTPR;      // owned columns per thread
-
-struct DiagLds {
-  double colv[2][2 * kCB];  // entries past kCB stay zero (reads for shifted-out registers)
-  double rowv[2][kCB];
-  double pv[2][2];
-  double Lt[kCB * (kCB + 1)];  // the finished columns of L, written out at the end
-};
+constexpr int kTPR = 8;  // workgroup of the diagonal and update kernels: kCB * kTPR threads
 
 // Square root and reciprocal square root of a pivot: the hardware estimate of
 // 1 / sqrt(p) refined by one Newton step y <- y + y (1 - p y^2) / 2 (the
@@ -221,102 +198,166 @@ __device__ __forceinline__ void report_pivot(double p, int col, int d, int* info
   if (!(p > 0.0) && info && col < d) atomicMax(info, d - col);
 }
 
-// The tile to factor is read from src (row stride lds: global memory, or the
-// LDS copy left by the fused update).  The caller synchronizes the workgroup
-// after src is complete.
-__device__ __forceinline__ void diag_body(const double* src, int64_t lds, double* __restrict__ A,
-                                          double* __restrict__ X, int dp, int k, int d, int* info, DiagLds& S) {
-  auto& colv = S.colv;
-  auto& rowv = S.rowv;
-  auto& pv = S.pv;
-  const int t = threadIdx.x;
-  const int i = t / kTPR, cls = t % kTPR;
-  double* Ag = tile_at(A, dp, k, k);
-  double* Xg = tile_at(X, dp, k, k);
-  double T[kPer], Y[kPer];
+// Factor and invert the diagonal tile k, blocked: four panels of 16 columns.
+// The tile T (lower triangle valid, float64, LDS, row stride kDL) is
+// overwritten by L; Y = L^-1 is built in LDS.  For each panel:
+//  * one wave factors the panel's 16 columns over all rows at or below it,
+//    with no barrier: lane i holds row i's 16 entries of the panel (the
+//    diagonal block filled symmetrically from its lower triangle); column
+//    j's pivot and row (the pivot row's entries right of it, equal by
+//    symmetry to the column's entries below the pivot) reach every lane by
+//    readlane, and each lane applies T[i][c] -= (T[i][j] / p) T[j][c] to its
+//    remaining panel entries (p the pivot, taken through its reciprocal
+//    square root);
+//  * the waves then subtract the panel's product L_p L_p^T from the lower
+//    16 x 16 blocks right of it (float64 matrix cores).
+// Y: each 16 x 16 diagonal block is inverted by one wave (row j of the
+// block's inverse is final once scaled by 1 / L[j][j]; the rows below
+// subtract L[i][j] times it), then each block column s of Y below the
+// diagonal follows from Y_rs = -Y_rr (sum over s <= t < r of L_rt Y_ts),
+// one wave per block column, top to bottom.
+constexpr int kDL = kCB + 2;  // LDS row stride (doubles) of the diagonal step's tiles
+constexpr int kPB = 16;       // panel width
+
+struct DiagLdsB {
+  double Y[kCB * kDL];
+  double y[kCB];  // reciprocal of each column's diagonal entry of L
+};
+
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// T (LDS, stride kDL, written by the caller, workgroup synchronized) ->
+// L into A_kk and L^-1 into X_kk.  Needs at least 6 waves.
+__device__ __forceinline__ void diag_blocked(double* T, double* __restrict__ A, double* __restrict__ X, int dp, int k,
+                                             int d, int* info, DiagLdsB& S) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  for (int s = 0; s < kCB / kPB; ++s) {
+    const int c0 = kPB * s;
+    if (w == 0) {
+      const int i = lane;
+      double P[kPB];
 #pragma unroll
-  for (int m = 0; m < kPer; ++m) {
-    const int c = cls + kTPR * m;
-    T[m] = src[(int64_t)i * lds + c];
-    Y[m] = c == i ? 1.0 : 0.0;
-  }
-  if (t < 2 * kCB) {
-    colv[0][kCB + (t & (kCB - 1))] = 0.0;
-    colv[1][kCB + (t & (kCB - 1))] = 0.0;
-  }
-  // step 0's inputs: column 0, row 0 of Y, the first pivot
-  if (cls == 0) colv[0][i] = T[0];
-  if (i == 0) {
+      for (int q = 0; q < kPB; ++q) {
+        const int c = c0 + q;
+        P[q] = c <= i ? T[i * kDL + c] : T[c * kDL + i];
+      }
 #pragma unroll
-    for (int m = 0; m < kPer; ++m) rowv[0][cls + kTPR * m] = Y[m];
-    if (cls == 0) {
-      report_pivot(T[0], k * kCB, d, info);
-      pivot_root(T[0], pv[0][0], pv[0][1]);
+      for (int j = 0; j < kPB; ++j) {
+        const int r = c0 + j;
+        const double p = readlane_d(P[j], r);
+        if (lane == 0) report_pivot(p, k * kCB + r, d, info);
+        double l, y;
+        pivot_root(p, l, y);
+        const double lij = P[j] * y;
+        const double f = lij * y;
+#pragma unroll
+        for (int q = j + 1; q < kPB; ++q) P[q] = fma(-f, readlane_d(P[q], r), P[q]);
+        P[j] = i == r ? l : (i > r ? lij : 0.0);
+        if (lane == 0) S.y[r] = y;
+      }
+      if (i >= c0) {
+#pragma unroll
+        for (int q = 0; q < kPB; ++q) T[i * kDL + c0 + q] = P[q];
+      }
+    }
+    __syncthreads();
+    // trailing lower blocks (bi, bk), bk <= bi, right of the panel: one per wave
+    const int m = kCB / kPB - 1 - s;
+    if (w < m * (m + 1) / 2) {
+      int bi = 0, bk = w;
+      while (bk > bi) {
+        bk -= bi + 1;
+        ++bi;
+      }
+      const int I0 = c0 + kPB * (1 + bi), K0 = c0 + kPB * (1 + bk);
+      const int li = lane & 15, lk = lane >> 4;
+      f64x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = T[(I0 + lk + 4 * r) * kDL + K0 + li];
+#pragma unroll
+      for (int q = 0; q < kPB; q += 4) {
+        const double a = -T[(I0 + li) * kDL + c0 + q + lk];
+        const double b = T[(K0 + li) * kDL + c0 + q + lk];
+        acc = mfma_f64(a, b, acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) T[(I0 + lk + 4 * r) * kDL + K0 + li] = acc[r];
+    }
+    __syncthreads();
+  }
+  // inverse of each diagonal block (wave s, lanes 0..15 = the block's rows)
+  if (w < kCB / kPB) {
+    const int c0 = kPB * w, i = lane & 15;
+    double Lr[kPB], Yr[kPB];
+#pragma unroll
+    for (int q = 0; q < kPB; ++q) {
+      Lr[q] = T[(c0 + i) * kDL + c0 + q];
+      Yr[q] = q == i ? 1.0 : 0.0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPB; ++j) {
+      const double yj = S.y[c0 + j];
+      const double g = Lr[j] * yj;
+#pragma unroll
+      for (int q = 0; q <= j; ++q) {
+        const double v = readlane_d(Yr[q], j);
+        Yr[q] = i == j ? v * yj : fma(-g, v, Yr[q]);
+      }
+    }
+    if (lane < kPB) {
+#pragma unroll
+      for (int q = 0; q < kPB; ++q) S.Y[(c0 + i) * kDL + c0 + q] = Yr[q];
     }
   }
   __syncthreads();
-  for (int jb = 0; jb < kCB; jb += kTPR) {
-    const int cb = cls + jb;  // column held by T[0] in this block of steps
+  // blocks below the diagonal, block column s = w (waves 0..2), rows top to bottom
+  if (w < kCB / kPB - 1) {
+    const int s0 = kPB * w;
+    const int li = lane & 15, lk = lane >> 4;
+    for (int rb = w + 1; rb < kCB / kPB; ++rb) {
+      const int r0 = kPB * rb;
+      f64x4 g = f64x4{0.0, 0.0, 0.0, 0.0};
+      for (int tb = w; tb < rb; ++tb) {
+        const int t0 = kPB * tb;
 #pragma unroll
-    for (int u = 0; u < kTPR; ++u) {
-      const int j = jb + u;
-      const int b = u & 1, nb = b ^ 1;
-      // every read of the step at once: one LDS latency
-      const double l = pv[b][0], inv = pv[b][1];
-      const double ci = colv[b][i];
-      double cv[kPer], rv[kPer];
-#pragma unroll
-      for (int m = 0; m < kPer; ++m) {
-        cv[m] = colv[b][cb + kTPR * m];
-        rv[m] = rowv[b][cls + kTPR * m];
-      }
-      const double lij = i > j ? ci * inv : 0.0;
-      const double f = lij * inv;
-#pragma unroll
-      for (int m = 0; m < kPer; ++m) {
-        T[m] = fma(-f, cv[m], T[m]);
-        Y[m] = fma(-f, rv[m], Y[m]);
-      }
-      const double ys = i == j ? inv : 1.0;  // row j of L^-1
-#pragma unroll
-      for (int m = 0; m < kPer; ++m) Y[m] *= ys;
-      if (cls == u && i >= j) S.Lt[i * (kCB + 1) + j] = i == j ? l : lij;  // column j of L
-      const int c1 = j + 1;
-      if (c1 < kCB) {
-        // column c1 is T[0] of owner cls = u + 1, or T[1] of cls = 0 after the block's last step
-        const bool owner = cls == (u + 1) % kTPR;
-        const double next = (u + 1 < kTPR) ? T[0] : T[1];
-        double nl, ny;
-        pivot_root(next, nl, ny);
-        if (owner) colv[nb][i] = i >= c1 ? next : 0.0;
-        if (i == c1) {
-#pragma unroll
-          for (int m = 0; m < kPer; ++m) rowv[nb][cls + kTPR * m] = Y[m];
-          if (owner) {
-            report_pivot(next, k * kCB + c1, d, info);
-            pv[nb][0] = nl;
-            pv[nb][1] = ny;
-          }
+        for (int q = 0; q < kPB; q += 4) {
+          const double a = T[(r0 + li) * kDL + t0 + q + lk];
+          const double b = S.Y[(t0 + q + lk) * kDL + s0 + li];
+          g = mfma_f64(a, b, g);
         }
       }
-      __syncthreads();
+      // Y_rs = -Y_rr G: register q of g is G's rows 4 q + lane / 16, the
+      // matrix instruction's B operand for k-step q
+      f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = mfma_f64(-S.Y[(r0 + li) * kDL + r0 + 4 * q + lk], g[q], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S.Y[(r0 + lk + 4 * r) * kDL + s0 + li] = acc[r];
     }
-#pragma unroll
-    for (int m = 0; m + 1 < kPer; ++m) T[m] = T[m + 1];
-    T[kPer - 1] = 0.0;
   }
-#pragma unroll
-  for (int m = 0; m < kPer; ++m) {
-    const int c = cls + kTPR * m;
-    Xg[(int64_t)i * dp + c] = Y[m];
-    Ag[(int64_t)i * dp + c] = c <= i ? S.Lt[i * (kCB + 1) + c] : 0.0;
+  __syncthreads();
+  double* Ag = tile_at(A, dp, k, k);
+  double* Xg = tile_at(X, dp, k, k);
+  for (int e = t; e < kCB * kCB; e += blockDim.x) {
+    const int i = e / kCB, c = e % kCB;
+    Ag[(int64_t)i * dp + c] = c <= i ? T[i * kDL + c] : 0.0;
+    Xg[(int64_t)i * dp + c] = c <= i ? S.Y[i * kDL + c] : 0.0;
   }
 }
 
 __global__ void __launch_bounds__(kCB * kTPR) chol_diag(double* __restrict__ A, double* __restrict__ X, int dp, int k,
                                                         int d, int* info) {
-  __shared__ DiagLds S;
-  diag_body(tile_at(A, dp, k, k), dp, A, X, dp, k, d, info, S);
+  __shared__ double Tl[kCB * kDL];
+  __shared__ DiagLdsB S;
+  const double* src = tile_at(A, dp, k, k);
+  for (int e = threadIdx.x; e < kCB * kCB; e += blockDim.x) Tl[(e / kCB) * kDL + e % kCB] = src[(int64_t)(e / kCB) * dp + e % kCB];
+  __syncthreads();
+  diag_blocked(Tl, A, X, dp, k, d, info, S);
 }
 
 // Panel of block column k: workgroups b < m = nb - k - 1 take A_ib (i = k + 1
@@ -359,13 +400,13 @@ __global__ void __launch_bounds__(kCB * kTPR) chol_update(double* __restrict__ A
     // tile (k+1, k+1): update it into LDS, then factor and invert it here
     // (the next block column's diagonal step), while the other workgroups
     // update the rest
-    __shared__ double Tl[kCB * kCB];
-    __shared__ DiagLds S;
+    __shared__ double Tl[kCB * kDL];
+    __shared__ DiagLdsB S;
     const int I = k + 1;
     tile_update_direct(P + (int64_t)I * kCB * kCB, P + (int64_t)I * kCB * kCB, kCB, tile_at(A, dp, I, I), dp, Tl,
-                       kCB);
+                       kDL);
     __syncthreads();
-    diag_body(Tl, kCB, A, X, dp, I, d, info, S);
+    diag_blocked(Tl, A, X, dp, I, d, info, S);
   } else if (b < T1) {
     int ii = (int)((sqrt(8.0 * (double)b + 1.0) - 1.0) * 0.5);
     while ((int64_t)ii * (ii + 1) / 2 > b) --ii;
