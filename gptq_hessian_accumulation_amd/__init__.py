@@ -186,7 +186,7 @@ class Hessian:
     they are; float16, bfloat16 or float32 batches of another type are
     converted on their way into the staging buffer (rounded to nearest even
     when narrowing).  The Hessian is always float32.  ``staging_bytes`` sizes
-    the buffer that collects short batches (default: 1 GiB for bf16 at
+    the buffer that collects short batches (default: 1 GiB at
     d >= 1024, else 64 MiB; 0 disables staging and conversion).
     """
 

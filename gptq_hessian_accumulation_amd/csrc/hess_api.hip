@@ -606,17 +606,18 @@ int hess_set_tile_override(int edge) {
   return HESS_OK;
 }
 
-// Default staging: for bf16 at widths >= 1,024, 1 GiB, so that a flush
-// is long enough for the 256-tile kernel (209,664 tokens at 2,560: one ragged
+// Default staging at widths >= 1,024: 1 GiB, so that a flush is long
+// enough for the 256-tile kernel (209,664 bf16 tokens at 2,560: one ragged
 // calibration Hessian of ~375K tokens takes 2 passes).  Measured per Hessian
 // on that workload: 4.8 ms with 64 MiB and 128-tile passes, 3.53 ms with
-// 512 MiB (4 passes), 3.38-3.44 ms with 1 GiB, 3.52 ms with 2 GiB (one pass);
-// 64 MiB otherwise.
-int64_t default_staging(int64_t d, int in_dtype) {
-  return (in_dtype == HESS_BF16 && d >= 1024) ? HESS_STAGING_DEFAULT : ((int64_t)64 << 20);
+// 512 MiB (4 passes), 3.38-3.44 ms with 1 GiB, 3.52 ms with 2 GiB (one
+// pass).  float32 rows at 4,096 (366K ragged tokens): 64.0 ms with 64 MiB,
+// 54.3 with 256 MiB, 53.1-53.5 with 512 MiB or 1 GiB.  64 MiB otherwise.
+int64_t default_staging(int64_t d) {
+  return d >= 1024 ? HESS_STAGING_DEFAULT : ((int64_t)64 << 20);
 }
 
-hess_t hess_create(int64_t d, int in_dtype) { return hess_create_ex(d, in_dtype, default_staging(d, in_dtype)); }
+hess_t hess_create(int64_t d, int in_dtype) { return hess_create_ex(d, in_dtype, default_staging(d)); }
 
 hess_t hess_create_ex(int64_t d, int in_dtype, int64_t staging_bytes) {
   if (d < 1 || d > 65536) {

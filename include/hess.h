@@ -100,7 +100,7 @@ const char* hess_last_error(void);
 hess_t hess_create(int64_t d, int in_dtype);
 
 /* Size of a handle's staging buffer for short batches that hess_create
- * picks for bf16 handles with d >= 1024 (bytes); other handles get 64 MiB. */
+ * picks for handles with d >= 1024 (bytes); narrower handles get 64 MiB. */
 #define HESS_STAGING_DEFAULT ((int64_t)1 << 30)
 
 /*
@@ -108,7 +108,7 @@ hess_t hess_create(int64_t d, int in_dtype);
  * caller: staging_bytes in [0, 16 GiB]; 0 (or too small for 256 rows)
  * disables staging for the handle, e.g. for Hessians only ever updated by
  * hess_add_batch_grouped.  hess_create picks 1 GiB (HESS_STAGING_DEFAULT)
- * for bf16 handles with d >= 1024, so that a staged flush is long enough for
+ * for handles with d >= 1024, so that a staged flush is long enough for
  * the 256-tile kernel (209,664 tokens at d = 2560), and 64 MiB otherwise.
  * A smaller buffer saves memory at the cost of more, shorter flushes.
  * When a full buffer's flush would take the 256-tile kernel (bf16, d % 8 ==
