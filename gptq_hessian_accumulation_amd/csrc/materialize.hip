@@ -18,8 +18,8 @@
 //     staged through LDS and written both to H's tile (I, J) and, transposed,
 //     to tile (J, I), so both halves of every symmetric pair come from the
 //     same S element with the same operations (H is bitwise symmetric) and
-//     all global accesses are coalesced.  Only S's upper triangle is read,
-//     so H may alias S (in-place materialize).
+//     all global accesses are coalesced (16-byte accesses when d % 4 == 0).
+//     Only S's upper triangle is read, so H may alias S (in-place materialize).
 
 #include "hess_internal.hpp"
 
@@ -102,6 +102,68 @@ __global__ void __launch_bounds__(256) mirror_kernel(const float* S, int64_t lds
   }
 }
 
+// The same pass with 16-byte accesses, for d % 4 == 0 (every S and H row
+// 16-byte aligned): thread t moves columns 4 (t % 16) .. +3 of tile rows
+// t / 16 + 16 k (k < 4), so 16 lanes cover one 256-byte tile row; the tile's
+// row and column dead flags are read once into LDS.
+__global__ void __launch_bounds__(256) mirror_kernel_vec(const float* S, int64_t lds, int d, float scale,
+                                                         const uint8_t* dead, const float* damp_dev, float* H,
+                                                         int nt) {
+  __shared__ float tile[kT][kT + 1];
+  __shared__ uint8_t dR[kT], dC[kT];
+  // blockIdx.x -> (I, J), I <= J: blockIdx.x = J (J + 1) / 2 + I
+  const int b = blockIdx.x;
+  int J = (int)((sqrtf(8.0f * (float)b + 1.0f) - 1.0f) * 0.5f);
+  while (J * (J + 1) / 2 > b) --J;
+  while ((J + 1) * (J + 2) / 2 <= b) ++J;
+  const int I = b - J * (J + 1) / 2;
+  const int r0 = I * kT, c0 = J * kT;
+  const float damp = damp_dev[0];
+  const int t = threadIdx.x, cq = 4 * (t & 15), rr = t >> 4;
+  if (t < kT) dR[t] = r0 + t < d ? dead[r0 + t] : 0;
+  else if (t < 2 * kT) dC[t - kT] = c0 + t - kT < d ? dead[c0 + t - kT] : 0;
+  // stage the S tile (rows r0.., cols c0..); of the diagonal tile only the
+  // upper part (c >= r) is read
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = rr + 16 * k, gi = r0 + r, gj = c0 + cq;
+    float4 v = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (gi < d && gj < d && (I != J || cq + 3 >= r)) v = *reinterpret_cast<const float4*>(S + (int64_t)gi * lds + gj);
+    tile[r][cq] = v.x;
+    tile[r][cq + 1] = v.y;
+    tile[r][cq + 2] = v.z;
+    tile[r][cq + 3] = v.w;
+  }
+  __syncthreads();
+  // tile (I, J): H[r0 + r][c0 + c]
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = rr + 16 * k, gi = r0 + r, gj = c0 + cq;
+    if (gi >= d || gj >= d) continue;
+    const bool di = dR[r] != 0;
+    float o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = cq + q;
+      const float sv = (I == J && c < r) ? tile[c][r] : tile[r][c];
+      o[q] = hval(sv, scale, di, dC[c] != 0, gi == gj + q, damp);
+    }
+    *reinterpret_cast<float4*>(H + (int64_t)gi * lds + gj) = float4{o[0], o[1], o[2], o[3]};
+  }
+  if (I == J) return;
+  // tile (J, I): H[c0 + c][r0 + r] = value of S[r0 + r][c0 + c]
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = rr + 16 * k, gi = c0 + c, gj = r0 + cq;
+    if (gi >= d || gj >= d) continue;
+    const bool di = dC[c] != 0;
+    float o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = hval(tile[cq + q][c], scale, di, dR[cq + q] != 0, false, damp);
+    *reinterpret_cast<float4*>(H + (int64_t)gi * lds + gj) = float4{o[0], o[1], o[2], o[3]};
+  }
+}
+
 }  // namespace
 
 hipError_t launch_materialize(const float* S, int64_t lds, int d, float scale, float damp_percent, int neutralize,
@@ -113,7 +175,12 @@ hipError_t launch_materialize(const float* S, int64_t lds, int d, float scale, f
   if (e != hipSuccess) return e;
   const int nt = (d + kT - 1) / kT;
   const int tiles = nt * (nt + 1) / 2;
-  hipLaunchKernelGGL(mirror_kernel, dim3(tiles), dim3(256), 0, stream, S, lds, d, scale, dead, damp_dev, H, nt);
+  const bool vec = d % 4 == 0 && lds % 4 == 0 && (reinterpret_cast<uintptr_t>(S) & 15u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(H) & 15u) == 0;
+  if (vec)
+    hipLaunchKernelGGL(mirror_kernel_vec, dim3(tiles), dim3(256), 0, stream, S, lds, d, scale, dead, damp_dev, H, nt);
+  else
+    hipLaunchKernelGGL(mirror_kernel, dim3(tiles), dim3(256), 0, stream, S, lds, d, scale, dead, damp_dev, H, nt);
   return hipGetLastError();
 }
 
