@@ -910,7 +910,7 @@ int hess_reset(hess_t h, hess_stream_t stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = order_stream(h, s);
   if (rc != HESS_OK) return rc;
-  hipError_t e = launch_zero(h->S, h->d * h->d, s);
+  hipError_t e = launch_zero_upper(h->S, h->d, (int)h->d, s);
   if (e != hipSuccess) return hip_fail(e, "reset launch");
   h->stage_n = h->stage_real = 0;
   h->N = 0;

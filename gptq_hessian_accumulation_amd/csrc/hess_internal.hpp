@@ -143,6 +143,9 @@ hipError_t launch_local_blocks(const void* X, int in_dtype, int64_t n, int d, in
                                int accumulate, hipStream_t stream);
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
+// Zero S's rows from column 256 * (row / 256) on: the upper triangle and every
+// diagonal tile the SYRK kernels read or write.
+hipError_t launch_zero_upper(float* S, int64_t lds, int d, hipStream_t stream);
 
 // Error-propagating 4-bit quantization of W (rows x cols) with the factor U.
 struct QuantParams {

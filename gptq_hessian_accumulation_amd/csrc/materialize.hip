@@ -164,7 +164,29 @@ __global__ void __launch_bounds__(256) mirror_kernel_vec(const float* S, int64_t
   }
 }
 
+// Zero the part of S that holds the sum: row i from column 256 * (i / 256)
+// on, which covers every upper-triangle tile of every SYRK tile size (their
+// diagonal tiles included) and about half the bytes of the whole matrix.
+__global__ void __launch_bounds__(256) zero_upper_kernel(float* S, int64_t lds, int d, int vec) {
+  const int i = blockIdx.x;
+  const int c0 = (i / 256) * 256;
+  float* row = S + (int64_t)i * lds;
+  if (vec) {
+    for (int c = c0 + 4 * (int)threadIdx.x; c < d; c += 4 * 256)
+      *reinterpret_cast<float4*>(row + c) = float4{0.0f, 0.0f, 0.0f, 0.0f};
+  } else {
+    for (int c = c0 + (int)threadIdx.x; c < d; c += 256) row[c] = 0.0f;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_zero_upper(float* S, int64_t lds, int d, hipStream_t stream) {
+  if (d <= 0) return hipSuccess;
+  const int vec = d % 4 == 0 && lds % 4 == 0 && (reinterpret_cast<uintptr_t>(S) & 15u) == 0;
+  hipLaunchKernelGGL(zero_upper_kernel, dim3((unsigned)d), dim3(256), 0, stream, S, lds, d, vec);
+  return hipGetLastError();
+}
 
 hipError_t launch_materialize(const float* S, int64_t lds, int d, float scale, float damp_percent, int neutralize,
                               float* H, uint8_t* dead, float* damp_dev, double* /*sum_scratch*/,

@@ -243,7 +243,8 @@ int hess_set_staging(int enable);
  * whole buffer.  EINVAL for a negative value. */
 int hess_set_group_chunk(int64_t bytes);
 
-/* S = 0, N = 0 (enqueued on stream); also re-arms a consumed handle. */
+/* S = 0 (its upper triangle, where the sum lives; see hess_state_buffer),
+ * N = 0 (enqueued on stream); also re-arms a consumed handle. */
 int hess_reset(hess_t h, hess_stream_t stream);
 
 /* Tokens accumulated so far (host int64; exact, counted on the host). */
