@@ -25,9 +25,10 @@
 //           (for k > 0 inside the previous update launch: its first
 //           workgroup updates A_kk and factors it while the others update
 //           the rest);
-//   panel   A_ik <- A_ik L_kk^-T below the diagonal (a product with the
-//           inverse, so it runs on the matrix cores) and, for the inverse,
-//           X_kj <- L_kk^-1 X_kj left of it (block forward substitution);
+//   panel   P_i <- (A_ik L_kk^-T)^T below the diagonal (a product with the
+//           inverse, so it runs on the matrix cores; the transposed copy is
+//           what the update reads) and, for the inverse, X_kj <- L_kk^-1 X_kj
+//           left of it (block forward substitution);
 //   update  A_ij -= A_ik A_jk^T for k < j <= i (the trailing Schur
 //           complement) and X_ij -= A_ik X_kj for i > k, j <= k (the
 //           right-looking update of the forward substitution).
@@ -70,52 +71,6 @@ __device__ __forceinline__ void tile_to_lds(const double* __restrict__ src, int6
   for (int q = 0; q < 8; ++q) v[q] = s[q];
 #pragma unroll
   for (int q = 0; q < 8; ++q) *reinterpret_cast<f64x2*>(lds + r * kLdsLd + c0 + 2 * q) = v[q];
-}
-
-// C (64 x 64 tile at Cg, row stride dp) = init + sign * P, where P = A B^T
-// (BT) or A B, with A and B 64 x 64 tiles in LDS.  init is C's old value
-// (accumulate) or zero.  Wave w computes rows 32 (w >> 1) .. +31 and columns
-// 32 (w & 1) .. +31 as 2 x 2 blocks of 16 x 16.
-template <bool BT, bool ACCUM, bool NEG>
-__device__ __forceinline__ void tile_product(const double* Al, const double* Bl, double* __restrict__ Cg, int64_t dp,
-                                             double* __restrict__ Ct = nullptr) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r0 = 32 * (w >> 1), c0 = 32 * (w & 1);
-  const int li = lane & 15, lk = lane >> 4;
-  f64x4 acc[2][2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        acc[rb][cb][r] = ACCUM ? Cg[(int64_t)(r0 + 16 * rb + lk + 4 * r) * dp + c0 + 16 * cb + li] : 0.0;
-    }
-#pragma unroll 4
-  for (int kk = 0; kk < kCB; kk += 4) {
-    double a[2], b[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const double v = Al[(r0 + 16 * rb + li) * kLdsLd + kk + lk];
-      a[rb] = NEG ? -v : v;
-    }
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-      b[cb] = BT ? Bl[(c0 + 16 * cb + li) * kLdsLd + kk + lk] : Bl[(kk + lk) * kLdsLd + c0 + 16 * cb + li];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma_f64(a[rb], b[cb], acc[rb][cb]);
-  }
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        Cg[(int64_t)(r0 + 16 * rb + lk + 4 * r) * dp + c0 + 16 * cb + li] = acc[rb][cb][r];
-        if (Ct) Ct[(c0 + 16 * cb + li) * kCB + r0 + 16 * rb + lk + 4 * r] = acc[rb][cb][r];
-      }
 }
 
 // C (64 x 64 tile, row stride dp) -= A B with the fragments read straight
@@ -360,28 +315,80 @@ __global__ void __launch_bounds__(kCB * kTPR) chol_diag(double* __restrict__ A, 
   diag_blocked(Tl, A, X, dp, k, d, info, S);
 }
 
-// Panel of block column k: workgroups b < m = nb - k - 1 take A_ib (i = k + 1
-// + b) <- A_ib L_kk^-T, also written transposed to P_i (64 x 64, P_i[c][r] =
-// A_ib[r][c]) for the update's fragment loads; the others take X_kj
-// (j = b - m < k) <- L_kk^-1 X_kj.
-__global__ void __launch_bounds__(256) chol_panel(double* __restrict__ A, double* __restrict__ X,
+// Panel of block column k, on four workgroups per tile below the diagonal
+// and two per tile left of it, so that the float64 matrix cores of more CUs
+// share each step of the serial chain:
+//  * workgroups b < 4 m (m = nb - k - 1) take quadrant (b / 2 % 2, b % 2) of
+//    A_ik L_kk^-T (i = k + 1 + b / 4): 32 rows of A_ik times 32 rows of
+//    L_kk^-1, written transposed into P_i (P_i[c][r] = (A_ik L_kk^-T)[r][c]),
+//    the copy the trailing update reads.  A_ik itself is read by nothing
+//    later, so it is not rewritten, and the quadrants only read A_ik;
+//  * the others take column half (b - 4 m) % 2 of X_kj <- L_kk^-1 X_kj
+//    (j = (b - 4 m) / 2 < k), in place: each half reads only its own columns.
+__global__ void __launch_bounds__(256) chol_panel(const double* __restrict__ A, double* __restrict__ X,
                                                   double* __restrict__ P, int dp, int k, int nb) {
   __shared__ __attribute__((aligned(16))) double Al[kCB * kLdsLd];
   __shared__ __attribute__((aligned(16))) double Bl[kCB * kLdsLd];
   const int m = nb - k - 1;
   const int b = blockIdx.x;
-  if (b < m) {
-    double* C = tile_at(A, dp, k + 1 + b, k);
-    tile_to_lds(C, dp, Al);
-    tile_to_lds(tile_at(X, dp, k, k), dp, Bl);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int li = lane & 15, lk = lane >> 4;
+  if (b < 4 * m) {
+    const int i = k + 1 + b / 4, rh = (b >> 1) & 1, ch = b & 1;
+    // 32 rows of A_ik and 32 rows of L_kk^-1: thread t moves 8 doubles of row t / 8 of each
+    {
+      const int r = t >> 3, c = (t & 7) * 8;
+      const double* sa = A + ((int64_t)i * kCB + 32 * rh + r) * dp + (int64_t)k * kCB + c;
+      const double* sb = X + ((int64_t)k * kCB + 32 * ch + r) * dp + (int64_t)k * kCB + c;
+      f64x2 va[4], vb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        va[q] = reinterpret_cast<const f64x2*>(sa)[q];
+        vb[q] = reinterpret_cast<const f64x2*>(sb)[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        *reinterpret_cast<f64x2*>(Al + r * kLdsLd + c + 2 * q) = va[q];
+        *reinterpret_cast<f64x2*>(Bl + r * kLdsLd + c + 2 * q) = vb[q];
+      }
+    }
     __syncthreads();
-    tile_product<true, false, false>(Al, Bl, C, dp, P + (int64_t)(k + 1 + b) * kCB * kCB);
+    // wave w: rows 16 (w >> 1) .. +15, columns 16 (w & 1) .. +15 of the quadrant
+    const int r0 = 16 * (w >> 1), c0 = 16 * (w & 1);
+    f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int kk = 0; kk < kCB; kk += 4)
+      acc = mfma_f64(Al[(r0 + li) * kLdsLd + kk + lk], Bl[(c0 + li) * kLdsLd + kk + lk], acc);
+    double* Pi = P + (int64_t)i * kCB * kCB;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Pi[(32 * ch + c0 + li) * kCB + 32 * rh + r0 + lk + 4 * r] = acc[r];
   } else {
-    double* C = tile_at(X, dp, k, b - m);
+    const int j = (b - 4 * m) >> 1, ch = (b - 4 * m) & 1;
+    double* C = tile_at(X, dp, k, j) + 32 * ch;
     tile_to_lds(tile_at(X, dp, k, k), dp, Al);
-    tile_to_lds(C, dp, Bl);
+    {
+      // column half of X_kj: thread t moves 8 doubles of row t / 4
+      const int r = t >> 2, c = (t & 3) * 8;
+      const double* sc = C + (int64_t)r * dp + c;
+      f64x2 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = reinterpret_cast<const f64x2*>(sc)[q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<f64x2*>(Bl + r * kLdsLd + c + 2 * q) = v[q];
+    }
     __syncthreads();
-    tile_product<false, false, false>(Al, Bl, C, dp);
+    // wave w: rows 16 w .. +15, both 16-column blocks of the half
+    f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
+#pragma unroll 4
+    for (int kk = 0; kk < kCB; kk += 4) {
+      const double a = Al[(16 * w + li) * kLdsLd + kk + lk];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) acc[cb] = mfma_f64(a, Bl[(kk + lk) * kLdsLd + 16 * cb + li], acc[cb]);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) C[(int64_t)(16 * w + lk + 4 * r) * dp + 16 * cb + li] = acc[cb][r];
   }
 }
 
@@ -442,7 +449,7 @@ hipError_t launch_chol_inverse_upper(const float* H, int64_t ldh, int d, float* 
   for (int k = 0; k < nb; ++k) {
     // the update after block column k also factors diagonal tile k + 1
     const int m = nb - k - 1;
-    if (m + k > 0) hipLaunchKernelGGL(chol_panel, dim3(m + k), dim3(256), 0, s, A, X, P, dp, k, nb);
+    if (m + k > 0) hipLaunchKernelGGL(chol_panel, dim3(4 * m + 2 * k), dim3(256), 0, s, A, X, P, dp, k, nb);
     const int64_t tiles = (int64_t)m * (m + 1) / 2 + (int64_t)m * (k + 1);
     if (tiles > 0)
       hipLaunchKernelGGL(chol_update, dim3((unsigned)tiles), dim3(kCB * kTPR), 0, s, A, X, P, dp, k, nb, d, info);
