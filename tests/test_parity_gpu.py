@@ -372,22 +372,26 @@ def test_materialize_repeatable_and_accumulation_continues():
     h.close()
 
 
-def test_in_place_materialize_consumes_handle():
-    _say("in-place materialize")
-    wl = W.ragged_case(200, [150], seed=13, dtype=W.F32)
-    h = hs.Hessian(200, torch.float32)
-    h.add_batch(to_device(wl.batches[0], W.F32))
+@pytest.mark.parametrize("d,n,dtype", [(200, 150, W.F32), (264, 100, W.BF16), (1032, 1000, W.BF16)])
+def test_in_place_materialize_consumes_handle(d, n, dtype):
+    """After an in-place materialize the buffer holds H (both triangles); reset
+    clears the sum's region only, and a new accumulation over it is exact
+    again (128-tile, 64-tile and 256-tile kernels)."""
+    _say(f"in-place materialize d={d} n={n} {dtype}")
+    wl = W.ragged_case(d, [n], seed=13, dtype=dtype)
+    h = hs.Hessian(d, torch_dtype(dtype))
+    h.add_batch(to_device(wl.batches[0], dtype))
     ref, _, _ = h.materialize(0.01)
     dead, damp = h.materialize_in_place(0.01)
     torch.cuda.synchronize()
     with pytest.raises(hs.HessError) as e:
-        h.add_batch(to_device(wl.batches[0], W.F32))
+        h.add_batch(to_device(wl.batches[0], dtype))
     assert e.value.code == -4
     # the state buffer now holds H
     buf = h.state_tensor().clone()
     assert torch.equal(buf, ref)
     h.reset()
-    h.add_batch(to_device(wl.batches[0], W.F32))
+    h.add_batch(to_device(wl.batches[0], dtype))
     again, _, _ = h.materialize(0.01)
     assert torch.equal(again, ref)
     h.close()
