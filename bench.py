@@ -472,12 +472,12 @@ def run_extras(torch, hs, W, args):
         # (2 n d bytes).  batch_us: 200 back-to-back calls between two events on the stream (the
         # host's per-call cost, about 7 us from Python, bounds it when the kernel is shorter);
         # kernel_us: the library's HIP events around each launch (their own cost included).
-        for dt in (4096, 2560):
-            log(f"thin batches straight into S, d={dt}")
+        for dt, xdt in ((4096, "bf16"), (2560, "bf16"), (4096, "f32")):
+            log(f"thin batches straight into S, d={dt} {xdt}")
             gen = W.torch_generator(8, "cuda")
             sc = W.torch_column_scales(gen, dt, "cuda")
-            xs = W.torch_rows(gen, 64 * 16, dt, sc, "bf16", "cuda")
-            h = hs.Hessian(dt, torch.bfloat16, staging_bytes=0)
+            xs = W.torch_rows(gen, 64 * 16, dt, sc, xdt, "cuda")
+            h = hs.Hessian(dt, torch.bfloat16 if xdt == "bf16" else torch.float32, staging_bytes=0)
             res = {}
             for n in (1, 64):
                 views = [xs[i * 64:i * 64 + n] for i in range(16)]
@@ -496,11 +496,11 @@ def run_extras(torch, hs, W, args):
                     h.add_batch(views[i % 16])
                 launches, _, kms = h.timing()
                 h.set_timing(False)
-                byts = 4.0 * dt * (dt + 1) + 2.0 * n * dt
+                byts = 4.0 * dt * (dt + 1) + (2.0 if xdt == "bf16" else 4.0) * n * dt
                 res[f"n{n}"] = {"batch_us": round(b_us, 2), "kernel_us": round(kms * 1e3 / launches, 2),
                                 "GBps": round(byts / b_us / 1e3, 1), "hbm_frac": round(byts / (b_us * 1e-6) / HBM, 4)}
             h.close()
-            extra[f"thin_direct_d{dt}"] = res
+            extra[f"thin_direct_d{dt}" + ("" if xdt == "bf16" else "_f32")] = res
             del xs
     torch.cuda.empty_cache()
     return extra

@@ -338,11 +338,11 @@ int run_big(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s, bool 
   return HESS_OK;
 }
 
-// Thin bf16 batches added straight into S take the 64-tile kernel, whose
-// time is the read-modify-write of S's upper triangle.
+// Thin batches added straight into S take the 64-tile kernel, whose time is
+// the read-modify-write of S's upper triangle.
 constexpr int kThinTile = 64;
 bool use_thin(const hess_s* h, int64_t n, bool vec) {
-  if (h->dtype != HESS_BF16 || !vec || n > kSyrkThinMaxN) return false;
+  if (!vec || n > kSyrkThinMaxN) return false;
   return g_tile_override == 0 || g_tile_override == kThinTile;
 }
 
@@ -352,7 +352,7 @@ int run_thin(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s) {
     e = timing_begin(h, s);
     if (e != hipSuccess) return hip_fail(e, "timing event");
   }
-  e = launch_syrk_thin(X, ld, n, (int)h->d, h->S, h->d, s);
+  e = launch_syrk_thin(X, h->dtype, ld, n, (int)h->d, h->S, h->d, s);
   if (e != hipSuccess) return hip_fail(e, "thin SYRK launch");
   if (h->timing) {
     e = timing_end(h, s, n);

@@ -122,12 +122,13 @@ hipError_t launch_gather_rows_t8(const GatherParams& P, hipStream_t stream);
 hipError_t launch_imatrix(const void* X, int in_dtype, int64_t n, int d, int64_t ld, bool vec, float* part,
                           int max_splits, float* acc, hipStream_t stream);
 
-// Thin batches straight into S (bf16, X 16-byte aligned, ld * 2 % 16 == 0,
-// d % 8 == 0, n <= kSyrkThinMaxN): 64 x 64 upper-triangle tiles, one
-// workgroup each, no split and no workspace.
+// Thin batches straight into S (bf16 or float32 rows, X 16-byte aligned,
+// ld * esize % 16 == 0, d % 8 == 0, n <= kSyrkThinMaxN): 64 x 64
+// upper-triangle tiles, one workgroup each, no split and no workspace.
 constexpr int64_t kSyrkThinMaxN = 512;
 int64_t syrk_thin_tiles(int d);
-hipError_t launch_syrk_thin(const void* X, int64_t ld, int64_t n, int d, float* S, int64_t lds, hipStream_t stream);
+hipError_t launch_syrk_thin(const void* X, int in_dtype, int64_t ld, int64_t n, int d, float* S, int64_t lds,
+                            hipStream_t stream);
 
 int syrk_tile_edge();
 hipError_t launch_syrk(const SyrkParams& P, int in_dtype, bool vec, int grid, hipStream_t stream);

@@ -1,4 +1,5 @@
-// Symmetric rank-k update for thin bf16 batches, shaped for memory bandwidth:
+// Symmetric rank-k update for thin batches (bf16 or float32 rows), shaped for
+// memory bandwidth:
 //
 //   S[i][j] += sum_t X[t][i] * X[t][j]      for the upper-triangle tiles (j >= i)
 //
@@ -38,8 +39,10 @@ namespace {
 
 constexpr int kTE = 64;                 // tile edge
 constexpr int kTS = 32;                 // tokens per step
-constexpr int kRowPad = 144;            // LDS bytes per token row of a panel (128 used)
-constexpr int kPanel = kTS * kRowPad;   // one panel of a step
+constexpr int kRowPad = 144;            // LDS bytes per token row of a bf16 panel (128 used)
+constexpr int kPanel = kTS * kRowPad;   // one bf16 panel of a step
+constexpr int kRowPadF = 272;           // ... of a float32 panel (256 used)
+constexpr int kPanelF = kTS * kRowPadF;
 constexpr uint32_t kFar = 0x80000000u;  // an offset past any descriptor's range
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t thin_rsrc(const void* base, int64_t bytes) {
@@ -63,10 +66,16 @@ __device__ __forceinline__ u32x4 thin_operand(const char* p) {
 // LDS of one workgroup: the two panels of a step during the products, then
 // the tile's 64 x 64 sums (row stride kAccLd floats) for the output.
 constexpr int kAccLd = kTE + 4;
-constexpr int kThinLds = kTE * kAccLd * 4 > 2 * kPanel ? kTE * kAccLd * 4 : 2 * kPanel;
+constexpr int kThinLds = kTE * kAccLd * 4 > 2 * kPanelF ? kTE * kAccLd * 4 : 2 * kPanelF;
 
-__global__ void __launch_bounds__(256) syrk_thin_bf16(const char* __restrict__ X, int64_t ld_bytes, int n, int d,
-                                                      float* __restrict__ S, int64_t lds) {
+// F32: float32 rows (4 features per 16-byte load, two loads per thread and
+// panel; the panels hold the raw words, token-major, and each 4-token slice
+// of a step is one v_mfma_f32_16x16x4_f32 per accumulator, exact products).
+template <bool F32>
+__global__ void __launch_bounds__(256) syrk_thin(const char* __restrict__ X, int64_t ld_bytes, int n, int d,
+                                                 float* __restrict__ S, int64_t lds) {
+  constexpr int kRow = F32 ? kRowPadF : kRowPad;
+  constexpr int kPan = F32 ? kPanelF : kPanel;
   __shared__ __attribute__((aligned(16))) char lbuf[kThinLds];
   // workgroup b -> tile (I, J), I <= J: b = J (J + 1) / 2 + I
   const int b = blockIdx.x;
@@ -79,19 +88,30 @@ __global__ void __launch_bounds__(256) syrk_thin_bf16(const char* __restrict__ X
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wr = w >> 1, wc = w & 1;
 
-  // activation loads: thread t moves features 8 (t % 8) .. +7 of token t / 8
-  // of the step, for panel I and (off the diagonal) panel J
-  const int tk = t >> 3, ch = t & 7;
-  const int fI = I * kTE + 8 * ch, fJ = J * kTE + 8 * ch;
-  const uint32_t vI = fI < d ? (uint32_t)(tk * ld_bytes + fI * 2) : kFar;
-  const uint32_t vJ = fJ < d ? (uint32_t)(tk * ld_bytes + fJ * 2) : kFar;
-  auto load = [&](int k0, u32x4& a, u32x4& c) {
+  // activation loads of a step, for panel I and (off the diagonal) panel J:
+  // bf16, thread t moves features 8 (t % 8) .. +7 of token t / 8; float32,
+  // features 4 (t % 16) .. +3 of tokens t / 16 and t / 16 + 16
+  constexpr int kFeat = F32 ? 4 : 8, kEs = F32 ? 4 : 2, kLoads = F32 ? 2 : 1;
+  const int tk = F32 ? t >> 4 : t >> 3, ch = F32 ? t & 15 : t & 7;
+  const int fI = I * kTE + kFeat * ch, fJ = J * kTE + kFeat * ch;
+  uint32_t vI[kLoads], vJ[kLoads];
+#pragma unroll
+  for (int h = 0; h < kLoads; ++h) {
+    vI[h] = fI < d ? (uint32_t)((tk + 16 * h) * ld_bytes + fI * kEs) : kFar;
+    vJ[h] = fJ < d ? (uint32_t)((tk + 16 * h) * ld_bytes + fJ * kEs) : kFar;
+  }
+  u32x4 xa[kLoads], xc[kLoads];
+  auto load = [&](int k0) {
     const __amdgpu_buffer_rsrc_t r = thin_rsrc(X + (int64_t)k0 * ld_bytes, (int64_t)min(kTS, n - k0) * ld_bytes);
-    a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vI, 0, 0));
-    if (!diag) c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vJ, 0, 0));
+#pragma unroll
+    for (int h = 0; h < kLoads; ++h) {
+      xa[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vI[h], 0, 0));
+      if (!diag) xc[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vJ[h], 0, 0));
+    }
   };
-  u32x4 xa, xc = u32x4{0u, 0u, 0u, 0u};
-  load(0, xa, xc);
+#pragma unroll
+  for (int h = 0; h < kLoads; ++h) xc[h] = u32x4{0u, 0u, 0u, 0u};
+  load(0);
 
   // S entries of thread t: tile rows t / 16 + 16 k (k < 4), columns
   // 4 (t % 16) .. +3, so that 16 lanes cover one 256-byte tile row
@@ -107,13 +127,15 @@ __global__ void __launch_bounds__(256) syrk_thin_bf16(const char* __restrict__ X
     sv[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(sr, so[k], 0, 0));
   }
 
-  // operand addresses (see thin_operand): 16-lane group g reads tokens
-  // 8 g + (lane % 16) / 4, features f0 + 4 (lane % 4)
-  const int tl = 8 * (lane >> 4) + ((lane & 15) >> 2);
-  const char* pa = lbuf + tl * kRowPad + (32 * wr + 4 * (lane & 3)) * 2;
-  const char* pb = lbuf + (diag ? 0 : kPanel) + tl * kRowPad + (32 * wc + 4 * (lane & 3)) * 2;
-  char* const wI = lbuf + tk * kRowPad + ch * 16;
-  char* const wJ = wI + kPanel;
+  // operand addresses.  bf16 (see thin_operand): 16-lane group g reads
+  // tokens 8 g + (lane % 16) / 4, features f0 + 4 (lane % 4).  float32: lane
+  // l reads token 4 s + l / 16 of slice s, feature f0 + l % 16.
+  const int tl = F32 ? (lane >> 4) : 8 * (lane >> 4) + ((lane & 15) >> 2);
+  const int fl = F32 ? (lane & 15) : 4 * (lane & 3);
+  const char* pa = lbuf + tl * kRow + (32 * wr + fl) * kEs;
+  const char* pb = lbuf + (diag ? 0 : kPan) + tl * kRow + (32 * wc + fl) * kEs;
+  char* const wI = lbuf + tk * kRow + ch * 16;
+  char* const wJ = wI + kPan;
 
   // wave (wr, wc) sums the quadrant rows 32 wr .., columns 32 wc ..; on a
   // diagonal tile the below-diagonal quadrant is summed too (the same
@@ -124,20 +146,40 @@ __global__ void __launch_bounds__(256) syrk_thin_bf16(const char* __restrict__ X
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x4{};
   for (int k0 = 0; k0 < n; k0 += kTS) {
-    *reinterpret_cast<u32x4*>(wI) = xa;
-    if (!diag) *reinterpret_cast<u32x4*>(wJ) = xc;
-    __syncthreads();
-    if (k0 + kTS < n) load(k0 + kTS, xa, xc);
-    u32x4 a[2], c[2];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      a[p] = thin_operand(pa + 32 * p);
-      c[p] = thin_operand(pb + 32 * p);
+    for (int h = 0; h < kLoads; ++h) {
+      *reinterpret_cast<u32x4*>(wI + 16 * h * kRow) = xa[h];
+      if (!diag) *reinterpret_cast<u32x4*>(wJ + 16 * h * kRow) = xc[h];
     }
+    __syncthreads();
+    if (k0 + kTS < n) load(k0 + kTS);
+    if constexpr (F32) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int sl = 0; sl < kTS / 4; ++sl) {
+        float a[2], c[2];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma16x16x32(c[cb], a[rb], acc[rb][cb]);
+        for (int p = 0; p < 2; ++p) {
+          a[p] = *reinterpret_cast<const float*>(pa + 4 * sl * kRow + 16 * p * 4);
+          c[p] = *reinterpret_cast<const float*>(pb + 4 * sl * kRow + 16 * p * 4);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(c[cb], a[rb], acc[rb][cb], 0, 0, 0);
+      }
+    } else {
+      u32x4 a[2], c[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        a[p] = thin_operand(pa + 32 * p);
+        c[p] = thin_operand(pb + 32 * p);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma16x16x32(c[cb], a[rb], acc[rb][cb]);
+    }
     __syncthreads();
   }
   // the sums through LDS into the row layout of the S accesses: lane l of
@@ -169,15 +211,21 @@ int64_t syrk_thin_tiles(int d) {
   return nb * (nb + 1) / 2;
 }
 
-hipError_t launch_syrk_thin(const void* X, int64_t ld, int64_t n, int d, float* S, int64_t lds, hipStream_t stream) {
+hipError_t launch_syrk_thin(const void* X, int in_dtype, int64_t ld, int64_t n, int d, float* S, int64_t lds,
+                            hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int64_t tiles = syrk_thin_tiles(d);
-  if (n > kSyrkThinMaxN || d % 8 != 0 || (reinterpret_cast<uintptr_t>(X) & 15u) != 0 || ((ld * 2) & 15) != 0 ||
-      ld * 2 * kTS >= ((int64_t)1 << 31) || lds % 4 != 0 || lds * 4 * kTE >= ((int64_t)1 << 31) ||
+  const int es = in_dtype == kInF32 ? 4 : 2;
+  if (n > kSyrkThinMaxN || d % 8 != 0 || (reinterpret_cast<uintptr_t>(X) & 15u) != 0 || ((ld * es) & 15) != 0 ||
+      ld * es * kTS >= ((int64_t)1 << 31) || lds % 4 != 0 || lds * 4 * kTE >= ((int64_t)1 << 31) ||
       tiles >= ((int64_t)1 << 31))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(syrk_thin_bf16, dim3((unsigned)tiles), dim3(256), 0, stream, static_cast<const char*>(X), ld * 2,
-                     (int)n, d, S, lds);
+  if (in_dtype == kInF32)
+    hipLaunchKernelGGL(syrk_thin<true>, dim3((unsigned)tiles), dim3(256), 0, stream, static_cast<const char*>(X),
+                       ld * es, (int)n, d, S, lds);
+  else
+    hipLaunchKernelGGL(syrk_thin<false>, dim3((unsigned)tiles), dim3(256), 0, stream, static_cast<const char*>(X),
+                       ld * es, (int)n, d, S, lds);
   return hipGetLastError();
 }
 

@@ -254,7 +254,8 @@ int hess_token_count(hess_t h, int64_t* n_out);
  * tiles used by hess_add_batch (0 = automatic choice per call, 64, 128, or
  * 256).  256-tiles apply to bf16 handles with d % 8 == 0 and 16-byte aligned
  * rows; 64-tiles (the thin-batch kernel, whose time is the read-modify-write
- * of S) to the same handles and rows for passes of at most 512 tokens;
+ * of S) to bf16 and float32 handles with d % 8 == 0 and 16-byte aligned rows
+ * for passes of at most 512 tokens;
  * other calls keep 128-tiles.  The automatic choice takes 64-tiles for such
  * passes of at most 512 tokens, and 256-tiles at d >= 1,024 when a pass
  * (one batch, or one staging flush) gives each of the 256 workgroups at

@@ -105,16 +105,17 @@ def test_forced_tile_edges(edge):
     check_against_oracle(wl)
 
 
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
 @pytest.mark.parametrize("override", [0, 64])
 @pytest.mark.parametrize("d", [8, 64, 72, 264, 1000, 2056])
-def test_thin_tiles(d, override):
+def test_thin_tiles(d, override, dtype):
     """Batches added straight into S: the 64-tile kernel up to 512 tokens (edge
     and diagonal tiles, partial 32-token steps), the 128- or 256-tile kernels
     from 513 on."""
-    _say(f"thin 64-tile d={d} override={override}")
+    _say(f"thin 64-tile d={d} override={override} {dtype}")
     hs.set_tile_override(override)
     hs.set_staging(False)
-    wl = W.ragged_case(d, [1, 5, 31, 32, 33, 100, 0, 511, 512, 513], seed=900 + d, dtype=W.BF16, dead_frac=0.02)
+    wl = W.ragged_case(d, [1, 5, 31, 32, 33, 100, 0, 511, 512, 513], seed=900 + d, dtype=dtype, dead_frac=0.02)
     check_against_oracle(wl)
 
 
