@@ -171,7 +171,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--extras", default="all",
                     help="comma-separated subset of d4096_ragged,d4096_single,moe,local,imatrix,f16_staging,chol,quant,"
-                         "thin "
+                         "thin,graph "
                          "(default all; imatrix runs with local)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--print-kernel-sha", action="store_true",
@@ -279,7 +279,7 @@ def run_extras(torch, hs, W, args):
     steps = max(3, args.steps // 2)
     want = set(args.extras.split(",")) if args.extras != "all" else {"d4096_ragged", "d4096_single", "moe", "local",
                                                                     "imatrix", "f16_staging", "chol", "quant",
-                                                                    "thin"}
+                                                                    "thin", "graph"}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if "quant" in want:
         # error-propagating 4-bit quantization of a 4096 x 4096 layer (groups of 128), float64
@@ -466,6 +466,46 @@ def run_extras(torch, hs, W, args):
                                            "hbm_frac": round(byts / (per * 1e-3) / HBM, 4)}
             m.close()
         del xs
+    if "graph" in want:
+        # the headline Hessian (reset, 360 add_batch calls, materialize) captured once in a HIP graph
+        # and replayed: the same kernels without the host's per-call launch path
+        log("headline Hessian as a replayed graph")
+        dg = 2560
+        buf, views, _ = ragged_setup(torch, W, dg, seed=1)
+        outg = torch.empty((dg, dg), dtype=torch.float32, device="cuda")
+        hg = hs.Hessian(dg, torch.bfloat16)
+
+        def one_g():
+            hg.reset()
+            for x in views:
+                hg.add_batch(x)
+            hg.materialize(0.01, out=outg)
+
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            one_g()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        ref = outg.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cs):
+            one_g()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(outg, ref))
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        reps = max(3, steps)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        extra["headline_graph_replay"] = {"ms": round(e0.elapsed_time(e1) / reps, 4), "equal_to_eager": same}
+        del graph, hg, buf, views
     if "thin" in want:
         # thin batches added straight into S (a handle without staging): the 64-tile kernel, whose
         # time is the read-modify-write of S's upper triangle (4 d (d + 1) bytes) plus the batch

@@ -642,6 +642,50 @@ def test_grouped_equals_single_handle_runs():
         grouped[e].close()
 
 
+@pytest.mark.parametrize("d,sizes", [(1032, [100, 700, 1, 2000, 5]), (264, [30, 1, 300])])
+def test_graph_capture_replays_equal_eager(d, sizes):
+    """A whole Hessian (reset, staged and long batches, materialize) captured in
+    a graph: every replay, with eager work and synchronizations between the
+    replays, equals the eager result bit for bit."""
+    _say(f"graph capture d={d}")
+    wl = W.ragged_case(d, sizes, seed=41 + d, dtype=W.BF16, dead_frac=0.02)
+    xs = [to_device(b, W.BF16) for b in wl.batches]
+    out = torch.empty((d, d), dtype=torch.float32, device="cuda")
+    h = hs.Hessian(d, torch.bfloat16)
+
+    def one():
+        h.reset()
+        for x in xs:
+            h.add_batch(x)
+        h.materialize(0.01, out=out)
+
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        one()
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    Hr, _, _, _ = run_oracle(wl)
+    assert agreement(ref.cpu().numpy(), Hr) <= TOL[W.BF16]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cs):
+        one()
+    other = hs.Hessian(d, torch.bfloat16, staging_bytes=0)
+    for r in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r}"
+        other.add_batch(xs[0])              # eager work between replays
+        other.materialize(0.0)
+        torch.cuda.synchronize()
+    other.close()
+    del graph
+    h.close()
+
+
 def test_kernel_timing_counts_launches():
     _say("SYRK launch timing")
     h = hs.Hessian(512, torch.bfloat16)
