@@ -12,10 +12,16 @@
  * - The Gram sum S, H_out, local blocks and dead masks are device memory.
  *   Pointers marked (host) are host memory.
  * - Every device operation is enqueued on the given HIP stream
- *   (hipStream_t passed as hess_stream_t; NULL is the null stream).  No call
- *   synchronizes with the host or allocates device memory after
- *   hess_create(), so the calls may be captured into a HIP graph.  X must
- *   stay valid and unchanged until the stream has executed the call.
+ *   (hipStream_t passed as hess_stream_t; NULL is the null stream).  Apart
+ *   from create and destroy calls, hess_timing and hess_add_batch_grouped,
+ *   no call synchronizes with the host or allocates device memory, so those
+ *   calls (batches, casts, flush, reset, materialize, adopt, local blocks,
+ *   imatrix, the Cholesky factor, the block quantize) may be captured into a
+ *   HIP graph.  hess_add_batch_grouped builds each launch's schedule on the
+ *   host, sends it through a pinned buffer after the previous call's copy
+ *   has finished, and sizes the device's gather buffer on first use: it is
+ *   not for capture.  X must stay valid and unchanged until the stream has
+ *   executed the call.
  * - A handle remembers the stream of its last call.  A call on a different
  *   stream first makes that stream wait for the previous one (an event), so
  *   updates of one Hessian never overlap.  Different handles are independent.
