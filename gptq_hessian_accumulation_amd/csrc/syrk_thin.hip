@@ -154,6 +154,13 @@ __global__ void __launch_bounds__(256) syrk_thin(const char* __restrict__ X, int
     __syncthreads();
     if (k0 + kTS < n) load(k0 + kTS);
     if constexpr (F32) {
+      // the step's 8 slices sum into a fresh accumulator that is then added
+      // to the running one, so no float32 chain exceeds 8 + n / 32 additions
+      f32x4 st[2][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) st[rb][cb] = f32x4{};
 #pragma unroll
       for (int sl = 0; sl < kTS / 4; ++sl) {
         float a[2], c[2];
@@ -166,8 +173,12 @@ __global__ void __launch_bounds__(256) syrk_thin(const char* __restrict__ X, int
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(c[cb], a[rb], acc[rb][cb], 0, 0, 0);
+            st[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(c[cb], a[rb], st[rb][cb], 0, 0, 0);
       }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] += st[rb][cb];
     } else {
       u32x4 a[2], c[2];
 #pragma unroll

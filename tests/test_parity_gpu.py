@@ -220,7 +220,7 @@ def _sampled_gram_check(h, wl, n_samples=400, seed=0):
     up_r, up_c = np.minimum(rows, cols), np.maximum(rows, cols)
     diag = np.arange(d)
     r_all, c_all = np.concatenate([up_r, diag]), np.concatenate([up_c, diag])
-    ref = O.gram_entries(wl.batches, W.BF16, r_all, c_all)
+    ref = O.gram_entries(wl.batches, wl.dtype, r_all, c_all)
     got = S[torch.from_numpy(r_all).cuda(), torch.from_numpy(c_all).cuda()].double().cpu().numpy()
     N = wl.total_tokens
     mean_diag = float(np.mean(ref[len(up_r):])) * 2.0 / N
@@ -241,6 +241,24 @@ def test_big_tiles_full_size_sampled(d, n):
     assert h.nsamples == n
     assert err <= TOL[W.BF16], err
     h.close()
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_thin_tiles_widest_sampled(dtype):
+    """The thin-batch kernel at width 32,768 (131,328 tiles of 64, a 4 GiB sum):
+    batches of 1, 64 and 300 tokens straight into S, on sampled entries."""
+    _say(f"thin 64-tile d=32768 {dtype}")
+    hs.set_staging(False)
+    d = 32768
+    wl = W.ragged_case(d, [1, 64, 300], seed=3276, dtype=dtype, dead_frac=0.0)
+    h = hs.Hessian(d, torch_dtype(dtype), staging_bytes=0)
+    for b in wl.batches:
+        h.add_batch(to_device(b, dtype))
+    err = _sampled_gram_check(h, wl)
+    assert h.nsamples == 365
+    assert err <= TOL[dtype], err
+    h.close()
+    torch.cuda.empty_cache()
 
 
 def test_transposed_staging_full_flush_sampled():
