@@ -11,7 +11,8 @@
 // (4 d (d + 1) bytes) sets the time:
 //
 //  * 64 x 64 tiles, one workgroup of 4 waves each (a 32 x 32 quadrant per
-//    wave, 2 x 2 accumulators of v_mfma_f32_16x16x32_bf16): many small
+//    wave, 2 x 2 accumulators of v_mfma_f32_16x16x32_bf16, or of
+//    v_mfma_f32_16x16x4_f32 for float32 rows): many small
 //    workgroups resident per CU keep the most S traffic in flight, and the
 //    tile count (2,080 at width 4,096) spreads evenly over the 256 CUs.
 //  * The tile's S entries are requested right after the first step's
@@ -23,9 +24,10 @@
 //    the accumulators' own layout (16 rows of 64 bytes per instruction).
 //  * The activations of one 32-token step (two 32 x 64 panels, one on a
 //    diagonal tile) go from memory into registers (one 16-byte load per
-//    thread and panel, the next step's issued before this step's products)
-//    and through LDS, token-major with a padded row; the matrix operands (8
-//    tokens of one feature) are read transposed with ds_read_b64_tr_b16.
+//    thread and panel for bf16, two for float32; the next step's issued
+//    before this step's products) and through LDS, token-major with a padded
+//    row.  bf16 operands (8 tokens of one feature) are read transposed with
+//    ds_read_b64_tr_b16; a float32 operand is one word per lane.
 //  * Buffer descriptors end at the batch's last row and features past d get
 //    an out-of-range offset, so loads need no masks; S entries past d are
 //    neither read nor written.
