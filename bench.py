@@ -184,7 +184,7 @@ def main():
         print("syrk_big", kernel_source_sha256(BIG_KERNEL_SOURCES))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the Hessian path runs on a single MI355X).", file=sys.stderr)
         sys.exit(2)
 
