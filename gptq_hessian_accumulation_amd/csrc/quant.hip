@@ -143,6 +143,20 @@ __global__ void __launch_bounds__(256) q_rows(double* __restrict__ Wd, int ldd, 
   __shared__ double invd[kQB];
   const int group = GC >= 0 ? GC : group_rt;
   const int nb = FULL ? kQB : min(kQB, K - i1);
+  const int lane = threadIdx.x & 63, j = lane & 15;
+  const int slot = (threadIdx.x >> 6) * 4 + (lane >> 4);  // row slot in the workgroup
+  const int r = blockIdx.x * kRowsPerWg + slot;
+  const bool live = r < N;
+  const int base = lane & 48;
+  // this lane's row entries and step are requested first, so that their
+  // latency overlaps the staging of the factor slice below
+  double wr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c = j + 16 * k;
+    wr[k] = (live && c < nb) ? Wd[(int64_t)r * ldd + i1 + c] : 0.0;
+  }
+  double s = (!group && live) ? step[r] : 1.0;
   {
     // all of a thread's loads in flight before its first store: thread t takes
     // column t % 128 of rows t / 128 + 2 q (q < 64)
@@ -159,18 +173,6 @@ __global__ void __launch_bounds__(256) q_rows(double* __restrict__ Wd, int ldd, 
   if (threadIdx.x < kQB)
     invd[threadIdx.x] = threadIdx.x < nb ? 1.0 / (double)U[(int64_t)(i1 + threadIdx.x) * ldu + i1 + threadIdx.x] : 0.0;
   __syncthreads();
-  const int lane = threadIdx.x & 63, j = lane & 15;
-  const int slot = (threadIdx.x >> 6) * 4 + (lane >> 4);  // row slot in the workgroup
-  const int r = blockIdx.x * kRowsPerWg + slot;
-  const bool live = r < N;
-  const int base = lane & 48;
-  double wr[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int c = j + 16 * k;
-    wr[k] = (live && c < nb) ? Wd[(int64_t)r * ldd + i1 + c] : 0.0;
-  }
-  double s = (!group && live) ? step[r] : 1.0;
   double inv_s = 1.0 / s;
   double sk[8];  // the step of each held column's group
 #pragma unroll
