@@ -10,7 +10,9 @@
 // Gram diagonal is exactly zero; its row and column are zero already and its
 // diagonal becomes 1, so neutralization precedes the mean.
 //
-// Two kernels:
+// Two kernels (one when H does not alias S and d <= 4,096: then every
+// workgroup of the tiled pass does step 1's reduction itself, in the same
+// order, and the first one writes the dead mask and the damping):
 //  1. one workgroup reads the d diagonal entries, writes the dead mask and
 //     reduces the (neutralized) diagonal in float64 in a fixed order; the
 //     damping is that mean times damp_percent, rounded once to float32;
@@ -27,30 +29,36 @@ namespace hess {
 
 namespace {
 
-constexpr int kDiagThreads = 1024;
+constexpr int kDiagThreads = 256;
+
+// damp_percent * mean of the (neutralized) scaled diagonal, in float64 in a
+// fixed order: thread t sums entries t, t + 256, ..., then wave shuffles, then
+// the 4 wave partials in order.  Every caller gets the same bits.  part: 4
+// doubles of LDS.  The result is valid in every thread after the call.
+__device__ __forceinline__ float diag_damp(const float* S, int64_t lds, int d, float scale, float damp_percent,
+                                           int neutralize, double* part) {
+  double sum = 0.0;
+  for (int j = threadIdx.x; j < d; j += kDiagThreads) {
+    const float s = S[(int64_t)j * lds + j];
+    const bool dj = neutralize && (s == 0.0f);
+    sum += (double)(dj ? 1.0f : s * scale);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_down(sum, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sum;
+  __syncthreads();
+  double tot = 0.0;
+  for (int w = 0; w < kDiagThreads / 64; ++w) tot += part[w];
+  return (float)((double)damp_percent * (tot / (double)d));
+}
 
 __global__ void __launch_bounds__(kDiagThreads) diag_kernel(const float* S, int64_t lds, int d, float scale,
                                                             float damp_percent, int neutralize, uint8_t* dead,
                                                             float* damp_dev) {
   __shared__ double part[kDiagThreads / 64];
-  double sum = 0.0;
-  for (int j = threadIdx.x; j < d; j += kDiagThreads) {
-    const float s = S[(int64_t)j * lds + j];
-    const bool dj = neutralize && (s == 0.0f);
-    dead[j] = dj ? 1 : 0;
-    const float h = dj ? 1.0f : s * scale;
-    sum += (double)h;
-  }
-  // fixed-order reduction: wave shuffles, then wave partials in order
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_down(sum, off, 64);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sum;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double tot = 0.0;
-    for (int w = 0; w < kDiagThreads / 64; ++w) tot += part[w];
-    damp_dev[0] = (float)((double)damp_percent * (tot / (double)d));
-  }
+  for (int j = threadIdx.x; j < d; j += kDiagThreads) dead[j] = (neutralize && S[(int64_t)j * lds + j] == 0.0f) ? 1 : 0;
+  const float damp = diag_damp(S, lds, d, scale, damp_percent, neutralize, part);
+  if (threadIdx.x == 0) damp_dev[0] = damp;
 }
 
 constexpr int kT = 64;  // tile edge
@@ -106,11 +114,18 @@ __global__ void __launch_bounds__(256) mirror_kernel(const float* S, int64_t lds
 // 16-byte aligned): thread t moves columns 4 (t % 16) .. +3 of tile rows
 // t / 16 + 16 k (k < 4), so 16 lanes cover one 256-byte tile row; the tile's
 // row and column dead flags are read once into LDS.
+// FUSED: H does not alias S and d is small enough for every workgroup to
+// read the whole diagonal: each workgroup takes the damping and its tile's
+// dead flags from S itself (the same fixed-order sum as diag_kernel, so the
+// same bits), and workgroup 0 writes the dead mask and the damping out, so
+// materialize is one launch.
+template <bool FUSED>
 __global__ void __launch_bounds__(256) mirror_kernel_vec(const float* S, int64_t lds, int d, float scale,
-                                                         const uint8_t* dead, const float* damp_dev, float* H,
-                                                         int nt) {
+                                                         float damp_percent, int neutralize, uint8_t* dead,
+                                                         float* damp_dev, float* H, int nt) {
   __shared__ float tile[kT][kT + 1];
   __shared__ uint8_t dR[kT], dC[kT];
+  __shared__ double part[kDiagThreads / 64];
   // blockIdx.x -> (I, J), I <= J: blockIdx.x = J (J + 1) / 2 + I
   const int b = blockIdx.x;
   int J = (int)((sqrtf(8.0f * (float)b + 1.0f) - 1.0f) * 0.5f);
@@ -118,10 +133,22 @@ __global__ void __launch_bounds__(256) mirror_kernel_vec(const float* S, int64_t
   while ((J + 1) * (J + 2) / 2 <= b) ++J;
   const int I = b - J * (J + 1) / 2;
   const int r0 = I * kT, c0 = J * kT;
-  const float damp = damp_dev[0];
   const int t = threadIdx.x, cq = 4 * (t & 15), rr = t >> 4;
-  if (t < kT) dR[t] = r0 + t < d ? dead[r0 + t] : 0;
-  else if (t < 2 * kT) dC[t - kT] = c0 + t - kT < d ? dead[c0 + t - kT] : 0;
+  float damp;
+  if constexpr (FUSED) {
+    auto is_dead = [&](int j) { return neutralize && S[(int64_t)j * lds + j] == 0.0f; };
+    if (t < kT) dR[t] = r0 + t < d ? is_dead(r0 + t) : 0;
+    else if (t < 2 * kT) dC[t - kT] = c0 + t - kT < d ? is_dead(c0 + t - kT) : 0;
+    damp = diag_damp(S, lds, d, scale, damp_percent, neutralize, part);
+    if (b == 0) {
+      for (int j = t; j < d; j += 256) dead[j] = is_dead(j) ? 1 : 0;
+      if (t == 0) damp_dev[0] = damp;
+    }
+  } else {
+    damp = damp_dev[0];
+    if (t < kT) dR[t] = r0 + t < d ? dead[r0 + t] : 0;
+    else if (t < 2 * kT) dC[t - kT] = c0 + t - kT < d ? dead[c0 + t - kT] : 0;
+  }
   // stage the S tile (rows r0.., cols c0..); of the diagonal tile only the
   // upper part (c >= r) is read
 #pragma unroll
@@ -188,19 +215,29 @@ hipError_t launch_zero_upper(float* S, int64_t lds, int d, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Widest d for the one-launch materialize: every workgroup reads the d
+// diagonal entries (16 KB at 4,096, from L2) besides its tile.
+constexpr int kFusedMaxD = 4096;
+
 hipError_t launch_materialize(const float* S, int64_t lds, int d, float scale, float damp_percent, int neutralize,
                               float* H, uint8_t* dead, float* damp_dev, double* /*sum_scratch*/,
                               hipStream_t stream) {
-  hipLaunchKernelGGL(diag_kernel, dim3(1), dim3(kDiagThreads), 0, stream, S, lds, d, scale, damp_percent,
-                     neutralize, dead, damp_dev);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int nt = (d + kT - 1) / kT;
   const int tiles = nt * (nt + 1) / 2;
   const bool vec = d % 4 == 0 && lds % 4 == 0 && (reinterpret_cast<uintptr_t>(S) & 15u) == 0 &&
                    (reinterpret_cast<uintptr_t>(H) & 15u) == 0;
+  if (vec && H != S && d <= kFusedMaxD) {
+    hipLaunchKernelGGL(mirror_kernel_vec<true>, dim3(tiles), dim3(256), 0, stream, S, lds, d, scale, damp_percent,
+                       neutralize, dead, damp_dev, H, nt);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(diag_kernel, dim3(1), dim3(kDiagThreads), 0, stream, S, lds, d, scale, damp_percent,
+                     neutralize, dead, damp_dev);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (vec)
-    hipLaunchKernelGGL(mirror_kernel_vec, dim3(tiles), dim3(256), 0, stream, S, lds, d, scale, dead, damp_dev, H, nt);
+    hipLaunchKernelGGL(mirror_kernel_vec<false>, dim3(tiles), dim3(256), 0, stream, S, lds, d, scale, damp_percent,
+                       neutralize, dead, damp_dev, H, nt);
   else
     hipLaunchKernelGGL(mirror_kernel, dim3(tiles), dim3(256), 0, stream, S, lds, d, scale, dead, damp_dev, H, nt);
   return hipGetLastError();
