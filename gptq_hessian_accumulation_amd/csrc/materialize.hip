@@ -10,7 +10,7 @@
 // Gram diagonal is exactly zero; its row and column are zero already and its
 // diagonal becomes 1, so neutralization precedes the mean.
 //
-// Two kernels (one when H does not alias S and d <= 4,096: then every
+// Two kernels (one when H does not alias S and d <= 2,048: then every
 // workgroup of the tiled pass does step 1's reduction itself, in the same
 // order, and the first one writes the dead mask and the damping):
 //  1. one workgroup reads the d diagonal entries, writes the dead mask and
@@ -216,8 +216,10 @@ hipError_t launch_zero_upper(float* S, int64_t lds, int d, hipStream_t stream) {
 }
 
 // Widest d for the one-launch materialize: every workgroup reads the d
-// diagonal entries (16 KB at 4,096, from L2) besides its tile.
-constexpr int kFusedMaxD = 4096;
+// diagonal entries (one L2 line each) besides its tile, which costs more
+// than the second launch saves above this width (measured per materialize:
+// 13.6 against 15.5 us at 2,048, 16.5 against 14.3 us at 2,560).
+constexpr int kFusedMaxD = 2048;
 
 hipError_t launch_materialize(const float* S, int64_t lds, int d, float scale, float damp_percent, int neutralize,
                               float* H, uint8_t* dead, float* damp_dev, double* /*sum_scratch*/,
