@@ -29,16 +29,19 @@ namespace hess {
 
 namespace {
 
-constexpr int kDiagThreads = 256;
+constexpr int kDiagThreads = 256;       // the one-launch path's workgroup (and its sum order)
+constexpr int kDiagThreadsWide = 1024;  // the diagonal pass above that path's widths
 
 // damp_percent * mean of the (neutralized) scaled diagonal, in float64 in a
-// fixed order: thread t sums entries t, t + 256, ..., then wave shuffles, then
-// the 4 wave partials in order.  Every caller gets the same bits.  part: 4
-// doubles of LDS.  The result is valid in every thread after the call.
+// fixed order for NT threads: thread t sums entries t, t + NT, ..., then wave
+// shuffles, then the NT / 64 wave partials in order.  Every caller with the
+// same NT gets the same bits.  part: NT / 64 doubles of LDS.  The result is
+// valid in every thread after the call.
+template <int NT>
 __device__ __forceinline__ float diag_damp(const float* S, int64_t lds, int d, float scale, float damp_percent,
                                            int neutralize, double* part) {
   double sum = 0.0;
-  for (int j = threadIdx.x; j < d; j += kDiagThreads) {
+  for (int j = threadIdx.x; j < d; j += NT) {
     const float s = S[(int64_t)j * lds + j];
     const bool dj = neutralize && (s == 0.0f);
     sum += (double)(dj ? 1.0f : s * scale);
@@ -48,16 +51,19 @@ __device__ __forceinline__ float diag_damp(const float* S, int64_t lds, int d, f
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sum;
   __syncthreads();
   double tot = 0.0;
-  for (int w = 0; w < kDiagThreads / 64; ++w) tot += part[w];
+  for (int w = 0; w < NT / 64; ++w) tot += part[w];
   return (float)((double)damp_percent * (tot / (double)d));
 }
 
-__global__ void __launch_bounds__(kDiagThreads) diag_kernel(const float* S, int64_t lds, int d, float scale,
-                                                            float damp_percent, int neutralize, uint8_t* dead,
-                                                            float* damp_dev) {
-  __shared__ double part[kDiagThreads / 64];
-  for (int j = threadIdx.x; j < d; j += kDiagThreads) dead[j] = (neutralize && S[(int64_t)j * lds + j] == 0.0f) ? 1 : 0;
-  const float damp = diag_damp(S, lds, d, scale, damp_percent, neutralize, part);
+// NT = kDiagThreads at the one-launch path's widths (so that an in-place
+// materialize, which takes this path, gives the same bits), else
+// kDiagThreadsWide (shorter per-thread chains on a wide diagonal).
+template <int NT>
+__global__ void __launch_bounds__(NT) diag_kernel(const float* S, int64_t lds, int d, float scale,
+                                                  float damp_percent, int neutralize, uint8_t* dead, float* damp_dev) {
+  __shared__ double part[NT / 64];
+  for (int j = threadIdx.x; j < d; j += NT) dead[j] = (neutralize && S[(int64_t)j * lds + j] == 0.0f) ? 1 : 0;
+  const float damp = diag_damp<NT>(S, lds, d, scale, damp_percent, neutralize, part);
   if (threadIdx.x == 0) damp_dev[0] = damp;
 }
 
@@ -139,7 +145,7 @@ __global__ void __launch_bounds__(256) mirror_kernel_vec(const float* S, int64_t
     auto is_dead = [&](int j) { return neutralize && S[(int64_t)j * lds + j] == 0.0f; };
     if (t < kT) dR[t] = r0 + t < d ? is_dead(r0 + t) : 0;
     else if (t < 2 * kT) dC[t - kT] = c0 + t - kT < d ? is_dead(c0 + t - kT) : 0;
-    damp = diag_damp(S, lds, d, scale, damp_percent, neutralize, part);
+    damp = diag_damp<kDiagThreads>(S, lds, d, scale, damp_percent, neutralize, part);
     if (b == 0) {
       for (int j = t; j < d; j += 256) dead[j] = is_dead(j) ? 1 : 0;
       if (t == 0) damp_dev[0] = damp;
@@ -233,8 +239,12 @@ hipError_t launch_materialize(const float* S, int64_t lds, int d, float scale, f
                        neutralize, dead, damp_dev, H, nt);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(diag_kernel, dim3(1), dim3(kDiagThreads), 0, stream, S, lds, d, scale, damp_percent,
-                     neutralize, dead, damp_dev);
+  if (d <= kFusedMaxD)
+    hipLaunchKernelGGL(diag_kernel<kDiagThreads>, dim3(1), dim3(kDiagThreads), 0, stream, S, lds, d, scale,
+                       damp_percent, neutralize, dead, damp_dev);
+  else
+    hipLaunchKernelGGL(diag_kernel<kDiagThreadsWide>, dim3(1), dim3(kDiagThreadsWide), 0, stream, S, lds, d, scale,
+                       damp_percent, neutralize, dead, damp_dev);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (vec)
