@@ -153,14 +153,22 @@ def _act_code(dtype) -> int:
 
 
 def _as_rows(x: torch.Tensor, d: int):
-    """(tokens, d) view of x with unit feature stride; returns (tensor, n, ld)."""
+    """(tokens, d) view of x whose rows are d contiguous elements at a stride ld >= d.
+
+    Returns (tensor, n, ld).  A view whose rows overlap or repeat (a broadcast
+    row, stride 0, or a sliding window, stride < d) or whose features are not
+    contiguous is copied first, so the library never reads past the storage.
+    """
     if x.shape[-1] != d:
         raise ValueError(f"last dimension {x.shape[-1]} != d = {d}")
     x2 = x.reshape(-1, d) if x.dim() != 2 else x
-    if x2.shape[0] > 0 and d > 1 and x2.stride(1) != 1:
+    n = x2.shape[0]
+    if n > 0 and d > 1 and x2.stride(1) != 1:
         x2 = x2.contiguous()
-    ld = x2.stride(0) if x2.shape[0] > 1 else d
-    return x2, x2.shape[0], max(ld, d)
+    if n > 1 and x2.stride(0) < d:
+        x2 = x2.contiguous()
+    ld = x2.stride(0) if n > 1 else d
+    return x2, n, ld
 
 
 def set_staging(enable: bool) -> None:

@@ -237,7 +237,7 @@ constexpr int64_t kBigMinWork = 300;     // ... and at least this many iteration
 constexpr int64_t kGroupScratchMax = (int64_t)4 << 30;  // largest gather buffer of grouped updates, per device
 // its tail holds one launch's schedule: 257 offsets and at most 64 groups x ntiles items (d <= 32768)
 constexpr int64_t kGroupSchedBytes = (int64_t)(kCUs + 1 + kBigMaxGroups * (128 * 129 / 2)) * 4;
-constexpr int64_t kGroupItemCost = 24;   // a tile's prologue and output, in 32-token iterations
+constexpr int64_t kGroupItemCost = 24;   // a tile chunk's prologue and output, in 32-token iterations
 
 bool big_capable(int64_t d, int dtype) { return dtype == HESS_BF16 && d % 8 == 0 && d >= 8 && d <= 32768; }
 
@@ -531,7 +531,8 @@ int grouped_big(hess_t* hs, int n_groups, const void* X, int64_t ld, const int32
       std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> pq;
       for (int w = 0; w < kCUs; ++w) pq.push({0, w});
       for (int g : idx) {
-        const int64_t cost = (Gb.n[g] + kBigKI - 1) / kBigKI + kGroupItemCost;
+        const int64_t iters = (Gb.n[g] + kBigKI - 1) / kBigKI;
+        const int64_t cost = iters + kGroupItemCost * ((iters + kBigChain - 1) / kBigChain);
         for (int t = 0; t < P.ntiles; ++t) {
           Slot sl = pq.top();
           pq.pop();

@@ -77,6 +77,11 @@ struct BigParams {
   int t8;                 // X is in the transposed staging layout
 };
 
+// Longest float32 accumulation chain of the 256-tile kernel, in 32-token
+// iterations: longer pieces of a tile are done as chunks of at most this many
+// iterations, each chunk's sums added into the tile's destination.
+constexpr int kBigChain = 512;
+
 hipError_t launch_syrk_big(const BigParams& P, hipStream_t stream);
 hipError_t launch_syrk_big_fixup(const BigParams& P, hipStream_t stream);
 

@@ -344,7 +344,7 @@ def quant_scale(x: np.ndarray, bits: int = 4) -> np.ndarray:
 
 
 def gptq_quantize(W: np.ndarray, U: np.ndarray, group_size: int = -1, bits: int = 4, dead=None,
-                  nsamples: int = 1, follow=None, tie_tol: float = 0.0):
+                  nsamples: int = 1, tie_tol: float = 0.0, ties=None, tie_break=None):
     """Error-propagating quantization of W (rows = outputs, columns = inputs).
 
     U is the upper Cholesky factor of the inverse damped Hessian (only its
@@ -356,10 +356,15 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, group_size: int = -1, bits: int 
     Rounding ties: the largest magnitude of a group sits at 7.5 steps, so
     ties between two codes are part of the method, and a run whose float64
     additions come in another order may round such a tie the other way.  Both
-    codes are then correct.  With ``follow`` (a code array of the same shape)
-    the oracle takes follow's code wherever w / step lies within ``tie_tol``
-    (relative) of a half-integer and follow's code is one of its two
-    neighbours; everything else is decided as above.
+    codes are then correct, and the choice decides the errors propagated
+    after it.  The oracle therefore reports every position where w / step
+    lies within ``tie_tol`` (relative) of a half-integer: when ``ties`` is a
+    list, one record ``(column, rows, lower code, upper code)`` per column
+    with such positions is appended to it.  The code taken there is
+    round-half-to-even unless ``tie_break`` is given: a function
+    ``tie_break(column, rows, lower, upper, default)`` returning one of the
+    two neighbour codes for each listed row (the method's decision at a tie,
+    passed in as an input).
     """
     W = np.array(W, dtype=np.float64)
     U = np.triu(np.asarray(U, dtype=np.float64))
@@ -383,12 +388,18 @@ def gptq_quantize(W: np.ndarray, U: np.ndarray, group_size: int = -1, bits: int 
         w = W[:, i].copy()
         x = w / scale
         q = np.clip(np.rint(x) + centre, 0, maxq)
-        if follow is not None:
-            tie = np.abs(x - np.floor(x) - 0.5) <= tie_tol * np.maximum(1.0, np.abs(x))
-            lo = np.clip(np.floor(x) + centre, 0, maxq)
-            hi = np.clip(np.ceil(x) + centre, 0, maxq)
-            f = np.asarray(follow)[:, i].astype(np.float64)
-            q = np.where(tie & ((f == lo) | (f == hi)), f, q)
+        if tie_tol > 0.0 and (ties is not None or tie_break is not None):
+            rows = np.flatnonzero(np.abs(x - np.floor(x) - 0.5) <= tie_tol * np.maximum(1.0, np.abs(x)))
+            if rows.size:
+                lo = np.clip(np.floor(x[rows]) + centre, 0, maxq)
+                hi = np.clip(np.floor(x[rows]) + 1.0 + centre, 0, maxq)
+                if ties is not None:
+                    ties.append((i, rows, lo.astype(np.uint8), hi.astype(np.uint8)))
+                if tie_break is not None:
+                    pick = np.asarray(tie_break(i, rows, lo, hi, q[rows].copy()), dtype=np.float64)
+                    if not np.all((pick == lo) | (pick == hi)):
+                        raise ValueError(f"tie_break returned a code that is not a neighbour (column {i})")
+                    q[rows] = pick
         deq = scale * (q - centre)
         err = (w - deq) / U[i, i]
         W[:, i + 1:] -= np.outer(err, U[i, i + 1:])

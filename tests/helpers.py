@@ -42,3 +42,35 @@ def block_agreement(B: np.ndarray, B_ref: np.ndarray) -> float:
             continue
         worst = max(worst, diff / md)
     return worst
+
+
+# Relative distance from a half-integer below which w / step is a rounding tie: both neighbour
+# codes are correct there (the float64 additions of the propagated errors come in another order
+# on the GPU, about 1e-16 relative, which can tip such a tie either way).
+TIE_TOL = 1e-12
+
+
+def quantize_against_gpu_ties(Wr, U, group, gpu_codes, **kw):
+    """The oracle's block quantize with the GPU's choice taken at rounding ties.
+
+    The oracle reports every tie and its two neighbour codes; this checker takes
+    the GPU's code there when it is one of them (and the oracle's own choice
+    otherwise, which then fails the code comparison).  Returns the oracle's
+    ``(Q, codes, scales, loss)`` and ``(ties, taken)``: how many tie positions
+    there were and at how many the GPU's code differed from the oracle's own.
+    """
+    import oracle as O
+    count = {"ties": 0, "taken": 0}
+    gpu_codes = np.asarray(gpu_codes)
+
+    def pick(i, rows, lo, hi, dflt):
+        g = gpu_codes[rows, i].astype(np.float64)
+        ok = (g == lo) | (g == hi)
+        out = np.where(ok, g, dflt)
+        count["ties"] += int(rows.size)
+        count["taken"] += int(np.sum(out != dflt))
+        return out
+
+    res = O.gptq_quantize(Wr, U, group_size=group, tie_tol=TIE_TOL, tie_break=pick, **kw)
+    assert count["taken"] <= count["ties"]
+    return res, (count["ties"], count["taken"])

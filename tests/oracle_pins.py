@@ -458,18 +458,31 @@ def pin_gptq_quantize(O, seed=31):
         assert np.allclose(Q, Qr, rtol=1e-12, atol=1e-12)
         assert abs(loss * 7 - loss_r) <= 1e-10 * max(1.0, loss_r)
         assert scales.shape == (N, 1 if group == -1 else -(-K // group))
-    # following one's own codes at ties changes nothing; codes that are not a neighbour are ignored
-    Q2, codes2, _, _ = O.gptq_quantize(W, U, group_size=group, nsamples=7, follow=codes, tie_tol=1e-12)
+    # a tie decision that returns the default changes nothing, and every reported tie holds the
+    # default code between its two neighbours
+    ties = []
+    Q2, codes2, _, _ = O.gptq_quantize(W, U, group_size=group, nsamples=7, tie_tol=1e-12, ties=ties,
+                                       tie_break=lambda i, rows, lo, hi, dflt: dflt)
     assert np.array_equal(codes2, codes) and np.array_equal(Q2, Q)
-    Q3, codes3, _, _ = O.gptq_quantize(W, U, group_size=group, nsamples=7, follow=np.full_like(codes, 200),
-                                       tie_tol=1e-12)
-    assert np.array_equal(codes3, codes)
-    # an exact tie: w / step = -7.5 rounds to the even -8 (code 0); following code 1 is allowed there
+    for i, rows, lo, hi in ties:
+        assert np.all(hi.astype(int) - lo.astype(int) <= 1) and np.all(
+            (codes[rows, i] == lo) | (codes[rows, i] == hi))
+    # a tie decision that is not a neighbour code is refused
+    try:
+        O.gptq_quantize(W, U, group_size=group, tie_tol=1e-12, tie_break=lambda i, rows, lo, hi, dflt: dflt + 3)
+        raise AssertionError("a non-neighbour tie decision must be refused")
+    except ValueError:
+        pass
+    # an exact tie: w / step = -7.5 rounds to the even -8 (code 0); the other neighbour (code 1)
+    # may be taken there, and the error it leaves propagates
     row = np.array([[-3.75, 1.0]])
     _, c_tie, _, _ = O.gptq_quantize(row, np.eye(2))
     assert c_tie[0, 0] == 0
-    _, c_f, _, _ = O.gptq_quantize(row, np.eye(2), follow=np.array([[1, 0]]), tie_tol=1e-12)
+    ties = []
+    _, c_f, _, _ = O.gptq_quantize(row, np.eye(2), tie_tol=1e-12, ties=ties,
+                                   tie_break=lambda i, rows, lo, hi, dflt: hi)
     assert c_f[0, 0] == 1
+    assert [(t[0], t[1].tolist(), t[2].tolist(), t[3].tolist()) for t in ties][0] == (0, [0], [0], [1])
     # dead columns: zero weights, centre codes, no error to move
     W = rng.standard_normal((4, 8))
     X = rng.standard_normal((30, 8))

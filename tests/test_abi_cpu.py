@@ -105,3 +105,40 @@ def test_quantize_arguments_rejected_without_gpu():
     assert call(work_bytes=need - 8) == -1 and b"workspace" in lib.hess_last_error()
     assert call(q=base + 64) == -1 and b"overlaps" in lib.hess_last_error()
     assert call(n=70000) == -1
+
+
+def _span_elems(x2, n, ld, d):
+    """Elements the library reads from the returned view's start: (n - 1) * ld + d."""
+    return 0 if n == 0 else (n - 1) * ld + d
+
+
+@pytest.mark.parametrize("make", ["expand", "unfold", "strided", "contig", "transposed", "one_row", "empty"])
+def test_as_rows_never_reads_past_storage(make):
+    """The rows handed to the library lie inside the tensor's storage and hold its values,
+    for broadcast (stride 0) and overlapping (stride < d) views too."""
+    import torch
+    d = 8
+    base = torch.arange(5 * d, dtype=torch.float32).reshape(5, d)
+    if make == "expand":
+        x = base[0][None].expand(5, d)                     # row stride 0
+    elif make == "unfold":
+        x = torch.arange(40, dtype=torch.float32).unfold(0, d, 2)   # (17, 8), row stride 2 < d
+    elif make == "strided":
+        x = torch.zeros(5, d + 4)[:, :d]
+        x.copy_(base)
+    elif make == "contig":
+        x = base
+    elif make == "transposed":
+        x = base.reshape(d, 5).t()                         # feature stride 5
+    elif make == "one_row":
+        x = base[:1]
+    else:
+        x = base[:0]
+    x2, n, ld = hs._as_rows(x, d)
+    assert n == x.shape[0] and ld >= d
+    assert x2.stride(1) == 1 or n == 0
+    storage = x2.untyped_storage().nbytes() // 4 - x2.storage_offset()
+    assert _span_elems(x2, n, ld, d) <= storage
+    if n > 0:
+        flat = torch.as_strided(x2, (n, d), (ld, 1))
+        assert torch.equal(flat, x)

@@ -16,7 +16,7 @@ import torch
 import oracle as O
 import workloads as W
 import gptq_hessian_accumulation_amd as hs
-from tests.helpers import TOL, agreement, block_agreement, to_device, torch_dtype
+from tests.helpers import TOL, agreement, block_agreement, quantize_against_gpu_ties, to_device, torch_dtype
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
@@ -1002,8 +1002,8 @@ def test_new_entry_points_on_a_side_stream():
     assert n == 900 and np.all(np.abs(sums.cpu().numpy() - sr) <= 5e-5 * sr + 1e-30)
     U32 = U.cpu().numpy()
     assert np.allclose(U32, O.chol_inverse_upper(H.cpu().numpy().astype(np.float64)), rtol=1e-5, atol=1e-9)
-    Qr, cr, _, _ = O.gptq_quantize(Wt.cpu().numpy().astype(np.float64), U32.astype(np.float64),
-                                   follow=codes.cpu().numpy(), tie_tol=1e-12)
+    (Qr, cr, _, _), _ = quantize_against_gpu_ties(Wt.cpu().numpy().astype(np.float64), U32.astype(np.float64), -1,
+                                                  codes.cpu().numpy())
     assert np.array_equal(codes.cpu().numpy(), cr)
     for o in (h, f, m):
         o.close()

@@ -17,6 +17,7 @@ import torch
 import oracle as O
 import workloads as W
 import gptq_hessian_accumulation_amd as hs
+from tests.helpers import quantize_against_gpu_ties
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
@@ -43,12 +44,10 @@ def weights(N, K, seed):
     return (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
 
 
-TIE_TOL = 1e-12   # relative distance from a half-integer below which both codes are correct
-
-
 def compare(Wt, U, group, got, dead=None, nsamples=1, rows=None):
-    """Codes exactly, except at rounding ties (both neighbours correct), where the oracle follows
-    the GPU's choice and must then agree on everything after it."""
+    """Codes exactly, except at rounding ties (both neighbours correct): the oracle reports each
+    tie, the checker takes the GPU's code there when it is one of the two neighbours, and both
+    sides must then agree on everything after it."""
     Q, codes, scales, loss = got
     Wr = Wt if rows is None else Wt[rows]
     Qg = Q.cpu().numpy().astype(np.float64)
@@ -56,11 +55,9 @@ def compare(Wt, U, group, got, dead=None, nsamples=1, rows=None):
     sg = scales.cpu().numpy().astype(np.float64)
     if rows is not None:
         Qg, cg, sg = Qg[rows], cg[rows], sg[rows]
-    Qr, cr, sr, lr = O.gptq_quantize(Wr.astype(np.float64), U.astype(np.float64), group_size=group, dead=dead,
-                                     nsamples=nsamples, follow=cg, tie_tol=TIE_TOL)
-    _, c_own, _, _ = O.gptq_quantize(Wr.astype(np.float64), U.astype(np.float64), group_size=group, dead=dead,
-                                     nsamples=nsamples)
-    print(f"  codes decided at ties: {int((c_own != cr).sum())} of {cr.size}")
+    (Qr, cr, sr, lr), (ties, taken) = quantize_against_gpu_ties(Wr.astype(np.float64), U.astype(np.float64), group,
+                                                               cg, dead=dead, nsamples=nsamples)
+    print(f"  rounding ties: {ties}; the GPU took the other neighbour at {taken} of them; {cr.size} codes")
     assert np.array_equal(cg, cr), f"{int((cg != cr).sum())} codes differ"
     assert np.all(np.abs(Qg - Qr) <= 2.0 ** -23 * np.abs(Qr)), float(np.max(np.abs(Qg - Qr)))
     assert np.all(np.abs(sg - sr) <= 2.0 ** -23 * np.abs(sr))

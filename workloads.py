@@ -181,3 +181,54 @@ def torch_rows(gen, n: int, d: int, scales, dtype: str, device, out=None):
         out.copy_(x)
         return out
     return x
+
+
+def torch_ragged(d: int, seed: int, dtype: str = BF16, count: int = 360, dead_frac: float = 0.0,
+                 device="cuda"):
+    """A ragged calibration Hessian's batches, resident on ``device``.
+
+    Batch sizes are uniform integers in [1, 2000] and the dead columns are
+    chosen with numpy PCG64 (seed ``seed``, in that order); column scales and
+    activations come from the device generator seeded the same.  The batches
+    are views into one buffer, back to back.  For one seed, the float32
+    values are the same whatever ``dtype`` is; bf16 and fp16 round them.
+    Returns ``(buf, views, sizes, dead)``.
+    """
+    import torch
+    rng = np.random.default_rng(seed)
+    sizes = ragged_sizes(rng, count)
+    dead = dead_columns(rng, d, dead_frac)
+    gen = torch_generator(seed, device)
+    scales = torch_column_scales(gen, d, device)
+    if dead.size:
+        scales[torch.from_numpy(dead).to(device)] = 0.0
+    buf = torch_rows(gen, int(sizes.sum()), d, scales, dtype, device)
+    views, off = [], 0
+    for n in sizes:
+        views.append(buf[off:off + int(n)])
+        off += int(n)
+    return buf, views, sizes, dead
+
+
+def torch_single(d: int, n: int, seed: int, dtype: str = BF16, dead_frac: float = 0.0, device="cuda"):
+    """One batch of ``n`` tokens on ``device``, same recipe as ``torch_ragged``.
+
+    Returns ``(x, dead)``.
+    """
+    import torch
+    rng = np.random.default_rng(seed)
+    dead = dead_columns(rng, d, dead_frac)
+    gen = torch_generator(seed, device)
+    scales = torch_column_scales(gen, d, device)
+    if dead.size:
+        scales[torch.from_numpy(dead).to(device)] = 0.0
+    return torch_rows(gen, n, d, scales, dtype, device), dead
+
+
+def host_copy(x, dtype: str) -> np.ndarray:
+    """Host array of a device batch in the storage format the oracle reads
+    (bf16 as uint16 bit patterns, fp16 as numpy float16, float32 as is)."""
+    import torch
+    if dtype == BF16:
+        return x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return x.contiguous().cpu().numpy()
