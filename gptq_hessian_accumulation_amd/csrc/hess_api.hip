@@ -92,6 +92,19 @@ struct BigWorkspace {
 constexpr int kMaxDevices = 64;
 BigWorkspace g_big[kMaxDevices];
 
+// Partial-sum scratch of the local blocks, one per device, allocated by the
+// first call on the device (kLocalPartBytes, or more for widths past
+// 262,144).  Calls on another stream than the previous user wait for its event.
+struct LocalScratch {
+  std::mutex mu;
+  float* ptr = nullptr;
+  int64_t bytes = 0;
+  hipEvent_t ev = nullptr;
+  bool used = false;
+  hipStream_t last = nullptr;
+};
+LocalScratch g_local[kMaxDevices];
+
 thread_local char g_err[512] = "";
 int g_tile_override = 0;  // 0 = automatic; 64, 128 or 256 force that SYRK tile edge where it applies
 int64_t g_group_chunk = 0; // test hook: cap on the gathered bytes per grouped launch (0 = scratch size)
@@ -1095,8 +1108,8 @@ int hess_state_buffer(hess_t h, const float** S_out) {
   return HESS_OK;
 }
 
-int hess_local_blocks_ex(const void* X, int in_dtype, int64_t n_tokens, int64_t d, int64_t ld, int block,
-                         float* out, int accumulate, hess_stream_t stream) {
+// Argument checks shared by the local-block entry points.
+int local_check(const void* X, int in_dtype, int64_t n_tokens, int64_t d, int64_t ld, int block, const float* out) {
   if (in_dtype != HESS_BF16 && in_dtype != HESS_F32) return fail(HESS_EINVAL, "unknown input dtype %d", in_dtype);
   if (block != 16) return fail(HESS_EINVAL, "block must be 16");
   if (d < 16 || d % 16 != 0 || d > (1 << 30)) return fail(HESS_EINVAL, "d must be a positive multiple of 16");
@@ -1105,10 +1118,56 @@ int hess_local_blocks_ex(const void* X, int in_dtype, int64_t n_tokens, int64_t 
   if (!out) return fail(HESS_EINVAL, "out is NULL");
   if (n_tokens > 0 && !X) return fail(HESS_EINVAL, "X is NULL with n_tokens > 0");
   if (reinterpret_cast<uintptr_t>(X) % esize(in_dtype) != 0) return fail(HESS_EALIGN, "X not element-aligned");
+  return HESS_OK;
+}
+
+int hess_local_blocks_ex(const void* X, int in_dtype, int64_t n_tokens, int64_t d, int64_t ld, int block,
+                         float* out, int accumulate, hess_stream_t stream) {
+  int rc = local_check(X, in_dtype, n_tokens, d, ld, block, out);
+  if (rc != HESS_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   const bool vec = n_tokens > 0 && vec_ok(X, ld, d, esize(in_dtype));
-  hipError_t e = launch_local_blocks(X, in_dtype, n_tokens, (int)d, ld, vec, out, accumulate,
-                                     static_cast<hipStream_t>(stream));
+  // the plan fits kLocalPartBytes up to width 262,144 (one slice beyond)
+  const int64_t part_cap = std::max<int64_t>(kLocalPartBytes, (d / 16) * 1024);
+  const LocalPlan pl = local_plan(n_tokens, (int)d, part_cap);
+  if (n_tokens == 0) {
+    hipError_t e = launch_local_blocks(X, in_dtype, 0, (int)d, ld, vec, out, accumulate, pl, nullptr, s);
+    return e == hipSuccess ? HESS_OK : hip_fail(e, "local blocks launch");
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HESS_EINVAL, "device %d out of range", dev);
+  LocalScratch& L = g_local[dev];
+  std::lock_guard<std::mutex> lock(L.mu);
+  if (L.bytes < pl.part_bytes) {
+    if (L.ptr) {
+      e = hipDeviceSynchronize();
+      if (e == hipSuccess) e = hipFree(L.ptr);
+      L.ptr = nullptr;
+      L.bytes = 0;
+      L.used = false;
+    }
+    const int64_t want = std::max(pl.part_bytes, kLocalPartBytes);
+    if (e == hipSuccess) e = hipMalloc(&L.ptr, (size_t)want);
+    if (e == hipSuccess && !L.ev) e = hipEventCreateWithFlags(&L.ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      L.ptr = nullptr;
+      const int code = (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) ? HESS_ENOMEM : HESS_EHIP;
+      return fail(code, "local-block scratch (%lld bytes): %s", (long long)want, hipGetErrorString(e));
+    }
+    L.bytes = want;
+  }
+  if (L.used && L.last != s) {
+    e = hipStreamWaitEvent(s, L.ev, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  e = launch_local_blocks(X, in_dtype, n_tokens, (int)d, ld, vec, out, accumulate, pl, L.ptr, s);
   if (e != hipSuccess) return hip_fail(e, "local blocks launch");
+  e = hipEventRecord(L.ev, s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  L.used = true;
+  L.last = s;
   return HESS_OK;
 }
 

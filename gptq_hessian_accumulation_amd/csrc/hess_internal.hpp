@@ -144,9 +144,19 @@ hipError_t launch_syrk_reduce(float* S, int64_t lds, const float* ws, int d, int
 hipError_t launch_materialize(const float* S, int64_t lds, int d, float scale, float damp_percent, int neutralize,
                               float* H, uint8_t* dead, float* damp_dev, double* sum_scratch, hipStream_t stream);
 
-// Local 16 x 16 block Grams: out[b] (+)= X_b^T X_b.
+// Local 16 x 16 block Grams: out[b] (+)= X_b^T X_b, through per-workgroup
+// partial sums in a scratch buffer of plan.part_bytes (slices x d/16 x 1 KB)
+// added in a fixed order.
+constexpr int64_t kLocalPartBytes = (int64_t)16 << 20;  // the scratch every plan fits in (d <= 262,144)
+struct LocalPlan {
+  int gx;            // 256-feature columns
+  int64_t gy;        // token runs (scratch slices)
+  int64_t tpw;       // tokens per run, a multiple of 32
+  int64_t part_bytes;
+};
+LocalPlan local_plan(int64_t n, int d, int64_t part_bytes);
 hipError_t launch_local_blocks(const void* X, int in_dtype, int64_t n, int d, int64_t ld, bool vec, float* out,
-                               int accumulate, hipStream_t stream);
+                               int accumulate, const LocalPlan& plan, float* part, hipStream_t stream);
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 // Zero S's rows from column 256 * (row / 256) on: the upper triangle and every

@@ -7,20 +7,28 @@
 // matrices built by a batched product that reads bfloat16 and writes
 // float32.  Unscaled; the blocks only weight candidate-scale errors.
 //
-// The work is a single streaming read of X (HBM-bound): each workgroup takes
-// 256 features (16 blocks, 4 per wave) of a run of tokens.  32-token slabs are
-// copied into LDS in their natural [token][feature] layout with 16-byte loads
-// (one load stage ahead in registers), and each wave reads its block operands
-// with ds_read_b64_tr_b16, which returns a feature's 4 consecutive tokens per
-// lane: two such reads give the 8 tokens a v_mfma_f32_16x16x32_bf16 lane
-// needs.  The same register is both the A and the B operand, because a
-// block's Gram pairs each feature with itself over the same tokens.  Each
-// workgroup adds its 16 blocks into `out` with float32 atomics at the end.
+// The work is a single streaming read of X (HBM-bound), in two kernels:
+//  1. local_part: workgroup (x, y) takes the 256 features of column x (16
+//     blocks, 4 per wave) over the y-th run of tokens and writes its 16
+//     block sums to its own slice of a scratch buffer (no atomics).
+//     32-token slabs are copied into LDS in their natural [token][feature]
+//     layout with 16-byte loads (one slab ahead in registers).
+//     - bf16: each wave reads its block operands with ds_read_b64_tr_b16,
+//       which returns a feature's 4 consecutive tokens per lane; two such
+//       reads give the 8 tokens a v_mfma_f32_16x16x32_bf16 lane needs.
+//     - float32: v_mfma_f32_16x16x4_f32 with exact products, one float per
+//       lane (token t0 + l/16, feature l%16 of the block).
+//     In both the same register is the A and the B operand, because a
+//     block's Gram pairs each feature with itself over the same tokens.
+//     Each wave's sums pass through three accumulators (every 64 slabs of
+//     bf16 or 16 of float32 into the second, every 32 of those into the
+//     third), so no float32 chain grows long with the batch.
+//  2. local_reduce: out[b] (+)= the slices' sums for block b, added in a
+//     fixed grouped order (runs of 16).  Every run gives the same bits.
 //
-// float32 inputs are split into hi + lo bf16 planes.  The hi*hi, the cross
-// (hi*lo + lo*hi) and the lo*lo products go to three separate accumulators,
-// combined smallest first at the end, so the small terms are never rounded
-// against the large accumulator.
+// The scratch (slices x blocks x 1 KB) is at most kLocalPartBytes: the plan
+// takes about 1,024 workgroups, fewer token runs when the blocks of a slice
+// would not fit.
 
 #include "hess_device.hpp"
 #include "hess_internal.hpp"
@@ -32,18 +40,21 @@ namespace {
 constexpr int kLThreads = 256;
 constexpr int kLFeat = 256;                      // features per workgroup
 constexpr int kLTok = 32;                        // tokens per slab
-constexpr int kLRow = kLFeat * 2 + 32;           // LDS bytes per token row (padded)
-constexpr int kLPlane = kLTok * kLRow;           // one bf16 plane of a slab
+constexpr int kLChain2 = 32;                     // first-level sums per second-level chain
 
 template <int IN>
-struct LocalRegs;
+struct LocalCfg;
 template <>
-struct LocalRegs<kInBF16> {
-  u32x4 v[4];  // 4 chunks of 8 bf16
+struct LocalCfg<kInBF16> {
+  static constexpr int ES = 2;                   // bytes per element
+  static constexpr int ROW = kLFeat * 2 + 32;    // LDS bytes per token row (padded)
+  static constexpr int CHAIN = 64;               // slabs per first-level chain (256 roundings)
 };
 template <>
-struct LocalRegs<kInF32> {
-  u32x4 v[8];  // 8 chunks of 4 floats
+struct LocalCfg<kInF32> {
+  static constexpr int ES = 4;
+  static constexpr int ROW = kLFeat * 4 + 64;    // rows 16 banks apart: a 64-lane read is conflict-free
+  static constexpr int CHAIN = 16;               // slabs per first-level chain (128 roundings)
 };
 
 __device__ __forceinline__ s16x4 tr_read(const char* lds_base, int byte_off) {
@@ -53,22 +64,23 @@ __device__ __forceinline__ s16x4 tr_read(const char* lds_base, int byte_off) {
 
 template <int IN, bool VEC>
 __device__ __forceinline__ void local_body(const void* Xv, int64_t n, int d, int64_t ld, int64_t tok_per_wg,
-                                           float* out, char* lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int F0 = blockIdx.x * kLFeat;
-  const int64_t t_begin = (int64_t)blockIdx.y * tok_per_wg;
-  const int64_t t_end = min(n, t_begin + tok_per_wg);
-  if (t_begin >= t_end) return;
-  const int nslab = (int)((t_end - t_begin + kLTok - 1) / kLTok);
-  constexpr int ES = IN == kInF32 ? 4 : 2;
+                                           float* part, char* lds) {
+  using C = LocalCfg<IN>;
+  constexpr int ES = C::ES;
+  constexpr int ROW = C::ROW;
   constexpr int CH = 16 / ES;                        // features per 16-byte chunk
   constexpr int CHUNKS = kLTok * kLFeat / CH;        // chunks per slab
   constexpr int CPT = CHUNKS / kLThreads;            // chunks per thread
-  constexpr int PLANES = IN == kInF32 ? 2 : 1;
-  constexpr int STAGE = PLANES * kLPlane;
+  constexpr int STAGE = kLTok * ROW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int F0 = blockIdx.x * kLFeat;
+  const int nblk = d / 16;
+  const int64_t t_begin = (int64_t)blockIdx.y * tok_per_wg;
+  const int64_t t_end = min(n, t_begin + tok_per_wg);
+  const int nslab = t_begin < t_end ? (int)((t_end - t_begin + kLTok - 1) / kLTok) : 0;
   const char* X = static_cast<const char*>(Xv);
 
-  LocalRegs<IN> R;
+  u32x4 R[CPT];
   auto load = [&](int s) {
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
@@ -97,7 +109,7 @@ __device__ __forceinline__ void local_body(const void* Xv, int64_t n, int d, int
           v = u32x4{w[0], w[1], w[2], w[3]};
         }
       }
-      R.v[q] = v;
+      R[q] = v;
     }
   };
   auto store = [&](char* stage) {
@@ -105,30 +117,25 @@ __device__ __forceinline__ void local_body(const void* Xv, int64_t n, int d, int
     for (int q = 0; q < CPT; ++q) {
       const int c = tid + q * kLThreads;
       const int row = c / (kLFeat / CH), colc = c % (kLFeat / CH);
-      if constexpr (IN == kInBF16) {
-        *reinterpret_cast<u32x4*>(stage + row * kLRow + colc * 16) = R.v[q];
-      } else {
-        uint32_t h[4], l[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) split_bf16(__uint_as_float(R.v[q][k]), h[k], l[k]);
-        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<u32x2*>(stage + row * kLRow + colc * 8) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-        *reinterpret_cast<u32x2*>(stage + kLPlane + row * kLRow + colc * 8) =
-            u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-      }
+      *reinterpret_cast<u32x4*>(stage + row * ROW + colc * 16) = R[q];
     }
   };
 
-  f32x4 acc[4], accx[4], accl[4];
+  // three levels: slab sums chain in acc for C::CHAIN slabs, those sums in
+  // acc2 for kLChain2 of them, and those in acc3, so that no float32 chain
+  // grows long with the run of tokens (with identical values in a column,
+  // every rounding of a long chain errs the same way)
+  f32x4 acc[4], acc2[4], acc3[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accx[b] = acc[b];
-    accl[b] = acc[b];
+    acc2[b] = acc[b];
+    acc3[b] = acc[b];
   }
 
-  // operand addressing: lane l, group g = l/16, i = l%16; rows 8g + 4*half + r
-  // supplied by lanes 4r + q at feature column 4q of the block
+  // lane l: group g = l/16, i16 = l%16.  bf16: rows 8g + 4*half + r supplied
+  // by lanes 4r + q at feature column 4q of the block; float32: token 4j + g,
+  // feature i16 of the block
   const int g = lane >> 4, i16 = lane & 15;
   const int rsel = i16 >> 2, qsel = i16 & 3;
 
@@ -137,58 +144,103 @@ __device__ __forceinline__ void local_body(const void* Xv, int64_t n, int d, int
     for (int bb = 0; bb < 4; ++bb) {
       const int blk = wave * 4 + bb;  // block within the workgroup
       if (F0 + blk * 16 >= d) continue;
-      const int colb = blk * 32 + qsel * 8;  // bytes
-      const int off0 = (8 * g + rsel) * kLRow + colb;
-      const int off1 = (8 * g + 4 + rsel) * kLRow + colb;
-      s16x4 lo0 = tr_read(stage, off0), lo1 = tr_read(stage, off1);
-      u32x4 a = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo0, lo1, 0, 1, 2, 3, 4, 5, 6, 7));
       if constexpr (IN == kInBF16) {
+        const int colb = blk * 32 + qsel * 8;  // bytes
+        const s16x4 lo0 = tr_read(stage, (8 * g + rsel) * ROW + colb);
+        const s16x4 lo1 = tr_read(stage, (8 * g + 4 + rsel) * ROW + colb);
+        const u32x4 a = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo0, lo1, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[bb] = mfma16x16x32(a, a, acc[bb]);
       } else {
-        s16x4 l0 = tr_read(stage + kLPlane, off0), l1 = tr_read(stage + kLPlane, off1);
-        u32x4 al = __builtin_bit_cast(u32x4, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
-        accl[bb] = mfma16x16x32(al, al, accl[bb]);
-        accx[bb] = mfma16x16x32(al, a, accx[bb]);
-        accx[bb] = mfma16x16x32(a, al, accx[bb]);
-        acc[bb] = mfma16x16x32(a, a, acc[bb]);
+        // token 4 j + g of the slab: 4 j rows (j * ROW floats) past row g
+        const float* col = reinterpret_cast<const float*>(stage + g * ROW) + blk * 16 + i16;
+#pragma unroll
+        for (int j = 0; j < kLTok / 4; ++j) {
+          const float v = col[j * ROW];
+          acc[bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, v, acc[bb], 0, 0, 0);
+        }
       }
     }
   };
 
-  load(0);
-  store(lds);
-  __syncthreads();
+  if (nslab > 0) {
+    load(0);
+    store(lds);
+    __syncthreads();
+  }
   for (int s = 0; s < nslab; ++s) {
     char* cur = lds + (s & 1) * STAGE;
     char* nxt = lds + ((s + 1) & 1) * STAGE;
     const bool more = s + 1 < nslab;
     if (more) load(s + 1);
     compute(cur);
+    if ((s + 1) % C::CHAIN == 0 || !more) {
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        acc2[bb] += acc[bb];
+        acc[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      if ((s + 1) % (C::CHAIN * kLChain2) == 0 || !more) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          acc3[bb] += acc2[bb];
+          acc2[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
     if (more) store(nxt);
     __syncthreads();
   }
 
-  if constexpr (IN == kInF32) {
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) acc[bb] = (accl[bb] + accx[bb]) + acc[bb];
-  }
   // register r of lane l holds C[4*(l/16) + r][l%16] of each block
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb) {
-    const int blk = wave * 4 + bb;
-    const int gb = F0 / 16 + blk;
-    if (gb * 16 >= d) continue;
-    float* o = out + (int64_t)gb * 256;
+    const int gb = F0 / 16 + wave * 4 + bb;
+    if (gb >= nblk) continue;
+    float* o = part + ((int64_t)blockIdx.y * nblk + gb) * 256;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) unsafeAtomicAdd(o + (4 * g + r) * 16 + i16, acc[bb][r]);
+    for (int r = 0; r < 4; ++r) o[(4 * g + r) * 16 + i16] = acc3[bb][r];
   }
 }
 
 template <int IN, bool VEC>
-__global__ void __launch_bounds__(kLThreads) local_kernel(const void* X, int64_t n, int d, int64_t ld,
-                                                          int64_t tok_per_wg, float* out) {
+__global__ void __launch_bounds__(kLThreads) local_part(const void* X, int64_t n, int d, int64_t ld,
+                                                        int64_t tok_per_wg, float* part) {
   extern __shared__ __attribute__((aligned(16))) char hess_llds[];
-  local_body<IN, VEC>(X, n, d, ld, tok_per_wg, out, hess_llds);
+  local_body<IN, VEC>(X, n, d, ld, tok_per_wg, part, hess_llds);
+}
+
+// out[b][e] (+)= sum over slices y = 0 .. nslice-1 of part[y][b][e], in a
+// fixed order: runs of 16 slices summed in order, runs of 16 such sums, then
+// those, so no chain is longer than 16 + 16 + nslice / 256 additions.
+__global__ void __launch_bounds__(256) local_reduce(const float* part, int nblk, int nslice, float* out,
+                                                    int accumulate) {
+  const int b = blockIdx.x, e = threadIdx.x;
+  const float* p = part + (int64_t)b * 256 + e;
+  const int64_t stride = (int64_t)nblk * 256;  // floats between slices
+  float s = 0.0f;
+  for (int y2 = 0; y2 < nslice; y2 += 256) {
+    const int lim = min(nslice, y2 + 256);
+    float s2 = 0.0f;
+    // four runs of 16 at a time: their 64 loads are issued together, the
+    // sums still taken run by run in slice order
+    for (int y1 = y2; y1 < lim; y1 += 64) {
+      float v[64];
+#pragma unroll
+      for (int k = 0; k < 64; ++k) v[k] = y1 + k < lim ? p[(int64_t)(y1 + k) * stride] : 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (y1 + 16 * q >= lim) break;
+        float s1 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (y1 + 16 * q + k < lim) s1 += v[16 * q + k];
+        s2 += s1;
+      }
+    }
+    s += s2;
+  }
+  float* o = out + (int64_t)b * 256 + e;
+  *o = accumulate ? *o + s : s;
 }
 
 __global__ void zero_kernel(float* p, int64_t n) {
@@ -206,32 +258,48 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_local_blocks(const void* X, int in_dtype, int64_t n, int d, int64_t ld, bool vec, float* out,
-                               int accumulate, hipStream_t stream) {
-  const int nblocks = d / 16;
-  if (!accumulate) {
-    hipError_t e = launch_zero(out, (int64_t)nblocks * 256, stream);
-    if (e != hipSuccess) return e;
-  }
-  if (n <= 0) return hipSuccess;
-  const int gx = (d + kLFeat - 1) / kLFeat;
-  // about 1024 workgroups over the whole GPU, at least one slab each
-  int64_t gy = (1024 + gx - 1) / gx;
+LocalPlan local_plan(int64_t n, int d, int64_t part_bytes) {
+  LocalPlan p{};
+  const int64_t nblk = d / 16;
+  p.gx = (d + kLFeat - 1) / kLFeat;
+  // about 1024 workgroups over the whole GPU, at least four slabs each, and
+  // no more token runs than slices fit in the scratch
+  int64_t gy = (1024 + p.gx - 1) / p.gx;
+  const int64_t fit = part_bytes / (nblk * 1024);
+  if (gy > fit) gy = fit;
+  if (gy < 1) gy = 1;
   int64_t tpw = (n + gy - 1) / gy;
   tpw = ((tpw + kLTok - 1) / kLTok) * kLTok;
   if (tpw < 4 * kLTok) tpw = 4 * kLTok;
-  gy = (n + tpw - 1) / tpw;
-  const int planes = in_dtype == kInF32 ? 2 : 1;
-  const int lds = 2 * planes * kLPlane;
+  p.tpw = tpw;
+  p.gy = n > 0 ? (n + tpw - 1) / tpw : 0;
+  p.part_bytes = p.gy * nblk * 1024;
+  return p;
+}
+
+hipError_t launch_local_blocks(const void* X, int in_dtype, int64_t n, int d, int64_t ld, bool vec, float* out,
+                               int accumulate, const LocalPlan& pl, float* part, hipStream_t stream) {
+  const int nblk = d / 16;
+  if (n <= 0) {
+    if (!accumulate) return launch_zero(out, (int64_t)nblk * 256, stream);
+    return hipSuccess;
+  }
+  if (pl.gy < 1 || pl.gy >= 65536) return hipErrorInvalidValue;
+  const int lds = 2 * kLTok * (in_dtype == kInF32 ? LocalCfg<kInF32>::ROW : LocalCfg<kInBF16>::ROW);
   const void* fn;
   if (in_dtype == kInBF16)
-    fn = vec ? reinterpret_cast<const void*>(&local_kernel<kInBF16, true>)
-             : reinterpret_cast<const void*>(&local_kernel<kInBF16, false>);
+    fn = vec ? reinterpret_cast<const void*>(&local_part<kInBF16, true>)
+             : reinterpret_cast<const void*>(&local_part<kInBF16, false>);
   else
-    fn = vec ? reinterpret_cast<const void*>(&local_kernel<kInF32, true>)
-             : reinterpret_cast<const void*>(&local_kernel<kInF32, false>);
-  void* args[] = {const_cast<void**>(&X), &n, &d, &ld, &tpw, &out};
-  return hipLaunchKernel(fn, dim3(gx, (unsigned)gy), dim3(kLThreads), args, lds, stream);
+    fn = vec ? reinterpret_cast<const void*>(&local_part<kInF32, true>)
+             : reinterpret_cast<const void*>(&local_part<kInF32, false>);
+  int64_t tpw = pl.tpw;
+  void* args[] = {const_cast<void**>(&X), &n, &d, &ld, &tpw, &part};
+  hipError_t e = hipLaunchKernel(fn, dim3(pl.gx, (unsigned)pl.gy), dim3(kLThreads), args, lds, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(local_reduce, dim3(nblk), dim3(256), 0, stream, static_cast<const float*>(part), nblk,
+                     (int)pl.gy, out, accumulate);
+  return hipGetLastError();
 }
 
 }  // namespace hess

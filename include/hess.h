@@ -15,9 +15,10 @@
  *   (hipStream_t passed as hess_stream_t; NULL is the null stream).  Apart
  *   from create and destroy calls, hess_timing and hess_add_batch_grouped,
  *   no call synchronizes with the host or allocates device memory, so those
- *   calls (batches, casts, flush, reset, materialize, adopt, local blocks,
- *   imatrix, the Cholesky factor, the block quantize) may be captured into a
- *   HIP graph.  hess_add_batch_grouped builds each launch's schedule on the
+ *   calls (batches, casts, flush, reset, materialize, adopt, imatrix, the
+ *   Cholesky factor, the block quantize, and local blocks after the first
+ *   call on a device, which allocates the device's partial-sum scratch) may
+ *   be captured into a HIP graph.  hess_add_batch_grouped builds each launch's schedule on the
  *   host, sends it through a pinned buffer after the previous call's copy
  *   has finished, and sizes the device's gather buffer on first use: it is
  *   not for capture.  X must stay valid and unchanged until the stream has
@@ -312,6 +313,13 @@ int hess_local_blocks(const void* X, int64_t n_tokens, int64_t d, int block, flo
 /*
  * hess_local_blocks_ex -- hess_local_blocks with dtype, stride, stream and
  * accumulate (nonzero: out += ..., zero: out = ...).
+ *   in_dtype  HESS_BF16 or HESS_F32 (float32 products are exact).
+ *   ld        row stride of X in elements, >= d.
+ * Sums go through per-workgroup partials added in a fixed order, so a call
+ * gives the same bits every time (no atomics).  The partials live in a
+ * per-device scratch that the first call on a device allocates (16 MiB, or
+ * 1 KB per block beyond width 262,144) and later calls reuse; a call on
+ * another stream than the previous one waits for it.
  */
 int hess_local_blocks_ex(const void* X, int in_dtype, int64_t n_tokens, int64_t d, int64_t ld,
                          int block, float* out, int accumulate, hess_stream_t stream);

@@ -520,6 +520,46 @@ def test_local_blocks(dtype, n, d):
     assert block_agreement(out.cpu().numpy(), ref) <= TOL[dtype]
 
 
+def test_local_blocks_fixed_order_bitwise_repeatable():
+    """Block sums go through per-workgroup partials added in a fixed order: two runs give the
+    same bits (bf16 and float32, accumulate and overwrite)."""
+    _say("local blocks repeatable")
+    rng = np.random.default_rng(44)
+    for dtype in (W.BF16, W.F32):
+        x = to_device(W.encode(W.normal_rows(rng, 20000, 1024, W.column_scales(rng, 1024)), dtype), dtype)
+        a = hs.local_blocks(x, accumulate=False)
+        b = hs.local_blocks(x, accumulate=False)
+        hs.local_blocks(x, out=a)
+        hs.local_blocks(x, out=b)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("n", [100000, 300001, 600000])
+def test_local_blocks_fp32_constant_column_and_long_chains(n):
+    """float32 rows through exact-product float32 matrix instructions: a constant-valued column
+    (every product the same, so a split into bf16 parts would err systematically) and long
+    batches whose per-wave sums pass through a second accumulator every 2,048 tokens."""
+    _say(f"local blocks fp32 constant column n={n}")
+    rng = np.random.default_rng(45)
+    d = 64
+    x = W.normal_rows(rng, n, d, W.column_scales(rng, d))
+    x[:, 5] = np.float32(1.2345679)
+    x[:, 40] = np.float32(-3.0000002)
+    ref = O.local_blocks(x, W.F32)
+    out = hs.local_blocks(to_device(x, W.F32), accumulate=False)
+    torch.cuda.synchronize()
+    err = block_agreement(out.cpu().numpy(), ref)
+    print(f"  fp32 local n={n}: {err:.3e}")
+    assert err <= TOL[W.F32]
+    xb = W.encode(x, W.BF16)
+    outb = hs.local_blocks(to_device(xb, W.BF16), accumulate=False)
+    torch.cuda.synchronize()
+    errb = block_agreement(outb.cpu().numpy(), O.local_blocks(xb, W.BF16))
+    print(f"  bf16 local n={n}: {errb:.3e}")
+    assert errb <= TOL[W.BF16]
+
+
 def test_local_blocks_match_full_path_diagonal_blocks():
     _say("local vs full diagonal blocks")
     rng = np.random.default_rng(41)
