@@ -98,6 +98,7 @@ def _load():
         "hess_state_buffer": (c_int, [vp, ctypes.POINTER(vp)]),
         "hess_local_blocks": (c_int, [vp, i64, i64, c_int, vp]),
         "hess_local_blocks_ex": (c_int, [vp, c_int, i64, i64, i64, c_int, vp, c_int, vp]),
+        "hess_local_blocks_noalloc": (c_int, [vp, c_int, i64, i64, i64, c_int, vp, c_int, vp]),
         "hess_add_batch_grouped": (c_int, [ctypes.POINTER(vp), c_int, vp, i64, vp, ctypes.POINTER(i64), vp]),
         "hess_adopt": (c_int, [vp, vp, vp]),
         "hess_chol_inverse_workspace": (i64, [i64]),

@@ -1171,6 +1171,26 @@ int hess_local_blocks_ex(const void* X, int in_dtype, int64_t n_tokens, int64_t 
   return HESS_OK;
 }
 
+int hess_local_blocks_noalloc(const void* X, int in_dtype, int64_t n_tokens, int64_t d, int64_t ld, int block,
+                              float* out, int accumulate, hess_stream_t stream) {
+  int rc = local_check(X, in_dtype, n_tokens, d, ld, block, out);
+  if (rc != HESS_OK) return rc;
+  const LocalPlan pl = local_plan(n_tokens, (int)d, kLocalPartBytes);
+  if (n_tokens > 0 && pl.part_bytes > kLocalPartBytes)
+    return fail(HESS_EINVAL, "width %lld needs %lld bytes of partial sums; the allocation-free call holds %lld "
+                "(widths up to 262,144)", (long long)d, (long long)pl.part_bytes, (long long)kLocalPartBytes);
+  float* part = nullptr;
+  hipError_t e = hipSuccess;
+  if (n_tokens > 0) {
+    e = local_static_scratch(&part);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress");
+  }
+  const bool vec = n_tokens > 0 && vec_ok(X, ld, d, esize(in_dtype));
+  e = launch_local_blocks(X, in_dtype, n_tokens, (int)d, ld, vec, out, accumulate, pl, part,
+                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HESS_OK : hip_fail(e, "local blocks launch");
+}
+
 int hess_local_blocks(const void* X, int64_t n_tokens, int64_t d, int block, float* out) {
   return hess_local_blocks_ex(X, HESS_BF16, n_tokens, d, d, block, out, 1, nullptr);
 }

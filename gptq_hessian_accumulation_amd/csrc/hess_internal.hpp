@@ -155,6 +155,9 @@ struct LocalPlan {
   int64_t part_bytes;
 };
 LocalPlan local_plan(int64_t n, int d, int64_t part_bytes);
+// Device address, on the current device, of the fixed kLocalPartBytes array
+// used by the allocation-free local-block call (looked up once per device).
+hipError_t local_static_scratch(float** out);
 hipError_t launch_local_blocks(const void* X, int in_dtype, int64_t n, int d, int64_t ld, bool vec, float* out,
                                int accumulate, const LocalPlan& plan, float* part, hipStream_t stream);
 

@@ -30,8 +30,16 @@
 // takes about 1,024 workgroups, fewer token runs when the blocks of a slice
 // would not fit.
 
+#include <mutex>
+
 #include "hess_device.hpp"
 #include "hess_internal.hpp"
+
+// Partial sums of hess_local_blocks_noalloc: a fixed array in device memory,
+// one copy per GPU the library runs on, held until the process ends.  Host
+// code never passes this name to a kernel: it is a host-side stand-in, and
+// the device address comes from hipGetSymbolAddress (local_static_scratch).
+static __device__ __align__(256) float scratch[hess::kLocalPartBytes / sizeof(float)];
 
 namespace hess {
 
@@ -256,6 +264,25 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t stream) {
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
   return hipGetLastError();
+}
+
+hipError_t local_static_scratch(float** out) {
+  constexpr int kDevices = 64;
+  static std::mutex mu;
+  static float* addr[kDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 LocalPlan local_plan(int64_t n, int d, int64_t part_bytes) {

@@ -325,6 +325,23 @@ int hess_local_blocks_ex(const void* X, int in_dtype, int64_t n_tokens, int64_t 
                          int block, float* out, int accumulate, hess_stream_t stream);
 
 /*
+ * hess_local_blocks_noalloc -- hess_local_blocks_ex for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, same result bit for bit
+ * (the same plan and summation order).
+ *   - Allocates nothing: its partial sums live in a fixed 16 MiB array of
+ *     device memory in the library, one per GPU, held until the process ends.
+ *     The first call on a device looks up that array's address there.
+ *   - d up to 262,144 (d/16 blocks of 1 KB must fit the array); wider
+ *     returns HESS_EINVAL.
+ *   - Every call on one GPU shares the array: calls that overlap on a GPU
+ *     (concurrent streams, or another host thread) race and give wrong
+ *     sums; order them.  Nothing in the array needs clearing between calls.
+ */
+int hess_local_blocks_noalloc(const void* X, int in_dtype, int64_t n_tokens, int64_t d, int64_t ld,
+                              int block, float* out, int accumulate, hess_stream_t stream);
+
+/*
  * hess_add_batch_grouped -- for each group e < n_groups:
  *   S_e += X[rows_e]^T X[rows_e],  N_e += |rows_e|,
  * in one launch.  One Hessian per routed expert over the tokens routed to it
