@@ -392,14 +392,12 @@ def run_extras(torch, hs, W, args):
         x = W.torch_rows(gen, 32768, 2048, sc, "bf16", "cuda")
         ridx = torch.from_numpy(row_idx).cuda()
         hsx = [hs.Hessian(2048, torch.bfloat16, staging_bytes=0) for _ in range(64)]  # grouped updates only
-        outs = torch.empty((2048, 2048), dtype=torch.float32, device="cuda")
+        outs = [torch.empty((2048, 2048), dtype=torch.float32, device="cuda") for _ in range(64)]
 
         def moe_once():
-            for h in hsx:
-                h.reset()
+            hs.reset_grouped(hsx)
             hs.add_batch_grouped(hsx, x, offsets, ridx)
-            for h in hsx:
-                h.materialize(0.01, out=outs)
+            hs.materialize_grouped(hsx, 0.01, outs=outs)
 
         moe_once()
         torch.cuda.synchronize()
@@ -407,12 +405,17 @@ def run_extras(torch, hs, W, args):
         e2 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
-            for h in hsx:
-                h.reset()
+            hs.reset_grouped(hsx)
             hs.add_batch_grouped(hsx, x, offsets, ridx)
         e1.record()
         torch.cuda.synchronize()
         grouped_ms = e0.elapsed_time(e1) / steps
+        e0.record()
+        for _ in range(steps):
+            hs.materialize_grouped(hsx, 0.01, outs=outs)
+        e1.record()
+        torch.cuda.synchronize()
+        mat_ms = e0.elapsed_time(e1) / steps
         e0.record()
         for _ in range(steps):
             moe_once()
@@ -420,8 +423,12 @@ def run_extras(torch, hs, W, args):
         torch.cuda.synchronize()
         total_ms = e0.elapsed_time(e2) / steps
         fl = sum(syrk_flops(2048, int(offsets[e + 1] - offsets[e])) for e in range(64))
+        # materialize bytes: each expert's upper triangle read (d (d + 1) / 2 floats), H written (d^2 floats)
+        mat_bytes = 64 * (2.0 * 2048 * 2049 + 4.0 * 2048 * 2048)
         extra["moe_64x2048_grouped"] = {"ms_total": round(total_ms, 3), "ms_reset_plus_grouped": round(grouped_ms, 3),
                                         "tflops_grouped": round(fl / grouped_ms / 1e9, 1),
+                                        "ms_materialize_64": round(mat_ms, 4),
+                                        "materialize_hbm_frac": round(mat_bytes / (mat_ms * 1e-3) / HBM, 4),
                                         "rows": int(offsets[-1])}
         for h in hsx:
             h.close()

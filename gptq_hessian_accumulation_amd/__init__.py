@@ -29,6 +29,8 @@ __all__ = [
     "HessError",
     "local_blocks",
     "add_batch_grouped",
+    "reset_grouped",
+    "materialize_grouped",
     "chol_inverse_upper",
     "gptq_quantize",
     "set_tile_override",
@@ -101,6 +103,9 @@ def _load():
         "hess_local_blocks_noalloc": (c_int, [vp, c_int, i64, i64, i64, c_int, vp, c_int, vp]),
         "hess_add_batch_grouped": (c_int, [ctypes.POINTER(vp), c_int, vp, i64, vp, ctypes.POINTER(i64), vp]),
         "hess_adopt": (c_int, [vp, vp, vp]),
+        "hess_reset_grouped": (c_int, [ctypes.POINTER(vp), c_int, vp]),
+        "hess_materialize_grouped": (c_int, [ctypes.POINTER(vp), c_int, ctypes.c_float, ctypes.c_uint,
+                                             ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), vp]),
         "hess_chol_inverse_workspace": (i64, [i64]),
         "hess_gptq_quantize_workspace": (i64, [i64, i64]),
         "hess_gptq_quantize": (c_int, [vp, i64, i64, i64, vp, i64, vp, c_int, vp, i64, vp, i64, vp, vp, i64, vp,
@@ -465,3 +470,36 @@ def add_batch_grouped(hessians, x: torch.Tensor, offsets, row_idx: torch.Tensor 
     _check(_load().hess_add_batch_grouped(arr, len(hessians), x2.data_ptr() if n > 0 else None, ld,
                                           row_idx.data_ptr() if row_idx is not None else None, oarr,
                                           _stream(stream)))
+
+
+def reset_grouped(hessians, stream=None) -> None:
+    """hessians[e].reset() for every e, in one launch per 64 Hessians of one width."""
+    arr = (ctypes.c_void_p * len(hessians))(*[h._h.value for h in hessians])
+    _check(_load().hess_reset_grouped(arr, len(hessians), _stream(stream)))
+
+
+def materialize_grouped(hessians, damp_percent: float = 0.01, outs=None, neutralize: bool = True, stream=None):
+    """Materialize many Hessians of one width in two launches per 64; returns [(H, dead, damp)] as
+    ``Hessian.materialize`` would for each (the same bits)."""
+    if not hessians:
+        return []
+    d = hessians[0].d
+    dev = torch.device("cuda", hessians[0]._device)
+    if outs is None:
+        outs = [torch.empty((d, d), dtype=torch.float32, device=dev) for _ in hessians]
+    if len(outs) != len(hessians):
+        raise ValueError("one output per Hessian")
+    for o in outs:
+        if o.dtype != torch.float32 or tuple(o.shape) != (d, d) or not o.is_contiguous():
+            raise ValueError("each output must be a contiguous float32 (d, d) GPU tensor")
+    dead = torch.empty((len(hessians), d), dtype=torch.uint8, device=dev)
+    damp = torch.empty((len(hessians), 1), dtype=torch.float32, device=dev)
+    n = len(hessians)
+    hs_arr = (ctypes.c_void_p * n)(*[h._h.value for h in hessians])
+    h_arr = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    d_arr = (ctypes.c_void_p * n)(*[dead[e].data_ptr() for e in range(n)])
+    p_arr = (ctypes.c_void_p * n)(*[damp[e].data_ptr() for e in range(n)])
+    flags = 0 if neutralize else HESS_NO_NEUTRALIZE
+    _check(_load().hess_materialize_grouped(hs_arr, n, float(damp_percent), flags, h_arr, d_arr, p_arr,
+                                            _stream(stream)))
+    return [(outs[e], dead[e].view(torch.bool), damp[e]) for e in range(n)]

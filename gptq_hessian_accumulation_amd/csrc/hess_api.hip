@@ -919,6 +919,95 @@ int hess_materialize(hess_t h, float damp_percent, float* H_out) {
   return hess_materialize_ex(h, damp_percent, 0u, H_out, nullptr, nullptr, h->has_stream ? h->last : nullptr);
 }
 
+namespace {
+// Handles of one grouped call: non-null, distinct, one width; ordered on s.
+int check_group(hess_t* hs, int n_groups, hipStream_t s, bool allow_consumed) {
+  if (!hs || n_groups < 1) return fail(HESS_EINVAL, "need at least one handle");
+  for (int e = 0; e < n_groups; ++e) {
+    if (!hs[e]) return fail(HESS_EINVAL, "null handle %d", e);
+    if (hs[e]->d != hs[0]->d) return fail(HESS_EINVAL, "handle %d differs in width from handle 0", e);
+    if (!allow_consumed && hs[e]->consumed) return fail(HESS_ESTATE, "handle %d was materialized in place", e);
+    for (int f = 0; f < e; ++f)
+      if (hs[f] == hs[e]) return fail(HESS_EINVAL, "handle %d repeats handle %d", e, f);
+  }
+  for (int e = 0; e < n_groups; ++e) {
+    const int rc = order_stream(hs[e], s);
+    if (rc != HESS_OK) return rc;
+  }
+  return HESS_OK;
+}
+}  // namespace
+
+int hess_reset_grouped(hess_t* hs, int n_groups, hess_stream_t stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = check_group(hs, n_groups, s, true);
+  if (rc != HESS_OK) return rc;
+  const int64_t d = hs[0]->d;
+  for (int base = 0; base < n_groups; base += kMatMaxGroups) {
+    const int cnt = std::min(kMatMaxGroups, n_groups - base);
+    float* S[kMatMaxGroups];
+    for (int k = 0; k < cnt; ++k) S[k] = hs[base + k]->S;
+    hipError_t e = launch_zero_upper_grouped(S, cnt, d, (int)d, s);
+    if (e != hipSuccess) return hip_fail(e, "grouped reset launch");
+  }
+  for (int e = 0; e < n_groups; ++e) {
+    hs[e]->stage_n = hs[e]->stage_real = 0;
+    hs[e]->N = 0;
+    hs[e]->consumed = false;
+  }
+  return HESS_OK;
+}
+
+int hess_materialize_grouped(hess_t* hs, int n_groups, float damp_percent, unsigned flags, float* const* H_out,
+                             uint8_t* const* dead_out, float* const* damp_out, hess_stream_t stream) {
+  if (!(damp_percent >= 0.0f && damp_percent < 1.0f)) return fail(HESS_EINVAL, "damp_percent must be in [0, 1)");
+  if (flags & ~HESS_NO_NEUTRALIZE) return fail(HESS_EINVAL, "unknown flags 0x%x", flags);
+  if (!H_out) return fail(HESS_EINVAL, "H_out is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = check_group(hs, n_groups, s, false);
+  if (rc != HESS_OK) return rc;
+  for (int e = 0; e < n_groups; ++e)
+    if (H_out[e] == hs[e]->S) return fail(HESS_EINVAL, "H_out[%d] aliases its Gram buffer; pass NULL for in place", e);
+  for (int e = 0; e < n_groups; ++e) {
+    rc = flush_stage(hs[e], s);
+    if (rc != HESS_OK) return rc;
+  }
+  const int64_t d = hs[0]->d;
+  for (int base = 0; base < n_groups; base += kMatMaxGroups) {
+    const int cnt = std::min(kMatMaxGroups, n_groups - base);
+    MatGroupParams P;
+    std::memset(&P, 0, sizeof(P));
+    P.ngroups = cnt;
+    P.d = (int)d;
+    P.lds = d;
+    P.damp_percent = damp_percent;
+    P.neutralize = (flags & HESS_NO_NEUTRALIZE) ? 0 : 1;
+    for (int k = 0; k < cnt; ++k) {
+      const hess_t h = hs[base + k];
+      P.g[k].S = h->S;
+      P.g[k].H = H_out[base + k] ? H_out[base + k] : h->S;
+      P.g[k].dead = (dead_out && dead_out[base + k]) ? dead_out[base + k] : h->dead;
+      P.g[k].damp = (damp_out && damp_out[base + k]) ? damp_out[base + k] : h->damp;
+      P.g[k].scale = h->N > 0 ? (float)(2.0 / (double)h->N) : 0.0f;
+    }
+    if (materialize_grouped_ok(P)) {
+      hipError_t e = launch_materialize_grouped(P, s);
+      if (e != hipSuccess) return hip_fail(e, "grouped materialize launch");
+    } else {
+      // unaligned buffers or d % 4 != 0: one materialize per Hessian
+      for (int k = 0; k < cnt; ++k) {
+        const hess_t h = hs[base + k];
+        hipError_t e = launch_materialize(h->S, d, (int)d, P.g[k].scale, damp_percent, P.neutralize, P.g[k].H,
+                                          P.g[k].dead, P.g[k].damp, nullptr, s);
+        if (e != hipSuccess) return hip_fail(e, "materialize launch");
+      }
+    }
+  }
+  for (int e = 0; e < n_groups; ++e)
+    if (!H_out[e]) hs[e]->consumed = true;
+  return HESS_OK;
+}
+
 int hess_reset(hess_t h, hess_stream_t stream) {
   if (!h) return fail(HESS_EINVAL, "null handle");
   hipStream_t s = static_cast<hipStream_t>(stream);

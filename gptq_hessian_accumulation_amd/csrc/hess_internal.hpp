@@ -78,9 +78,10 @@ struct BigParams {
 };
 
 // Longest float32 accumulation chain of the 256-tile kernel, in 32-token
-// iterations: longer pieces of a tile are done as chunks of at most this many
-// iterations, each chunk's sums added into the tile's destination.
-constexpr int kBigChain = 512;
+// iterations (32,768 tokens): longer pieces of a tile are done as chunks of at
+// most this many iterations, each chunk's sums added into the tile's
+// destination.
+constexpr int kBigChain = 1024;
 
 hipError_t launch_syrk_big(const BigParams& P, hipStream_t stream);
 hipError_t launch_syrk_big_fixup(const BigParams& P, hipStream_t stream);
@@ -160,6 +161,34 @@ LocalPlan local_plan(int64_t n, int d, int64_t part_bytes);
 hipError_t local_static_scratch(float** out);
 hipError_t launch_local_blocks(const void* X, int in_dtype, int64_t n, int d, int64_t ld, bool vec, float* out,
                                int accumulate, const LocalPlan& plan, float* part, hipStream_t stream);
+
+// Materialize of many Hessians of one width (all 16-byte aligned, d % 4 == 0)
+// in two launches, bit for bit what launch_materialize gives each of them.
+constexpr int kMatMaxGroups = 64;
+struct MatGroup {
+  const float* S;
+  float* H;        // may equal S (in place)
+  uint8_t* dead;
+  float* damp;
+  float scale;
+};
+struct MatGroupParams {
+  int ngroups;
+  int d;
+  int64_t lds;
+  float damp_percent;
+  int neutralize;
+  MatGroup g[kMatMaxGroups];
+};
+bool materialize_grouped_ok(const MatGroupParams& P);
+hipError_t launch_materialize_grouped(const MatGroupParams& P, hipStream_t stream);
+struct ZeroGroupParams {
+  float* S[kMatMaxGroups];
+  int64_t lds;
+  int d;
+  int vec;
+};
+hipError_t launch_zero_upper_grouped(float* const* S, int n, int64_t lds, int d, hipStream_t stream);
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 // Zero S's rows from column 256 * (row / 256) on: the upper triangle and every

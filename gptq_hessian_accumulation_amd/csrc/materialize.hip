@@ -126,9 +126,8 @@ __global__ void __launch_bounds__(256) mirror_kernel(const float* S, int64_t lds
 // same bits), and workgroup 0 writes the dead mask and the damping out, so
 // materialize is one launch.
 template <bool FUSED>
-__global__ void __launch_bounds__(256) mirror_kernel_vec(const float* S, int64_t lds, int d, float scale,
-                                                         float damp_percent, int neutralize, uint8_t* dead,
-                                                         float* damp_dev, float* H, int nt) {
+__device__ __forceinline__ void mirror_vec_body(const float* S, int64_t lds, int d, float scale, float damp_percent,
+                                                int neutralize, uint8_t* dead, float* damp_dev, float* H) {
   __shared__ float tile[kT][kT + 1];
   __shared__ uint8_t dR[kT], dC[kT];
   __shared__ double part[kDiagThreads / 64];
@@ -197,6 +196,38 @@ __global__ void __launch_bounds__(256) mirror_kernel_vec(const float* S, int64_t
   }
 }
 
+template <bool FUSED>
+__global__ void __launch_bounds__(256) mirror_kernel_vec(const float* S, int64_t lds, int d, float scale,
+                                                         float damp_percent, int neutralize, uint8_t* dead,
+                                                         float* damp_dev, float* H, int nt) {
+  mirror_vec_body<FUSED>(S, lds, d, scale, damp_percent, neutralize, dead, damp_dev, H);
+}
+
+__device__ __forceinline__ void mirror_body(const float* S, int64_t lds, int d, float scale, const uint8_t* dead,
+                                            const float* damp_dev, float* H) {
+  mirror_vec_body<false>(S, lds, d, scale, 0.0f, 0, const_cast<uint8_t*>(dead), const_cast<float*>(damp_dev), H);
+}
+
+// Many Hessians of one width in two launches (MatGroupParams): one workgroup
+// per Hessian writes its dead mask and damping with diag_kernel's order
+// (NT as the single path would take it, so the bits are the same), then the
+// tiles of every Hessian go through mirror_kernel_vec<false>'s body with
+// blockIdx.y selecting the Hessian.
+template <int NT>
+__global__ void __launch_bounds__(NT) diag_grouped(MatGroupParams P) {
+  const MatGroup& g = P.g[blockIdx.x];
+  __shared__ double part[NT / 64];
+  for (int j = threadIdx.x; j < P.d; j += NT)
+    g.dead[j] = (P.neutralize && g.S[(int64_t)j * P.lds + j] == 0.0f) ? 1 : 0;
+  const float damp = diag_damp<NT>(g.S, P.lds, P.d, g.scale, P.damp_percent, P.neutralize, part);
+  if (threadIdx.x == 0) g.damp[0] = damp;
+}
+
+__global__ void __launch_bounds__(256) mirror_grouped(MatGroupParams P, int nt) {
+  const MatGroup& g = P.g[blockIdx.y];
+  mirror_body(g.S, P.lds, P.d, g.scale, g.dead, g.damp, g.H);
+}
+
 // Zero the part of S that holds the sum: row i from column 256 * (i / 256)
 // on, which covers every upper-triangle tile of every SYRK tile size (their
 // diagonal tiles included) and about half the bytes of the whole matrix.
@@ -209,6 +240,19 @@ __global__ void __launch_bounds__(256) zero_upper_kernel(float* S, int64_t lds, 
       *reinterpret_cast<float4*>(row + c) = float4{0.0f, 0.0f, 0.0f, 0.0f};
   } else {
     for (int c = c0 + (int)threadIdx.x; c < d; c += 256) row[c] = 0.0f;
+  }
+}
+
+// zero_upper_kernel for many Hessians of one width: blockIdx.y is the Hessian.
+__global__ void __launch_bounds__(256) zero_upper_grouped(ZeroGroupParams P) {
+  const int i = blockIdx.x;
+  const int c0 = (i / 256) * 256;
+  float* row = P.S[blockIdx.y] + (int64_t)i * P.lds;
+  if (P.vec) {
+    for (int c = c0 + 4 * (int)threadIdx.x; c < P.d; c += 4 * 256)
+      *reinterpret_cast<float4*>(row + c) = float4{0.0f, 0.0f, 0.0f, 0.0f};
+  } else {
+    for (int c = c0 + (int)threadIdx.x; c < P.d; c += 256) row[c] = 0.0f;
   }
 }
 
@@ -252,6 +296,41 @@ hipError_t launch_materialize(const float* S, int64_t lds, int d, float scale, f
                        neutralize, dead, damp_dev, H, nt);
   else
     hipLaunchKernelGGL(mirror_kernel, dim3(tiles), dim3(256), 0, stream, S, lds, d, scale, dead, damp_dev, H, nt);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_upper_grouped(float* const* S, int n, int64_t lds, int d, hipStream_t stream) {
+  if (d <= 0 || n <= 0) return hipSuccess;
+  if (n > kMatMaxGroups) return hipErrorInvalidValue;
+  ZeroGroupParams P;
+  for (int e = 0; e < n; ++e) P.S[e] = S[e];
+  P.lds = lds;
+  P.d = d;
+  P.vec = d % 4 == 0 && lds % 4 == 0;
+  for (int e = 0; e < n; ++e) P.vec = P.vec && (reinterpret_cast<uintptr_t>(S[e]) & 15u) == 0;
+  hipLaunchKernelGGL(zero_upper_grouped, dim3((unsigned)d, (unsigned)n), dim3(256), 0, stream, P);
+  return hipGetLastError();
+}
+
+bool materialize_grouped_ok(const MatGroupParams& P) {
+  if (P.d % 4 != 0 || P.lds % 4 != 0) return false;
+  for (int e = 0; e < P.ngroups; ++e)
+    if ((reinterpret_cast<uintptr_t>(P.g[e].S) & 15u) || (reinterpret_cast<uintptr_t>(P.g[e].H) & 15u)) return false;
+  return true;
+}
+
+hipError_t launch_materialize_grouped(const MatGroupParams& P, hipStream_t stream) {
+  if (P.ngroups <= 0) return hipSuccess;
+  if (P.ngroups > kMatMaxGroups || !materialize_grouped_ok(P)) return hipErrorInvalidValue;
+  const int nt = (P.d + kT - 1) / kT;
+  const int tiles = nt * (nt + 1) / 2;
+  if (P.d <= kFusedMaxD)
+    hipLaunchKernelGGL(diag_grouped<kDiagThreads>, dim3(P.ngroups), dim3(kDiagThreads), 0, stream, P);
+  else
+    hipLaunchKernelGGL(diag_grouped<kDiagThreadsWide>, dim3(P.ngroups), dim3(kDiagThreadsWide), 0, stream, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mirror_grouped, dim3(tiles, P.ngroups), dim3(256), 0, stream, P, nt);
   return hipGetLastError();
 }
 

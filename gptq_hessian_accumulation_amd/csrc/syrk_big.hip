@@ -58,8 +58,8 @@
 //    of a blocked tile order, so they share activation panels in that XCD's L2.
 //  * Diagonal tiles load one panel and leave the below-diagonal wave idle.
 //
-// A float32 accumulation chain here is at most kBigChain = 512 iterations
-// (16,384 tokens) of one tile, whatever the batch length: each addition
+// A float32 accumulation chain here is at most kBigChain = 1,024 iterations
+// (32,768 tokens) of one tile, whatever the batch length: each addition
 // brings in one instruction's sum of 32 exact products (rounded once per 8),
 // and a longer part or piece of a tile is cut into chunks whose sums are
 // added into S or into the piece's workspace slot, one addition per chunk.
@@ -121,14 +121,18 @@ __device__ __forceinline__ u32x4 tr_pair(const char* p) {
   return u32x4{a.x, a.y, b.x, b.y};
 }
 
-// Longest float32 accumulation chain, in 32-token iterations (16,384 tokens,
-// 2,048 roundings of an 8-product sum into the accumulator): a longer piece of
+// Longest float32 accumulation chain, in 32-token iterations (32,768 tokens,
+// 4,096 roundings of an 8-product sum into the accumulator): a longer piece of
 // a tile is cut into chunks of at most this many iterations, and each chunk's
 // sums are added into the tile's destination.  Measured against the float64
 // oracle on bf16 data with lognormal column scales, single chains of 16K
 // tokens agree to about 1.1e-5 of the mean diagonal, 37K-token chains to
 // 1.0e-5 and 65K-token chains to 1.75e-5; without a bound the error of one
-// very long batch grows with its length.
+// very long batch grows with its length.  Every chunk end is a read-modify-
+// write of the tile's 256 KB by all workgroups at once (about 20 us per
+// flush at width 2,560); the chunk ends are not staggered, because the
+// workgroups of an XCD share activation panels in its L2 only while they
+// stay at the same iteration (staggered ends measured 2.5% slower).
 constexpr int kChain = kBigChain;
 
 // Edge c of nch near-equal chunks of [k0, k1) (scalar).

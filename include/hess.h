@@ -342,6 +342,35 @@ int hess_local_blocks_noalloc(const void* X, int in_dtype, int64_t n_tokens, int
                               int block, float* out, int accumulate, hess_stream_t stream);
 
 /*
+ * hess_reset_grouped -- hess_reset of n_groups handles of one width in one
+ * launch (per 64 handles): S_e = 0, N_e = 0, staged rows dropped.  For the
+ * routed-expert Hessians of a MoE layer (Model-Optimizer PR 3002 page: the
+ * option applies to every GPTQ Hessian, fused MoE experts included).
+ *   hs        (host) n_groups distinct handles of equal d.
+ * Stream-ordered like hess_reset; clears handles consumed in place too.
+ */
+int hess_reset_grouped(hess_t* hs, int n_groups, hess_stream_t stream);
+
+/*
+ * hess_materialize_grouped -- hess_materialize_ex of n_groups handles of one
+ * width with the same damp_percent and flags, in two launches per 64 handles
+ * (one writes every dead mask and damping, one every H), with the same bits
+ * as n_groups separate hess_materialize_ex calls.
+ *   hs        (host) n_groups distinct handles of equal d, none consumed.
+ *   H_out     (host) array of n_groups device pointers: each a d x d float32
+ *             output, or NULL for that handle in place (it is then consumed,
+ *             as with hess_materialize_ex).  H_out itself must not be NULL.
+ *   dead_out, damp_out  (host) arrays of device pointers (d bytes / one
+ *             float each), or NULL arrays / NULL entries for the handles'
+ *             own buffers.
+ * Each handle's staged rows are folded in first.  Buffers that are not
+ * 16-byte aligned, or d % 4 != 0, take one materialize per handle.
+ */
+int hess_materialize_grouped(hess_t* hs, int n_groups, float damp_percent, unsigned flags,
+                             float* const* H_out, uint8_t* const* dead_out, float* const* damp_out,
+                             hess_stream_t stream);
+
+/*
  * hess_add_batch_grouped -- for each group e < n_groups:
  *   S_e += X[rows_e]^T X[rows_e],  N_e += |rows_e|,
  * in one launch.  One Hessian per routed expert over the tokens routed to it

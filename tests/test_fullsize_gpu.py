@@ -174,13 +174,13 @@ def test_local_blocks_32768x4096_full():
     assert err <= TOL[W.BF16]
 
 
-@pytest.mark.parametrize("d,n", [(2560, 393216), (5888, 20000)])
+@pytest.mark.parametrize("d,n", [(2560, 393216), (5888, 40000)])
 def test_long_single_batch_chains(d, n):
     """One long batch straight into S on the 256-tile kernel, compared in full.  At width 2,560
     the 393,216 tokens give each of 5 token parts of the 55 tiles 2,458 iterations, cut into
-    chunks of at most 512 (16,384 tokens) whose sums are added into S or the part's workspace
-    slot; at width 5,888 (276 tiles: 256 whole tiles, 20 split ones) the whole tiles chain 625
-    iterations in 2 chunks.  The agreement stays at the level of a single 16K-token chain."""
+    chunks of at most 1,024 (32,768 tokens) whose sums are added into S or the part's workspace
+    slot; at width 5,888 (276 tiles: 256 whole tiles, 20 split ones) the whole tiles' 1,250
+    iterations make two chunks.  The agreement stays at the level of a single 32K-token chain."""
     _say(f"full size: long single batch d={d} n={n}")
     x, dead = W.torch_single(d, n, seed=11 + d, dtype=W.BF16, dead_frac=0.0)
     h = hs.Hessian(d, torch.bfloat16)

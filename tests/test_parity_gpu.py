@@ -6,6 +6,7 @@ odd widths, unaligned rows) are covered; exactness cases (the pages' worked
 example, dyadic inputs whose every float32 sum is exact) are compared bitwise.
 """
 
+import ctypes
 import gc
 import sys
 
@@ -675,6 +676,59 @@ def test_grouped_moe_full_size_sampled():
         err = _sampled_gram_check(hsx[e], wl, n_samples=300, seed=e)
         assert hsx[e].nsamples == len(rows)
         assert err <= TOL[W.BF16], (e, err)
+    for h in hsx:
+        h.close()
+
+
+@pytest.mark.parametrize("d", [1032, 2048, 2560])
+def test_grouped_materialize_and_reset_equal_per_handle(d):
+    """hess_materialize_grouped equals one hess_materialize_ex per handle bit for bit (H, dead
+    mask, damping), with empty experts and dead columns, out of place and in place;
+    hess_reset_grouped leaves every handle as a fresh one."""
+    _say(f"grouped materialize / reset d={d}")
+    rng = np.random.default_rng(60 + d)
+    E, T = 9, 900
+    scales = W.column_scales(rng, d)
+    scales[[3, d - 1]] = 0.0                                   # dead columns
+    x = to_device(W.encode(W.normal_rows(rng, T, d, scales), W.BF16), W.BF16)
+    row_idx, offsets = W.moe_routing(rng, T, experts=E, topk=2)
+    n4 = offsets[5] - offsets[4]                               # expert 4: no tokens
+    row_idx = np.concatenate([row_idx[:offsets[4]], row_idx[offsets[5]:]])
+    offsets[5:] -= n4
+    ridx = torch.from_numpy(row_idx).cuda()
+    hsx = [hs.Hessian(d, torch.bfloat16, staging_bytes=0) for _ in range(E)]
+    for flags_neut in (True, False):
+        hs.reset_grouped(hsx)
+        hs.add_batch_grouped(hsx, x, offsets, ridx)
+        got = hs.materialize_grouped(hsx, 0.01, neutralize=flags_neut)
+        for e in range(E):
+            H, dead, damp = hsx[e].materialize(0.01, neutralize=flags_neut)
+            assert torch.equal(got[e][0], H), e
+            assert torch.equal(got[e][1], dead), e
+            assert torch.equal(got[e][2], damp), e
+            assert hsx[e].nsamples == int(offsets[e + 1] - offsets[e])
+        Hr, _, _ = O.materialize(np.zeros((d, d)), 0, 0.01, flags_neut)
+        assert np.array_equal(got[4][0].cpu().numpy(), Hr.astype(np.float32))
+    # in place for every other handle (NULL entries of H_out), through the C ABI
+    refs = [hsx[e].materialize(0.01)[0].clone() for e in range(E)]
+    lib = hs._load()
+    outs = [torch.empty((d, d), dtype=torch.float32, device="cuda") for _ in range(E)]
+    arr = (ctypes.c_void_p * E)(*[h._h.value for h in hsx])
+    harr = (ctypes.c_void_p * E)(*[None if e % 2 else outs[e].data_ptr() for e in range(E)])
+    assert lib.hess_materialize_grouped(arr, E, ctypes.c_float(0.01), 0, harr, None, None,
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+    torch.cuda.synchronize()
+    for e in range(E):
+        got_e = hsx[e].state_tensor() if e % 2 else outs[e]
+        assert torch.equal(got_e, refs[e]), e
+    with pytest.raises(hs.HessError):
+        hsx[1].add_batch(x[:10])                               # consumed in place
+    # reset clears consumed handles; accumulation starts over
+    hs.reset_grouped(hsx)
+    hs.add_batch_grouped(hsx, x, offsets, ridx)
+    again = hs.materialize_grouped(hsx, 0.01)
+    for e in range(E):
+        assert torch.equal(again[e][0], refs[e]), e
     for h in hsx:
         h.close()
 
