@@ -39,24 +39,6 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def ragged_setup(torch, W, d, seed, dtype="bf16", count=360, dead_frac=0.0, device="cuda"):
-    """Batches of U[1,2000] tokens, staged back to back in one device buffer."""
-    rng = np.random.default_rng(seed)
-    sizes = rng.integers(1, 2001, size=count)
-    dead = W.dead_columns(rng, d, dead_frac)
-    gen = W.torch_generator(seed, device)
-    scales = W.torch_column_scales(gen, d, device)
-    if dead.size:
-        scales[torch.from_numpy(dead).to(device)] = 0.0
-    total = int(sizes.sum())
-    buf = W.torch_rows(gen, total, d, scales, dtype, device)
-    views, off = [], 0
-    for n in sizes:
-        views.append(buf[off:off + int(n)])
-        off += int(n)
-    return buf, views, sizes
-
-
 def time_hessian(torch, hs, d, views, steps, warmup, dtype, kernel_timing=False):
     """Whole-Hessian timing with per-step HIP events on the library's stream.
 
@@ -136,31 +118,65 @@ def syrk_bytes(d, n, esize):
     return 4.0 * d * (d + 1) + float(n) * d * esize   # upper S read + write, X read
 
 
-def cpu_baseline(W, O, torch, views, d, total_flops, max_batches=60, budget_s=20.0):
-    """The float64 oracle on the host, on the first batches of the same workload."""
-    t_used, flops_done, nb = 0.0, 0.0, 0
+def _blas_info():
+    """(vendor, threads) of the BLAS numpy calls, from threadpoolctl when it is there."""
+    try:
+        from threadpoolctl import threadpool_info
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                return f"{p.get('internal_api', '?')} {p.get('version', '')}".strip(), int(p.get("num_threads", 1))
+    except Exception:
+        pass
+    return "unknown", len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(W, O, torch, views, d, budget_s=45.0):
+    """The float64 oracle on the host over the whole timed unit: every batch of the same
+    workload (host copies of the device batches) and the materialize.  If the first batches
+    show that the whole unit would take longer than budget_s, the rest is scaled by algorithmic
+    flops (and said so).  The tiny configuration (d=256, 100/37/0 fp32 tokens) is also timed
+    with one BLAS thread."""
+    host = [W.host_copy(v, "bf16") for v in views]
     acc = O.GramAccumulator(d)
-    for x in views[:max_batches]:
-        xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    t_used, flops_done, nb = 0.0, 0.0, 0
+    total_flops = sum(syrk_flops(d, x.shape[0]) for x in host)
+    for x in host:
         t0 = time.perf_counter()
-        acc.add_batch(xb, "bf16")
+        acc.add_batch(x, "bf16")
         t_used += time.perf_counter() - t0
-        flops_done += syrk_flops(d, xb.shape[0])
+        flops_done += syrk_flops(d, x.shape[0])
         nb += 1
-        if t_used > budget_s:
+        if nb >= 20 and t_used * total_flops / flops_done > budget_s:
             break
     t0 = time.perf_counter()
     acc.materialize(0.01)
     t_mat = time.perf_counter() - t0
-    ms = (t_used * total_flops / flops_done + t_mat) * 1e3
+    whole = nb == len(host)
+    ms = (t_used * (1.0 if whole else total_flops / flops_done) + t_mat) * 1e3
+    vendor, threads = _blas_info()
+    cores = len(os.sched_getaffinity(0))
+    tiny = W.tiny_case()
+    tiny_ms = None
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            reps = 20
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                a = O.GramAccumulator(tiny.d)
+                for b in tiny.batches:
+                    a.add_batch(b, tiny.dtype)
+                a.materialize(0.01)
+            tiny_ms = (time.perf_counter() - t0) * 1e3 / reps
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    return {"value": round(ms, 1), "unit": "ms/Hessian", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 NumPy oracle on the first {nb} of {len(views)} batches "
-                      f"({t_used:.1f} s), scaled by algorithmic flops to the whole Hessian, plus materialize"}
+        pass
+    sample = (f"float64 NumPy oracle over the whole timed unit: all {len(host)} batches ({t_used:.1f} s) plus "
+              f"materialize" if whole else
+              f"float64 NumPy oracle on the first {nb} of {len(host)} batches ({t_used:.1f} s), scaled by "
+              f"algorithmic flops to the whole Hessian, plus materialize")
+    return {"value": round(ms, 1), "unit": "ms/Hessian", "cores": threads, "kind": "oracle", "sample": sample,
+            "affinity_cores": cores, "blas": vendor, "blas_threads": threads,
+            "tiny_d256_single_thread_ms": None if tiny_ms is None else round(tiny_ms, 3)}
 
 
 def main():
@@ -195,7 +211,7 @@ def main():
     torch.cuda.set_device(0)
     d = 2560
     log("staging d=2560 ragged workload")
-    buf, views, sizes = ragged_setup(torch, W, d, seed=1)
+    buf, views, sizes, _ = W.torch_ragged(d, seed=1)
     N = int(sizes.sum())
     torch.cuda.synchronize()
     log(f"timing {args.steps} Hessians after {args.warmup} warm-ups")
@@ -269,8 +285,9 @@ def main():
     if not args.no_cpu:
         import oracle as O
         log("cpu baseline (oracle)")
-        buf, views, sizes = ragged_setup(torch, W, d, seed=1)
-        result["cpu_baseline"] = cpu_baseline(W, O, torch, views, d, flops)
+        buf, views, sizes, _ = W.torch_ragged(d, seed=1)
+        result["cpu_baseline"] = cpu_baseline(W, O, torch, views, d)
+        del buf, views
     print(json.dumps(result), flush=True)
 
 
@@ -339,7 +356,7 @@ def run_extras(torch, hs, W, args):
         # the d=2560 ragged workload with fp16 activations, staged in bf16:
         # each batch is rounded to bf16 by the staging copy
         log("d=2560 ragged, fp16 activations staged in bf16")
-        buf, views, sizes = ragged_setup(torch, W, 2560, seed=1, dtype="f16")
+        buf, views, sizes, _ = W.torch_ragged(2560, seed=1, dtype="f16")
         N = int(sizes.sum())
         ms, _, _, _ = time_hessian(torch, hs, 2560, views, steps, 1, torch.bfloat16)
         fl = syrk_flops(2560, N)
@@ -350,7 +367,7 @@ def run_extras(torch, hs, W, args):
     # d=4096 ragged (bf16 and fp32), dead columns 1%
     for dt, tdt in (() if "d4096_ragged" not in want else (("bf16", torch.bfloat16), ("f32", torch.float32))):
         log(f"d=4096 ragged {dt}")
-        buf, views, sizes = ragged_setup(torch, W, 4096, seed=2, dtype=dt, dead_frac=0.01)
+        buf, views, sizes, _ = W.torch_ragged(4096, seed=2, dtype=dt, dead_frac=0.01)
         N = int(sizes.sum())
         ms, _, _, _ = time_hessian(torch, hs, 4096, views, steps, 1, tdt)
         fl = syrk_flops(4096, N)
@@ -361,9 +378,7 @@ def run_extras(torch, hs, W, args):
     # d=4096, one 32768-token batch
     for dt, tdt in (() if "d4096_single" not in want else (("bf16", torch.bfloat16), ("f32", torch.float32))):
         log(f"d=4096 single 32K batch {dt}")
-        gen = W.torch_generator(2, "cuda")
-        sc = W.torch_column_scales(gen, 4096, "cuda")
-        x = W.torch_rows(gen, 32768, 4096, sc, dt, "cuda")
+        x, _ = W.torch_single(4096, 32768, seed=2, dtype=dt, dead_frac=0.01)   # 41 zeroed columns
         ms, _, _, (nl, _, kms) = time_hessian(torch, hs, 4096, [x], steps, 1, tdt, kernel_timing=True)
         kern = kms / nl
         fl = syrk_flops(4096, 32768)
@@ -478,7 +493,7 @@ def run_extras(torch, hs, W, args):
         # and replayed: the same kernels without the host's per-call launch path
         log("headline Hessian as a replayed graph")
         dg = 2560
-        buf, views, _ = ragged_setup(torch, W, dg, seed=1)
+        buf, views, _, _ = W.torch_ragged(dg, seed=1)
         outg = torch.empty((dg, dg), dtype=torch.float32, device="cuda")
         hg = hs.Hessian(dg, torch.bfloat16)
 
