@@ -10,9 +10,10 @@
 // Gram diagonal is exactly zero; its row and column are zero already and its
 // diagonal becomes 1, so neutralization precedes the mean.
 //
-// Two kernels (one when H does not alias S and d <= 2,048: then every
-// workgroup of the tiled pass does step 1's reduction itself, in the same
-// order, and the first one writes the dead mask and the damping):
+// One kernel when H does not alias S (and rows are 16-byte aligned): every
+// workgroup of the tiled pass reads its tile's dead flags from S's diagonal,
+// the diagonal tiles also take step 1's reduction (same order), and the first
+// one writes the dead mask and the damping.  Otherwise two kernels:
 //  1. one workgroup reads the d diagonal entries, writes the dead mask and
 //     reduces the (neutralized) diagonal in float64 in a fixed order; the
 //     damping is that mean times damp_percent, rounded once to float32;
@@ -29,8 +30,7 @@ namespace hess {
 
 namespace {
 
-constexpr int kDiagThreads = 256;       // the one-launch path's workgroup (and its sum order)
-constexpr int kDiagThreadsWide = 1024;  // the diagonal pass above that path's widths
+constexpr int kDiagThreads = 256;       // the damping's sum order (and the tiled pass's workgroup)
 
 // damp_percent * mean of the (neutralized) scaled diagonal, in float64 in a
 // fixed order for NT threads: thread t sums entries t, t + NT, ..., then wave
@@ -41,11 +41,18 @@ template <int NT>
 __device__ __forceinline__ float diag_damp(const float* S, int64_t lds, int d, float scale, float damp_percent,
                                            int neutralize, double* part) {
   double sum = 0.0;
-  for (int j = threadIdx.x; j < d; j += NT) {
-    const float s = S[(int64_t)j * lds + j];
-    const bool dj = neutralize && (s == 0.0f);
-    sum += (double)(dj ? 1.0f : s * scale);
+  auto term = [&](float s) { return (double)((neutralize && s == 0.0f) ? 1.0f : s * scale); };
+  int j = threadIdx.x;
+  // eight strided diagonal loads in flight at a time; the additions keep
+  // the order j = t, t + NT, t + 2 NT, ...
+  for (; j + 7 * NT < d; j += 8 * NT) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = S[(int64_t)(j + k * NT) * lds + j + k * NT];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sum += term(v[k]);
   }
+  for (; j < d; j += NT) sum += term(S[(int64_t)j * lds + j]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sum += __shfl_down(sum, off, 64);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sum;
@@ -55,9 +62,8 @@ __device__ __forceinline__ float diag_damp(const float* S, int64_t lds, int d, f
   return (float)((double)damp_percent * (tot / (double)d));
 }
 
-// NT = kDiagThreads at the one-launch path's widths (so that an in-place
-// materialize, which takes this path, gives the same bits), else
-// kDiagThreadsWide (shorter per-thread chains on a wide diagonal).
+// The two-launch path (in place, or rows not 16-byte aligned) runs this with
+// NT = kDiagThreads, the order the one-launch path's diagonal tiles use.
 template <int NT>
 __global__ void __launch_bounds__(NT) diag_kernel(const float* S, int64_t lds, int d, float scale,
                                                   float damp_percent, int neutralize, uint8_t* dead, float* damp_dev) {
@@ -120,11 +126,12 @@ __global__ void __launch_bounds__(256) mirror_kernel(const float* S, int64_t lds
 // 16-byte aligned): thread t moves columns 4 (t % 16) .. +3 of tile rows
 // t / 16 + 16 k (k < 4), so 16 lanes cover one 256-byte tile row; the tile's
 // row and column dead flags are read once into LDS.
-// FUSED: H does not alias S and d is small enough for every workgroup to
-// read the whole diagonal: each workgroup takes the damping and its tile's
-// dead flags from S itself (the same fixed-order sum as diag_kernel, so the
-// same bits), and workgroup 0 writes the dead mask and the damping out, so
-// materialize is one launch.
+// FUSED: H does not alias S, so S's diagonal stays intact throughout: each
+// workgroup takes its tile's dead flags from S itself, only the diagonal
+// tiles (the ones that add the damping) take the damping's fixed-order sum
+// over the diagonal (the same bits as diag_kernel), and workgroup 0 (tile
+// (0, 0)) writes the dead mask and the damping out, so materialize is one
+// launch.
 template <bool FUSED>
 __device__ __forceinline__ void mirror_vec_body(const float* S, int64_t lds, int d, float scale, float damp_percent,
                                                 int neutralize, uint8_t* dead, float* damp_dev, float* H) {
@@ -144,7 +151,7 @@ __device__ __forceinline__ void mirror_vec_body(const float* S, int64_t lds, int
     auto is_dead = [&](int j) { return neutralize && S[(int64_t)j * lds + j] == 0.0f; };
     if (t < kT) dR[t] = r0 + t < d ? is_dead(r0 + t) : 0;
     else if (t < 2 * kT) dC[t - kT] = c0 + t - kT < d ? is_dead(c0 + t - kT) : 0;
-    damp = diag_damp<kDiagThreads>(S, lds, d, scale, damp_percent, neutralize, part);
+    damp = I == J ? diag_damp<kDiagThreads>(S, lds, d, scale, damp_percent, neutralize, part) : 0.0f;
     if (b == 0) {
       for (int j = t; j < d; j += 256) dead[j] = is_dead(j) ? 1 : 0;
       if (t == 0) damp_dev[0] = damp;
@@ -210,7 +217,7 @@ __device__ __forceinline__ void mirror_body(const float* S, int64_t lds, int d, 
 
 // Many Hessians of one width in two launches (MatGroupParams): one workgroup
 // per Hessian writes its dead mask and damping with diag_kernel's order
-// (NT as the single path would take it, so the bits are the same), then the
+// (the single path's order, so the bits are the same), then the
 // tiles of every Hessian go through mirror_kernel_vec<false>'s body with
 // blockIdx.y selecting the Hessian.
 template <int NT>
@@ -265,12 +272,6 @@ hipError_t launch_zero_upper(float* S, int64_t lds, int d, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Widest d for the one-launch materialize: every workgroup reads the d
-// diagonal entries (one L2 line each) besides its tile, which costs more
-// than the second launch saves above this width (measured per materialize:
-// 13.6 against 15.5 us at 2,048, 16.5 against 14.3 us at 2,560).
-constexpr int kFusedMaxD = 2048;
-
 hipError_t launch_materialize(const float* S, int64_t lds, int d, float scale, float damp_percent, int neutralize,
                               float* H, uint8_t* dead, float* damp_dev, double* /*sum_scratch*/,
                               hipStream_t stream) {
@@ -278,17 +279,13 @@ hipError_t launch_materialize(const float* S, int64_t lds, int d, float scale, f
   const int tiles = nt * (nt + 1) / 2;
   const bool vec = d % 4 == 0 && lds % 4 == 0 && (reinterpret_cast<uintptr_t>(S) & 15u) == 0 &&
                    (reinterpret_cast<uintptr_t>(H) & 15u) == 0;
-  if (vec && H != S && d <= kFusedMaxD) {
+  if (vec && H != S) {
     hipLaunchKernelGGL(mirror_kernel_vec<true>, dim3(tiles), dim3(256), 0, stream, S, lds, d, scale, damp_percent,
                        neutralize, dead, damp_dev, H, nt);
     return hipGetLastError();
   }
-  if (d <= kFusedMaxD)
-    hipLaunchKernelGGL(diag_kernel<kDiagThreads>, dim3(1), dim3(kDiagThreads), 0, stream, S, lds, d, scale,
-                       damp_percent, neutralize, dead, damp_dev);
-  else
-    hipLaunchKernelGGL(diag_kernel<kDiagThreadsWide>, dim3(1), dim3(kDiagThreadsWide), 0, stream, S, lds, d, scale,
-                       damp_percent, neutralize, dead, damp_dev);
+  hipLaunchKernelGGL(diag_kernel<kDiagThreads>, dim3(1), dim3(kDiagThreads), 0, stream, S, lds, d, scale,
+                     damp_percent, neutralize, dead, damp_dev);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (vec)
@@ -324,10 +321,7 @@ hipError_t launch_materialize_grouped(const MatGroupParams& P, hipStream_t strea
   if (P.ngroups > kMatMaxGroups || !materialize_grouped_ok(P)) return hipErrorInvalidValue;
   const int nt = (P.d + kT - 1) / kT;
   const int tiles = nt * (nt + 1) / 2;
-  if (P.d <= kFusedMaxD)
-    hipLaunchKernelGGL(diag_grouped<kDiagThreads>, dim3(P.ngroups), dim3(kDiagThreads), 0, stream, P);
-  else
-    hipLaunchKernelGGL(diag_grouped<kDiagThreadsWide>, dim3(P.ngroups), dim3(kDiagThreadsWide), 0, stream, P);
+  hipLaunchKernelGGL(diag_grouped<kDiagThreads>, dim3(P.ngroups), dim3(kDiagThreads), 0, stream, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mirror_grouped, dim3(tiles, P.ngroups), dim3(256), 0, stream, P, nt);
