@@ -92,6 +92,7 @@ def _load():
         "hess_token_count": (c_int, [vp, ctypes.POINTER(i64)]),
         "hess_set_tile_override": (c_int, [c_int]),
         "hess_set_staging": (c_int, [c_int]),
+        "hess_set_async_flush": (c_int, [c_int]),
         "hess_set_group_chunk": (c_int, [i64]),
         "hess_flush": (c_int, [vp, vp]),
         "hess_set_timing": (c_int, [vp, c_int]),
@@ -180,6 +181,11 @@ def _as_rows(x: torch.Tensor, d: int):
 def set_staging(enable: bool) -> None:
     """Enable (default) or disable the staging of short batches; process-wide."""
     _check(_load().hess_set_staging(1 if enable else 0))
+
+
+def set_async_flush(enable: bool) -> None:
+    """Enable (default) or disable asynchronous staging flushes for Hessians created afterwards; process-wide."""
+    _check(_load().hess_set_async_flush(1 if enable else 0))
 
 
 def set_group_chunk(nbytes: int) -> None:

@@ -42,6 +42,24 @@ struct hess_s {
   // blocks of d 16-byte chunks (8 tokens of one feature), each batch padded
   // with zero rows to a multiple of 8; always flushed by that kernel
   bool stage_t8 = false;
+  // Asynchronous flushes (transposed staging whose halves are each long
+  // enough for the 256-tile kernel): the staging allocation is two halves of
+  // stage_cap tokens.  A full half is folded in on the handle's own stream
+  // (`side`) with fewer workgroups than CUs (async_wgs), which leaves CUs free for the
+  // staging copies that go on into the other half on the caller's stream.
+  // side_done[k] is recorded after half k's flush; busy[k]: that flush may
+  // still be reading half k; pending: a side flush may still be writing S
+  // (side_last is the newest).  Everything that touches S, or writes a busy
+  // half, first makes its stream wait for those events.
+  bool async = false;
+  void* half[2] = {nullptr, nullptr};
+  int cur = 0;
+  hipStream_t side = nullptr;
+  hipEvent_t side_done[2] = {nullptr, nullptr};
+  hipEvent_t fork = nullptr;
+  bool busy[2] = {false, false};
+  bool pending = false;
+  int side_last = 0;
   int64_t N = 0;
   bool consumed = false;     // in-place materialize done
   bool has_stream = false;
@@ -109,6 +127,7 @@ thread_local char g_err[512] = "";
 int g_tile_override = 0;  // 0 = automatic; 64, 128 or 256 force that SYRK tile edge where it applies
 int64_t g_group_chunk = 0; // test hook: cap on the gathered bytes per grouped launch (0 = scratch size)
 bool g_staging = true;    // thin-batch staging enabled (process-wide)
+bool g_async = true;      // asynchronous flushes for handles created from now on (process-wide)
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -291,7 +310,12 @@ bool use_big(const hess_s* h, int64_t n, bool vec) {
 //
 // t8: X is a transposed staging buffer (ld = chunks per 8-token block, n a
 // multiple of 8); n_real = rows that are batch rows, for the timing record.
-int run_big(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s, bool t8 = false, int64_t n_real = -1) {
+//
+// max_wgs caps the workgroups of the split tiles (a multiple of 8, at most
+// 256); the asynchronous flush takes fewer than the CUs so that staging
+// copies on another stream find free CUs.
+int run_big(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s, bool t8 = false, int64_t n_real = -1,
+            int max_wgs = kCUs) {
   BigParams B;
   std::memset(&B, 0, sizeof(B));
   B.t8 = t8 ? 1 : 0;
@@ -315,10 +339,10 @@ int run_big(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s, bool 
   if (B.sk_tiles > 0) {
     // enough aligned parts per tile to give every CU one; the parts past the
     // first 256 (fewer than sk_tiles) are shared out as pieces
-    B.parts = (int)std::min<int64_t>((kCUs + B.sk_tiles - 1) / B.sk_tiles, B.niter);
+    B.parts = (int)std::min<int64_t>((max_wgs + B.sk_tiles - 1) / B.sk_tiles, B.niter);
     B.part_len = (B.niter + B.parts - 1) / B.parts;
     B.items = B.sk_tiles * B.parts;
-    B.grid_sk = std::min(kCUs, B.items);
+    B.grid_sk = std::min(max_wgs, B.items);
     if (B.grid_sk >= 8) B.grid_sk -= B.grid_sk % 8;  // whole XCD rows
     B.excess_total = (int64_t)(B.items - B.grid_sk) * B.part_len;
   }
@@ -419,13 +443,79 @@ int run_syrk(hess_t h, const void* X, int64_t n, int64_t ld, hipStream_t s) {
   return HESS_OK;
 }
 
-// Fold the staged rows into S.
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+
+int pending_under_capture() {
+  return fail(HESS_ESTATE, "an asynchronous staging flush is pending: flush, materialize or reset the handle "
+              "before capturing it");
+}
+
+// Make s wait until the handle's asynchronous flushes are done (before s
+// touches S): then every half is free again.
+int join_side(hess_t h, hipStream_t s) {
+  if (!h->pending) return HESS_OK;
+  if (capturing(s)) return pending_under_capture();
+  const hipError_t e = hipStreamWaitEvent(s, h->side_done[h->side_last], 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  h->pending = false;
+  h->busy[0] = h->busy[1] = false;
+  return HESS_OK;
+}
+
+// Make s wait until the current half may be written again.
+int claim_half(hess_t h, hipStream_t s) {
+  if (!h->busy[h->cur]) return HESS_OK;
+  if (capturing(s)) return pending_under_capture();
+  const hipError_t e = hipStreamWaitEvent(s, h->side_done[h->cur], 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  h->busy[h->cur] = false;
+  return HESS_OK;
+}
+
+// Fold the staged rows into S, on s.
 int flush_stage(hess_t h, hipStream_t s) {
-  if (h->stage_n == 0) return HESS_OK;
-  const int rc = h->stage_t8 ? run_big(h, h->stage, h->stage_n, h->d, s, true, h->stage_real)
-                             : run_syrk(h, h->stage, h->stage_n, h->stage_ld, s);
+  int rc = join_side(h, s);
+  if (rc != HESS_OK || h->stage_n == 0) return rc;
+  rc = h->stage_t8 ? run_big(h, h->stage, h->stage_n, h->d, s, true, h->stage_real)
+                   : run_syrk(h, h->stage, h->stage_n, h->stage_ld, s);
   if (rc == HESS_OK) h->stage_n = h->stage_real = 0;
   return rc;
+}
+
+// Workgroups of an asynchronous flush (each holds a whole CU; the rest of
+// the CUs run the staging copies).  Measured on MI355X at width 2,560 with a
+// 187K-token flush and 180 staging copies of the next batches on the caller's
+// stream: 1.73 ms one after the other, 1.96 ms side by side at 256 workgroups
+// (the copies find no free CU), 1.56 / 1.52 / 1.43 ms at 224 / 208 / 192.
+// A flush's cost per token grows as d^2 and a copy's as d, so wider handles
+// leave fewer CUs to the copies: the ragged d=4096 Hessian took 6.55 ms with
+// synchronous flushes and 6.57 / 6.38 / 6.23 / 7.00 ms with asynchronous ones
+// at 192 / 216 / 224 / 240 workgroups (the headline at d=2560: 3.07 ms at
+// 192, 3.21 at 224, 3.85 at 240).
+int async_wgs(int64_t d) { return d <= 3072 ? 192 : 224; }
+
+// A full half: fold it into S on the side stream (after everything enqueued
+// on s so far) and go on staging into the other half.  Under graph capture
+// the flush runs on s itself.
+int flush_full_half(hess_t h, hipStream_t s) {
+  if (!h->async || capturing(s)) return flush_stage(h, s);
+  hipError_t e = hipEventRecord(h->fork, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
+  if (e != hipSuccess) return hip_fail(e, "side stream ordering");
+  const int rc = run_big(h, h->stage, h->stage_n, h->d, h->side, true, h->stage_real, async_wgs(h->d));
+  if (rc != HESS_OK) return rc;
+  e = hipEventRecord(h->side_done[h->cur], h->side);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  h->busy[h->cur] = true;
+  h->pending = true;
+  h->side_last = h->cur;
+  h->cur ^= 1;
+  h->stage = h->half[h->cur];
+  h->stage_n = h->stage_real = 0;
+  return HESS_OK;
 }
 
 // Grouped update on 256-tiles: the groups' rows are gathered into the
@@ -703,6 +793,20 @@ hess_t hess_create_ex(int64_t d, int in_dtype, int64_t staging_bytes) {
       h->stage_t8 = g_tile_override == kBig ||
                     (d >= kBigMinD && (int64_t)h->ntiles256 * niter >= kBigMinWork * kCUs);
     }
+    // two halves flushed asynchronously when each half still makes a long
+    // enough flush for the 256-tile kernel (and no tile is done whole)
+    if (e == hipSuccess && h->stage_t8 && g_async && g_tile_override == 0 && h->ntiles256 < kCUs) {
+      const int64_t hcap = stage_tokens(d, esize(in_dtype), staging_bytes / 2);
+      if (hcap > 0 && (int64_t)h->ntiles256 * (hcap / kBigKI) >= kBigMinWork * kCUs) {
+        h->async = true;
+        h->stage_cap = hcap;
+        h->half[0] = h->stage;
+        h->half[1] = static_cast<char*>(h->stage) + hcap * h->stage_ld * esize(in_dtype);
+        e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+        for (int k = 0; k < 2 && e == hipSuccess; ++k) e = hipEventCreateWithFlags(&h->side_done[k], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
+      }
+    }
   }
   if (e == hipSuccess) e = hipMemset(h->S, 0, sbytes);
   if (e == hipSuccess) e = hipMemset(h->damp, 0, 64);
@@ -719,6 +823,10 @@ hess_t hess_create_ex(int64_t d, int in_dtype, int64_t staging_bytes) {
     if (h->stage) (void)hipFree(h->stage);
     if (h->order256) (void)hipFree(h->order256);
     if (h->ev) (void)hipEventDestroy(h->ev);
+    if (h->side) (void)hipStreamDestroy(h->side);
+    for (hipEvent_t ev : h->side_done)
+      if (ev) (void)hipEventDestroy(ev);
+    if (h->fork) (void)hipEventDestroy(h->fork);
     delete h;
     return nullptr;
   }
@@ -729,6 +837,13 @@ int hess_destroy(hess_t h) {
   if (!h) return fail(HESS_EINVAL, "null handle");
   hipError_t e = hipSuccess;
   if (h->has_stream) e = hipStreamSynchronize(h->last);
+  if (h->side) {
+    const hipError_t e2 = hipStreamSynchronize(h->side);
+    if (e == hipSuccess) e = e2;
+    (void)hipStreamDestroy(h->side);
+    for (hipEvent_t ev : h->side_done) (void)hipEventDestroy(ev);
+    (void)hipEventDestroy(h->fork);
+  }
   (void)hipFree(h->S);
   (void)hipFree(h->dead);
   (void)hipFree(h->damp);
@@ -756,9 +871,11 @@ int hess_add_batch(hess_t h, const void* X, int64_t n_tokens, int64_t ld, hess_s
     // thin batch: append its rows to the staging buffer
     const int64_t rows = h->stage_t8 ? (n_tokens + 7) / 8 * 8 : n_tokens;
     if (h->stage_n + rows > h->stage_cap) {
-      rc = flush_stage(h, s);
+      rc = flush_full_half(h, s);
       if (rc != HESS_OK) return rc;
     }
+    rc = claim_half(h, s);
+    if (rc != HESS_OK) return rc;
     char* dst = static_cast<char*>(h->stage) + h->stage_n * h->stage_ld * esize(h->dtype);
     hipError_t e = h->stage_t8 ? launch_copy_rows_t8(X, ld, n_tokens, h->d, dst, s)
                                : launch_copy_rows(X, ld, esize(h->dtype), n_tokens, h->d, dst, h->stage_ld, s);
@@ -798,9 +915,11 @@ int hess_add_batch_cast(hess_t h, const void* X, int x_dtype, int64_t n_tokens, 
   const int64_t unit = h->stage_t8 ? 8 : 1;
   for (int64_t off = 0; off < n_tokens;) {
     if (h->stage_cap - h->stage_n < unit) {
-      rc = flush_stage(h, s);
+      rc = flush_full_half(h, s);
       if (rc != HESS_OK) return rc;
     }
+    rc = claim_half(h, s);
+    if (rc != HESS_OK) return rc;
     const int64_t space = h->stage_cap - h->stage_n;
     int64_t take = n_tokens - off < space ? n_tokens - off : space;
     if (take < n_tokens - off) take = take / unit * unit;
@@ -842,6 +961,7 @@ int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int e = 0; e < n_groups; ++e) {
     int rc = order_stream(hs[e], s);
+    if (rc == HESS_OK) rc = join_side(hs[e], s);
     if (rc != HESS_OK) return rc;
   }
   const bool vec = vec_ok(X, ld, h0->d, esize(h0->dtype));
@@ -931,7 +1051,8 @@ int check_group(hess_t* hs, int n_groups, hipStream_t s, bool allow_consumed) {
       if (hs[f] == hs[e]) return fail(HESS_EINVAL, "handle %d repeats handle %d", e, f);
   }
   for (int e = 0; e < n_groups; ++e) {
-    const int rc = order_stream(hs[e], s);
+    int rc = order_stream(hs[e], s);
+    if (rc == HESS_OK) rc = join_side(hs[e], s);
     if (rc != HESS_OK) return rc;
   }
   return HESS_OK;
@@ -1012,6 +1133,7 @@ int hess_reset(hess_t h, hess_stream_t stream) {
   if (!h) return fail(HESS_EINVAL, "null handle");
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = order_stream(h, s);
+  if (rc == HESS_OK) rc = join_side(h, s);
   if (rc != HESS_OK) return rc;
   hipError_t e = launch_zero_upper(h->S, h->d, (int)h->d, s);
   if (e != hipSuccess) return hip_fail(e, "reset launch");
@@ -1046,6 +1168,7 @@ int hess_adopt(hess_t dst, hess_t src, hess_stream_t stream) {
   rc = order_stream(dst, s);
   if (rc != HESS_OK) return rc;
   rc = flush_stage(src, s);  // the source's sum is complete
+  if (rc == HESS_OK) rc = join_side(dst, s);
   if (rc != HESS_OK) return rc;
   hipError_t e = hipMemcpyAsync(dst->S, src->S, (size_t)src->d * src->d * sizeof(float), hipMemcpyDeviceToDevice, s);
   if (e != hipSuccess) return hip_fail(e, "adopt copy");
@@ -1146,6 +1269,11 @@ int hess_set_group_chunk(int64_t bytes) {
 
 int hess_set_staging(int enable) {
   g_staging = enable != 0;
+  return HESS_OK;
+}
+
+int hess_set_async_flush(int enable) {
+  g_async = enable != 0;
   return HESS_OK;
 }
 

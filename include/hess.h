@@ -244,6 +244,21 @@ int hess_flush(hess_t h, hess_stream_t stream);
  * staging of short batches. */
 int hess_set_staging(int enable);
 
+/*
+ * hess_set_async_flush -- process-wide switch (default on) for handles
+ * created afterwards: a handle with transposed staging whose halves each make
+ * a long 256-tile flush splits its staging buffer in two; a full half is
+ * folded into the sum on the handle's own stream, with fewer workgroups than
+ * CUs, while the caller's stream goes on staging batches into the other half.
+ * Calls that read or write the sum (materialize, flush, reset, adopt, long
+ * batches, grouped calls) first make the caller's stream wait for it, so the
+ * results are stream-ordered as before.  Under HIP graph capture the flush
+ * stays on the capturing stream; capture a handle only after a flush,
+ * materialize or reset of it, so that no asynchronous flush is pending.
+ * Off: one buffer, every flush on the caller's stream.
+ */
+int hess_set_async_flush(int enable);
+
 /* Test hook, process-wide: cap (bytes, > 0) on the rows gathered per
  * 256-tile grouped launch (hess_add_batch_grouped fills its gather buffer as
  * often as needed, splitting groups that do not fit); 0 (default) = the

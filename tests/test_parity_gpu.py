@@ -1101,3 +1101,131 @@ def test_new_entry_points_on_a_side_stream():
     assert np.array_equal(codes.cpu().numpy(), cr)
     for o in (h, f, m):
         o.close()
+
+
+# ------------------------------------------------------ asynchronous flush --
+
+ASYNC_D = 2048
+ASYNC_STAGING = 540 << 20      # halves of 69,120 tokens: each flush long enough for the 256-tile kernel
+ASYNC_HALF = 69120
+
+
+def _async_workload(seed, count=150, long_at=None):
+    """Batches of U[500, 2000] tokens (all staged at width 2,048), optionally a 5,000-token one."""
+    rng = np.random.default_rng(seed)
+    sizes = [int(v) for v in rng.integers(500, 2001, count)]
+    if long_at is not None:
+        sizes.insert(long_at, 5000)        # 5,000 tokens: a pass of its own straight into S
+    return W.ragged_case(ASYNC_D, sizes, seed=seed, dtype=W.BF16, dead_frac=0.02)
+
+
+def test_async_flush_streams_and_long_batch():
+    """Full halves are folded in on the handle's own stream while staging goes on; batches arrive
+    on two streams in turn, a long batch in the middle takes its own pass (after the pending
+    flush), and the result matches the oracle (token count exact, dead mask bit for bit)."""
+    _say("async flush: two streams and a long batch")
+    hs.set_async_flush(True)
+    wl = _async_workload(71, count=200, long_at=100)
+    xs = [to_device(b, W.BF16) for b in wl.batches]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    h = hs.Hessian(ASYNC_D, torch.bfloat16, staging_bytes=ASYNC_STAGING)
+    for i, x in enumerate(xs):
+        h.add_batch(x, stream=s1 if (i // 40) % 2 == 0 else s2)
+    H, dead, dmp = h.materialize(0.01, stream=s2)
+    s2.synchronize()
+    Hr, deadr, dmpr, Nr = run_oracle(wl, 0.01, True)
+    assert h.nsamples == Nr > 2 * ASYNC_HALF   # at least two halves filled: two asynchronous flushes
+    assert np.array_equal(dead.cpu().numpy(), deadr)
+    err = agreement(H.cpu().numpy(), Hr)
+    print(f"  async: {err:.3e}")
+    assert err <= TOL[W.BF16]
+    h.close()
+
+
+def test_async_flush_two_handles_share_the_workspace():
+    """Two handles flush asynchronously, interleaved on one stream (their flushes share the
+    device's split workspace); a third adopts one of them while its flush is pending; a reset
+    and a destroy meet pending flushes too."""
+    _say("async flush: two handles, adopt, reset, destroy")
+    hs.set_async_flush(True)
+    wa, wb = _async_workload(72, count=150), _async_workload(73, count=150)
+    xa = [to_device(b, W.BF16) for b in wa.batches]
+    xb = [to_device(b, W.BF16) for b in wb.batches]
+    torch.cuda.synchronize()
+    ha = hs.Hessian(ASYNC_D, torch.bfloat16, staging_bytes=ASYNC_STAGING)
+    hb = hs.Hessian(ASYNC_D, torch.bfloat16, staging_bytes=ASYNC_STAGING)
+    for x1, x2 in zip(xa, xb):
+        ha.add_batch(x1)
+        hb.add_batch(x2)
+    hc = hs.Hessian(ASYNC_D, torch.bfloat16, staging_bytes=ASYNC_STAGING)
+    hc.adopt_from(ha)                                  # ha's flush may be pending here
+    for h, wl in ((ha, wa), (hb, wb), (hc, wa)):
+        H, dead, _ = h.materialize(0.01)
+        Hr, deadr, _, Nr = run_oracle(wl, 0.01, True)
+        assert h.nsamples == Nr
+        assert np.array_equal(dead.cpu().numpy(), deadr)
+        assert agreement(H.cpu().numpy(), Hr) <= TOL[W.BF16]
+    # reset with a flush pending, then a fresh accumulation
+    for x in xa:
+        hb.add_batch(x)
+    hb.reset()
+    for x in xa[:30]:
+        hb.add_batch(x)
+    H, _, _ = hb.materialize(0.0, neutralize=False)
+    sub = W.Workload(d=ASYNC_D, dtype=W.BF16, batches=wa.batches[:30])
+    Hr, _, _, _ = run_oracle(sub, 0.0, False)
+    assert agreement(H.cpu().numpy(), Hr) <= TOL[W.BF16]
+    for x in xa:
+        ha.add_batch(x)
+    ha.close()                                         # a flush may be pending: destroy waits for it
+    hb.close()
+    hc.close()
+
+
+def test_async_flush_pending_is_refused_under_capture():
+    """With an asynchronous flush pending, a captured call that needs the sum is refused
+    (HESS_ESTATE); after an eager flush the same sequence captures and replays equal to eager."""
+    _say("async flush: capture")
+    hs.set_async_flush(True)
+    wl = _async_workload(74, count=120)
+    xs = [to_device(b, W.BF16) for b in wl.batches]
+    out = torch.empty((ASYNC_D, ASYNC_D), dtype=torch.float32, device="cuda")
+    h = hs.Hessian(ASYNC_D, torch.bfloat16, staging_bytes=ASYNC_STAGING)
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        for x in xs:
+            h.add_batch(x)                              # a flush of the first half is now pending
+    torch.cuda.current_stream().wait_stream(cs)
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(hs.HessError) as e:
+        with torch.cuda.graph(g, stream=cs):
+            h.materialize(0.01, out=out)
+    assert e.value.code == -4
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cs):
+        h.flush()
+    torch.cuda.synchronize()
+    small = xs[:20]
+
+    def one():
+        h.reset()
+        for x in small:
+            h.add_batch(x)
+        h.materialize(0.01, out=out)
+
+    with torch.cuda.stream(cs):
+        one()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=cs):
+        one()
+    for _ in range(2):
+        out.zero_()
+        torch.cuda.synchronize()
+        g2.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+    h.close()
