@@ -558,9 +558,28 @@ def run_extras(torch, hs, W, args):
                     h.add_batch(views[i % 16])
                 launches, _, kms = h.timing()
                 h.set_timing(False)
+                # the same 200 calls captured once in a HIP graph and replayed: the GPU's time per
+                # batch without the host's per-call cost
+                cs = torch.cuda.Stream()
+                cs.wait_stream(torch.cuda.current_stream())
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cs):
+                    for i in range(reps):
+                        h.add_batch(views[i % 16])
+                g.replay()
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(3):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                g_us = e0.elapsed_time(e1) * 1e3 / (3 * reps)
+                del g
                 byts = 4.0 * dt * (dt + 1) + (2.0 if xdt == "bf16" else 4.0) * n * dt
                 res[f"n{n}"] = {"batch_us": round(b_us, 2), "kernel_us": round(kms * 1e3 / launches, 2),
-                                "GBps": round(byts / b_us / 1e3, 1), "hbm_frac": round(byts / (b_us * 1e-6) / HBM, 4)}
+                                "GBps": round(byts / b_us / 1e3, 1), "hbm_frac": round(byts / (b_us * 1e-6) / HBM, 4),
+                                "graph_batch_us": round(g_us, 2),
+                                "graph_hbm_frac": round(byts / (g_us * 1e-6) / HBM, 4)}
             h.close()
             extra[f"thin_direct_d{dt}" + ("" if xdt == "bf16" else "_f32")] = res
             del xs

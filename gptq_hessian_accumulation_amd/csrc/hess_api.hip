@@ -499,9 +499,17 @@ int async_wgs(int64_t d) { return d <= 3072 ? 192 : 224; }
 
 // A full half: fold it into S on the side stream (after everything enqueued
 // on s so far) and go on staging into the other half.  Under graph capture
-// the flush runs on s itself.
+// the flush runs on s itself, with the same workgroups (the same token parts,
+// so the same bits as outside a capture).
 int flush_full_half(hess_t h, hipStream_t s) {
-  if (!h->async || capturing(s)) return flush_stage(h, s);
+  if (!h->async) return flush_stage(h, s);
+  if (capturing(s)) {
+    int rc = join_side(h, s);
+    if (rc != HESS_OK || h->stage_n == 0) return rc;
+    rc = run_big(h, h->stage, h->stage_n, h->d, s, true, h->stage_real, async_wgs(h->d));
+    if (rc == HESS_OK) h->stage_n = h->stage_real = 0;
+    return rc;
+  }
   hipError_t e = hipEventRecord(h->fork, s);
   if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
   if (e != hipSuccess) return hip_fail(e, "side stream ordering");

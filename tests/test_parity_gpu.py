@@ -1185,7 +1185,9 @@ def test_async_flush_two_handles_share_the_workspace():
 
 def test_async_flush_pending_is_refused_under_capture():
     """With an asynchronous flush pending, a captured call that needs the sum is refused
-    (HESS_ESTATE); after an eager flush the same sequence captures and replays equal to eager."""
+    (HESS_ESTATE); after an eager flush, a whole Hessian whose halves fill captures (its flushes
+    then run on the capturing stream with the same workgroups) and every replay equals the eager
+    run, whose flushes went on the handle's own stream, bit for bit."""
     _say("async flush: capture")
     hs.set_async_flush(True)
     wl = _async_workload(74, count=120)
@@ -1207,11 +1209,10 @@ def test_async_flush_pending_is_refused_under_capture():
     with torch.cuda.stream(cs):
         h.flush()
     torch.cuda.synchronize()
-    small = xs[:20]
 
-    def one():
+    def one():                                          # fills two halves: flushes inside the sequence
         h.reset()
-        for x in small:
+        for x in xs:
             h.add_batch(x)
         h.materialize(0.01, out=out)
 
