@@ -25,6 +25,9 @@
 using namespace hess;
 
 struct hess_s {
+  // every call on the handle holds this lock (recursive: some calls call
+  // others), so calls from several host threads do not interleave
+  std::recursive_mutex mu;
   int64_t d = 0;
   int dtype = HESS_BF16;
   int device = 0;
@@ -78,6 +81,7 @@ struct hess_s {
 };
 
 struct hess_imx_s {
+  std::recursive_mutex mu;
   int64_t d = 0;
   int dtype = HESS_BF16;
   float* acc = nullptr;      // d floats: the running per-column sums of squares
@@ -124,6 +128,22 @@ struct LocalScratch {
 LocalScratch g_local[kMaxDevices];
 
 thread_local char g_err[512] = "";
+
+using HLock = std::lock_guard<std::recursive_mutex>;
+
+// The locks of several handles, taken in address order (so that two calls
+// over overlapping sets of handles cannot deadlock); null entries are skipped.
+struct GroupLock {
+  std::vector<std::unique_lock<std::recursive_mutex>> held;
+  GroupLock(hess_t* hs, int n) {
+    std::vector<hess_t> v;
+    for (int e = 0; hs && e < n; ++e)
+      if (hs[e]) v.push_back(hs[e]);
+    std::sort(v.begin(), v.end(), std::less<hess_t>());
+    v.erase(std::unique(v.begin(), v.end()), v.end());
+    for (hess_t h : v) held.emplace_back(h->mu);
+  }
+};
 int g_tile_override = 0;  // 0 = automatic; 64, 128 or 256 force that SYRK tile edge where it applies
 int64_t g_group_chunk = 0; // test hook: cap on the gathered bytes per grouped launch (0 = scratch size)
 bool g_staging = true;    // thin-batch staging enabled (process-wide)
@@ -844,10 +864,17 @@ hess_t hess_create_ex(int64_t d, int in_dtype, int64_t staging_bytes) {
 int hess_destroy(hess_t h) {
   if (!h) return fail(HESS_EINVAL, "null handle");
   hipError_t e = hipSuccess;
-  if (h->has_stream) e = hipStreamSynchronize(h->last);
+  {
+    // calls already inside the handle finish first; the caller must not
+    // start new ones once it destroys the handle
+    HLock lock(h->mu);
+    if (h->has_stream) e = hipStreamSynchronize(h->last);
+    if (h->side) {
+      const hipError_t e2 = hipStreamSynchronize(h->side);
+      if (e == hipSuccess) e = e2;
+    }
+  }
   if (h->side) {
-    const hipError_t e2 = hipStreamSynchronize(h->side);
-    if (e == hipSuccess) e = e2;
     (void)hipStreamDestroy(h->side);
     for (hipEvent_t ev : h->side_done) (void)hipEventDestroy(ev);
     (void)hipEventDestroy(h->fork);
@@ -856,7 +883,9 @@ int hess_destroy(hess_t h) {
   (void)hipFree(h->dead);
   (void)hipFree(h->damp);
   if (h->ws) (void)hipFree(h->ws);
-  if (h->stage) (void)hipFree(h->stage);
+  // the staging allocation starts at its first half (stage may point at the second)
+  void* stage_base = h->async ? h->half[0] : h->stage;
+  if (stage_base) (void)hipFree(stage_base);
   if (h->order256) (void)hipFree(h->order256);
   (void)hipEventDestroy(h->ev);
   for (hipEvent_t ev : h->tev) (void)hipEventDestroy(ev);
@@ -866,6 +895,7 @@ int hess_destroy(hess_t h) {
 
 int hess_add_batch(hess_t h, const void* X, int64_t n_tokens, int64_t ld, hess_stream_t stream) {
   if (!h) return fail(HESS_EINVAL, "null handle");
+  HLock lock(h->mu);
   if (h->consumed) return fail(HESS_ESTATE, "handle was materialized in place; hess_reset it first");
   if (n_tokens < 0) return fail(HESS_EINVAL, "n_tokens = %lld < 0", (long long)n_tokens);
   if (ld < h->d) return fail(HESS_EINVAL, "ld = %lld < d = %lld", (long long)ld, (long long)h->d);
@@ -903,6 +933,7 @@ int hess_add_batch(hess_t h, const void* X, int64_t n_tokens, int64_t ld, hess_s
 
 int hess_add_batch_cast(hess_t h, const void* X, int x_dtype, int64_t n_tokens, int64_t ld, hess_stream_t stream) {
   if (!h) return fail(HESS_EINVAL, "null handle");
+  HLock lock(h->mu);
   if (x_dtype != HESS_BF16 && x_dtype != HESS_F32 && x_dtype != HESS_F16)
     return fail(HESS_EINVAL, "unknown activation dtype %d", x_dtype);
   if (x_dtype == h->dtype) return hess_add_batch(h, X, n_tokens, ld, stream);
@@ -947,6 +978,7 @@ int hess_add_batch_cast(hess_t h, const void* X, int x_dtype, int64_t n_tokens, 
 int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld, const int32_t* row_idx,
                            const int64_t* offsets, hess_stream_t stream) {
   if (!hs || n_groups < 1) return fail(HESS_EINVAL, "need at least one handle");
+  GroupLock lock(hs, n_groups);
   if (!offsets) return fail(HESS_EINVAL, "offsets is NULL");
   const hess_t h0 = hs[0];
   if (!h0) return fail(HESS_EINVAL, "null handle 0");
@@ -1020,6 +1052,7 @@ int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld, 
 int hess_materialize_ex(hess_t h, float damp_percent, unsigned flags, float* H_out, uint8_t* dead_out,
                         float* damp_out, hess_stream_t stream) {
   if (!h) return fail(HESS_EINVAL, "null handle");
+  HLock lock(h->mu);
   if (h->consumed) return fail(HESS_ESTATE, "handle was materialized in place; hess_reset it first");
   if (!(damp_percent >= 0.0f && damp_percent < 1.0f))
     return fail(HESS_EINVAL, "damp_percent must be in [0, 1)");
@@ -1043,6 +1076,7 @@ int hess_materialize_ex(hess_t h, float damp_percent, unsigned flags, float* H_o
 
 int hess_materialize(hess_t h, float damp_percent, float* H_out) {
   if (!h) return fail(HESS_EINVAL, "null handle");
+  HLock lock(h->mu);
   if (!H_out) return fail(HESS_EINVAL, "H_out is NULL (use hess_materialize_ex for in place)");
   return hess_materialize_ex(h, damp_percent, 0u, H_out, nullptr, nullptr, h->has_stream ? h->last : nullptr);
 }
@@ -1069,6 +1103,7 @@ int check_group(hess_t* hs, int n_groups, hipStream_t s, bool allow_consumed) {
 
 int hess_reset_grouped(hess_t* hs, int n_groups, hess_stream_t stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  GroupLock lock(hs, hs ? n_groups : 0);
   int rc = check_group(hs, n_groups, s, true);
   if (rc != HESS_OK) return rc;
   const int64_t d = hs[0]->d;
@@ -1093,6 +1128,7 @@ int hess_materialize_grouped(hess_t* hs, int n_groups, float damp_percent, unsig
   if (flags & ~HESS_NO_NEUTRALIZE) return fail(HESS_EINVAL, "unknown flags 0x%x", flags);
   if (!H_out) return fail(HESS_EINVAL, "H_out is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  GroupLock lock(hs, hs ? n_groups : 0);
   int rc = check_group(hs, n_groups, s, false);
   if (rc != HESS_OK) return rc;
   for (int e = 0; e < n_groups; ++e)
@@ -1139,6 +1175,7 @@ int hess_materialize_grouped(hess_t* hs, int n_groups, float damp_percent, unsig
 
 int hess_reset(hess_t h, hess_stream_t stream) {
   if (!h) return fail(HESS_EINVAL, "null handle");
+  HLock lock(h->mu);
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = order_stream(h, s);
   if (rc == HESS_OK) rc = join_side(h, s);
@@ -1153,6 +1190,7 @@ int hess_reset(hess_t h, hess_stream_t stream) {
 
 int hess_flush(hess_t h, hess_stream_t stream) {
   if (!h) return fail(HESS_EINVAL, "null handle");
+  HLock lock(h->mu);
   if (h->consumed) return fail(HESS_ESTATE, "handle was materialized in place; hess_reset it first");
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = order_stream(h, s);
@@ -1163,6 +1201,8 @@ int hess_flush(hess_t h, hess_stream_t stream) {
 int hess_adopt(hess_t dst, hess_t src, hess_stream_t stream) {
   if (!dst || !src) return fail(HESS_EINVAL, "null handle");
   if (dst == src) return HESS_OK;
+  hess_t pair[2] = {dst, src};
+  GroupLock lock(pair, 2);
   if (dst->d != src->d) return fail(HESS_EINVAL, "width mismatch: %lld vs %lld", (long long)dst->d, (long long)src->d);
   // the staging type and the staging buffer (the chunking of the sum) decide
   // what the sum holds and its rounding order: only equal settings share
@@ -1287,6 +1327,7 @@ int hess_set_async_flush(int enable) {
 
 int hess_set_timing(hess_t h, int on) {
   if (!h) return fail(HESS_EINVAL, "null handle");
+  HLock lock(h->mu);
   h->timing = on != 0;
   h->tcount = 0;
   return HESS_OK;
@@ -1294,6 +1335,7 @@ int hess_set_timing(hess_t h, int on) {
 
 int hess_timing(hess_t h, int64_t* launches, int64_t* tokens, double* ms) {
   if (!h || !launches || !tokens || !ms) return fail(HESS_EINVAL, "null argument");
+  HLock lock(h->mu);
   double total = 0.0;
   int64_t tok = 0;
   if (h->tcount > 0) {
@@ -1316,12 +1358,14 @@ int hess_timing(hess_t h, int64_t* launches, int64_t* tokens, double* ms) {
 
 int hess_token_count(hess_t h, int64_t* n_out) {
   if (!h || !n_out) return fail(HESS_EINVAL, "null argument");
+  HLock lock(h->mu);
   *n_out = h->N;
   return HESS_OK;
 }
 
 int hess_info(hess_t h, int64_t* d_out, int* in_dtype_out) {
   if (!h) return fail(HESS_EINVAL, "null handle");
+  HLock lock(h->mu);
   if (d_out) *d_out = h->d;
   if (in_dtype_out) *in_dtype_out = h->dtype;
   return HESS_OK;
@@ -1329,6 +1373,7 @@ int hess_info(hess_t h, int64_t* d_out, int* in_dtype_out) {
 
 int hess_state_buffer(hess_t h, const float** S_out) {
   if (!h || !S_out) return fail(HESS_EINVAL, "null argument");
+  HLock lock(h->mu);
   *S_out = h->S;
   return HESS_OK;
 }
@@ -1459,7 +1504,10 @@ hess_imx_t hess_imatrix_create(int64_t d, int in_dtype) {
 int hess_imatrix_destroy(hess_imx_t m) {
   if (!m) return fail(HESS_EINVAL, "null handle");
   hipError_t e = hipSuccess;
-  if (m->has_stream) e = hipStreamSynchronize(m->last);
+  {
+    HLock lock(m->mu);
+    if (m->has_stream) e = hipStreamSynchronize(m->last);
+  }
   (void)hipFree(m->acc);
   (void)hipFree(m->part);
   (void)hipEventDestroy(m->ev);
@@ -1469,6 +1517,7 @@ int hess_imatrix_destroy(hess_imx_t m) {
 
 int hess_imatrix_add_batch(hess_imx_t m, const void* X, int64_t n_tokens, int64_t ld, hess_stream_t stream) {
   if (!m) return fail(HESS_EINVAL, "null handle");
+  HLock lock(m->mu);
   if (n_tokens < 0) return fail(HESS_EINVAL, "n_tokens = %lld < 0", (long long)n_tokens);
   if (ld < m->d) return fail(HESS_EINVAL, "ld = %lld < d = %lld", (long long)ld, (long long)m->d);
   if (n_tokens == 0) return HESS_OK;
@@ -1486,6 +1535,7 @@ int hess_imatrix_add_batch(hess_imx_t m, const void* X, int64_t n_tokens, int64_
 
 int hess_imatrix_read(hess_imx_t m, float* out, int64_t* n_out, hess_stream_t stream) {
   if (!m) return fail(HESS_EINVAL, "null handle");
+  HLock lock(m->mu);
   if (!out) return fail(HESS_EINVAL, "out is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = imx_order_stream(m, s);
@@ -1498,6 +1548,7 @@ int hess_imatrix_read(hess_imx_t m, float* out, int64_t* n_out, hess_stream_t st
 
 int hess_imatrix_reset(hess_imx_t m, hess_stream_t stream) {
   if (!m) return fail(HESS_EINVAL, "null handle");
+  HLock lock(m->mu);
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = imx_order_stream(m, s);
   if (rc != HESS_OK) return rc;

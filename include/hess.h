@@ -26,7 +26,11 @@
  * - A handle remembers the stream of its last call.  A call on a different
  *   stream first makes that stream wait for the previous one (an event), so
  *   updates of one Hessian never overlap.  Different handles are independent.
- *   A handle must not be used from two host threads at the same time.
+ *   Every call on a handle holds that handle's lock for its duration (grouped
+ *   calls lock their handles in address order), so calls from several host
+ *   threads never interleave; between threads, the order of the calls is the
+ *   order in which they take the lock (GPTQModel PR 2979 serializes updates
+ *   of one device's accumulator the same way, with a lock).
  * - Errors are returned as negative codes; the library never aborts and has
  *   no fallback paths.  hess_last_error() gives the calling thread's message
  *   for its last failed call.

@@ -1230,3 +1230,59 @@ def test_async_flush_pending_is_refused_under_capture():
         torch.cuda.synchronize()
         assert torch.equal(out, ref)
     h.close()
+
+
+def test_async_destroy_returns_staging_memory():
+    """A handle destroyed while it stages into its second half frees its whole staging
+    allocation (the allocation starts at the first half)."""
+    _say("async flush: destroy frees staging")
+    hs.set_async_flush(True)
+    wl = _async_workload(75, count=60)
+    xs = [to_device(b, W.BF16) for b in wl.batches]
+    warm = hs.Hessian(ASYNC_D, torch.bfloat16, staging_bytes=ASYNC_STAGING)   # device workspaces
+    warm.close()
+    gc.collect()
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    h = hs.Hessian(ASYNC_D, torch.bfloat16, staging_bytes=ASYNC_STAGING)
+    for x in xs:
+        h.add_batch(x)                  # 60 batches of ~1,250 tokens: past the first half
+    assert h.nsamples > ASYNC_HALF
+    h.close()
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 >= free0, (free0, free1)
+
+
+def test_one_handle_from_two_host_threads():
+    """Two host threads add batches to one handle at the same time: the per-handle lock keeps
+    every call whole, so the token count is exact and H matches the oracle."""
+    import threading
+    _say("one handle, two host threads")
+    d = 1032
+    wl = W.ragged_case(d, [int(v) for v in np.random.default_rng(76).integers(1, 800, 200)], seed=76,
+                       dtype=W.BF16, dead_frac=0.02)
+    xs = [to_device(b, W.BF16) for b in wl.batches]
+    torch.cuda.synchronize()
+    h = hs.Hessian(d, torch.bfloat16)
+    errors = []
+
+    def worker(part):
+        try:
+            for x in part:
+                h.add_batch(x)
+        except Exception as exc:       # reported below
+            errors.append(exc)
+
+    threads = [threading.Thread(target=worker, args=(xs[k::2],)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    H, dead, _ = h.materialize(0.01)
+    Hr, deadr, _, Nr = run_oracle(wl, 0.01, True)
+    assert h.nsamples == Nr
+    assert np.array_equal(dead.cpu().numpy(), deadr)
+    assert agreement(H.cpu().numpy(), Hr) <= TOL[W.BF16]
+    h.close()
