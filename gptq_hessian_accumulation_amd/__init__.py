@@ -140,9 +140,17 @@ def exported_symbols() -> list:
     return sorted(set(re.findall(r"\b(hess_[a-z0-9_]+)\s*\(", text)))
 
 
-def _stream(stream=None) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+# The current stream's raw handle without building a Stream object (about 2.5 us
+# per call saved, which matters at one call per short calibration batch).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream=None, device=None) -> int:
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device() if device is None else device)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _dtype_code(dtype) -> int:
@@ -223,6 +231,7 @@ class Hessian:
             raise HessError(-1, lib.hess_last_error().decode(errors="replace"))
         self._h = ctypes.c_void_p(h)
         self._device = torch.cuda.current_device()
+        self._add = lib.hess_add_batch
 
     # -- accumulation ----------------------------------------------------
     def add_batch(self, x: torch.Tensor, stream=None) -> None:
@@ -233,9 +242,11 @@ class Hessian:
         x2, n, ld = _as_rows(x, self.d)
         ptr = x2.data_ptr() if n > 0 else None
         if code == self._code:
-            _check(_load().hess_add_batch(self._h, ptr, n, ld, _stream(stream)))
+            rc = self._add(self._h, ptr, n, ld, _stream(stream))
         else:
-            _check(_load().hess_add_batch_cast(self._h, ptr, code, n, ld, _stream(stream)))
+            rc = _load().hess_add_batch_cast(self._h, ptr, code, n, ld, _stream(stream))
+        if rc != 0:
+            _check(rc)
 
     def materialize(self, damp_percent: float = 0.01, out: torch.Tensor | None = None, neutralize: bool = True,
                     stream=None):
