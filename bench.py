@@ -532,7 +532,7 @@ def run_extras(torch, hs, W, args):
         # thin batches added straight into S (a handle without staging): the 64-tile kernel, whose
         # time is the read-modify-write of S's upper triangle (4 d (d + 1) bytes) plus the batch
         # (2 n d bytes).  batch_us: 200 back-to-back calls between two events on the stream (the
-        # host's per-call cost, about 7 us from Python, bounds it when the kernel is shorter);
+        # host's per-call cost, about 5 us from Python, bounds it when the kernel is shorter);
         # kernel_us: the library's HIP events around each launch (their own cost included).
         for dt, xdt in ((4096, "bf16"), (2560, "bf16"), (4096, "f32")):
             log(f"thin batches straight into S, d={dt} {xdt}")

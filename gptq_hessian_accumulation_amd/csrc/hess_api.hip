@@ -85,7 +85,7 @@ struct hess_imx_s {
   int64_t d = 0;
   int dtype = HESS_BF16;
   float* acc = nullptr;      // d floats: the running per-column sums of squares
-  float* part = nullptr;     // (kImxSplits + 32) x d floats: one batch's split partials and their run sums
+  float* part = nullptr;     // kImxSplits x d floats: one batch's split partials
   int64_t N = 0;
   bool has_stream = false;
   hipStream_t last = nullptr;
@@ -1484,7 +1484,7 @@ hess_imx_t hess_imatrix_create(int64_t d, int in_dtype) {
   m->d = d;
   m->dtype = in_dtype;
   hipError_t e = hipMalloc(&m->acc, (size_t)d * sizeof(float));
-  if (e == hipSuccess) e = hipMalloc(&m->part, (size_t)(kImxSplits + 32) * d * sizeof(float));
+  if (e == hipSuccess) e = hipMalloc(&m->part, (size_t)kImxSplits * d * sizeof(float));
   if (e == hipSuccess) e = hipMemset(m->acc, 0, (size_t)d * sizeof(float));
   if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev, hipEventDisableTiming);
   if (e == hipSuccess) e = hipDeviceSynchronize();
