@@ -24,6 +24,7 @@
 //     all global accesses are coalesced (16-byte accesses when d % 4 == 0).
 //     Only S's upper triangle is read, so H may alias S (in-place materialize).
 
+#include "hess_device.hpp"
 #include "hess_internal.hpp"
 
 namespace hess {
@@ -125,7 +126,9 @@ __global__ void __launch_bounds__(256) mirror_kernel(const float* S, int64_t lds
 // The same pass with 16-byte accesses, for d % 4 == 0 (every S and H row
 // 16-byte aligned): thread t moves columns 4 (t % 16) .. +3 of tile rows
 // t / 16 + 16 k (k < 4), so 16 lanes cover one 256-byte tile row; the tile's
-// row and column dead flags are read once into LDS.
+// row and column dead flags are read once into LDS.  H is written with
+// nontemporal stores (nothing here reads it back; on MI355X they took the
+// pass from 14.7 to 10.5 us at width 2,560 and from 23.5 to 20.8 us at 4,096).
 // FUSED: H does not alias S, so S's diagonal stays intact throughout: each
 // workgroup takes its tile's dead flags from S itself, only the diagonal
 // tiles (the ones that add the damping) take the damping's fixed-order sum
@@ -187,7 +190,7 @@ __device__ __forceinline__ void mirror_vec_body(const float* S, int64_t lds, int
       const float sv = (I == J && c < r) ? tile[c][r] : tile[r][c];
       o[q] = hval(sv, scale, di, dC[c] != 0, gi == gj + q, damp);
     }
-    *reinterpret_cast<float4*>(H + (int64_t)gi * lds + gj) = float4{o[0], o[1], o[2], o[3]};
+    __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(H + (int64_t)gi * lds + gj));
   }
   if (I == J) return;
   // tile (J, I): H[c0 + c][r0 + r] = value of S[r0 + r][c0 + c]
@@ -199,7 +202,7 @@ __device__ __forceinline__ void mirror_vec_body(const float* S, int64_t lds, int
     float o[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) o[q] = hval(tile[cq + q][c], scale, di, dR[cq + q] != 0, false, damp);
-    *reinterpret_cast<float4*>(H + (int64_t)gi * lds + gj) = float4{o[0], o[1], o[2], o[3]};
+    __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(H + (int64_t)gi * lds + gj));
   }
 }
 
