@@ -103,6 +103,8 @@ def _load():
         "hess_local_blocks_ex": (c_int, [vp, c_int, i64, i64, i64, c_int, vp, c_int, vp]),
         "hess_local_blocks_noalloc": (c_int, [vp, c_int, i64, i64, i64, c_int, vp, c_int, vp]),
         "hess_add_batch_grouped": (c_int, [ctypes.POINTER(vp), c_int, vp, i64, vp, ctypes.POINTER(i64), vp]),
+        "hess_add_batch_grouped_ex": (c_int, [ctypes.POINTER(vp), c_int, vp, i64, i64, vp, ctypes.POINTER(i64), vp]),
+        "hess_set_group_direct": (c_int, [c_int]),
         "hess_adopt": (c_int, [vp, vp, vp]),
         "hess_reset_grouped": (c_int, [ctypes.POINTER(vp), c_int, vp]),
         "hess_materialize_grouped": (c_int, [ctypes.POINTER(vp), c_int, ctypes.c_float, ctypes.c_uint,
@@ -199,6 +201,11 @@ def set_async_flush(enable: bool) -> None:
 def set_group_chunk(nbytes: int) -> None:
     """Cap the rows gathered per 256-tile grouped launch (bytes; 0 = the whole buffer); process-wide."""
     _check(_load().hess_set_group_chunk(int(nbytes)))
+
+
+def set_group_direct(enable: bool) -> None:
+    """Grouped 256-tile updates read the routed rows in place (default) or gather them first; process-wide."""
+    _check(_load().hess_set_group_direct(1 if enable else 0))
 
 
 def set_tile_override(edge: int) -> None:
@@ -484,9 +491,9 @@ def add_batch_grouped(hessians, x: torch.Tensor, offsets, row_idx: torch.Tensor 
         raise ValueError("offsets exceed the number of rows of x")
     arr = (ctypes.c_void_p * len(hessians))(*[h._h.value for h in hessians])
     oarr = (ctypes.c_int64 * len(offs))(*offs)
-    _check(_load().hess_add_batch_grouped(arr, len(hessians), x2.data_ptr() if n > 0 else None, ld,
-                                          row_idx.data_ptr() if row_idx is not None else None, oarr,
-                                          _stream(stream)))
+    _check(_load().hess_add_batch_grouped_ex(arr, len(hessians), x2.data_ptr() if n > 0 else None, n, ld,
+                                             row_idx.data_ptr() if row_idx is not None else None, oarr,
+                                             _stream(stream)))
 
 
 def reset_grouped(hessians, stream=None) -> None:

@@ -146,6 +146,7 @@ struct GroupLock {
 };
 int g_tile_override = 0;  // 0 = automatic; 64, 128 or 256 force that SYRK tile edge where it applies
 int64_t g_group_chunk = 0; // test hook: cap on the gathered bytes per grouped launch (0 = scratch size)
+bool g_group_direct = true; // grouped 256-tile updates read the routed rows in place when X's size is known
 bool g_staging = true;    // thin-batch staging enabled (process-wide)
 bool g_async = true;      // asynchronous flushes for handles created from now on (process-wide)
 
@@ -551,16 +552,30 @@ int flush_full_half(hess_t h, hipStream_t s) {
 // group, zero-padded), then one launch takes whole upper tiles of every
 // group.  Groups that do not fit are split; the scratch is refilled as many
 // times as needed (each fill is one copy and one SYRK launch).
-int grouped_big(hess_t* hs, int n_groups, const void* X, int64_t ld, const int32_t* row_idx,
+//
+// direct (X's row count nrows known, nrows * ld * 2 < 2^31): no gather; the
+// launch reads each group's rows where they are, through a table of their
+// byte offsets in X (built per launch in the same buffer), with the same
+// operands in the same order, so the same bits as the gathered path.
+int grouped_big(hess_t* hs, int n_groups, const void* X, int64_t nrows, int64_t ld, const int32_t* row_idx,
                 const int64_t* offsets, hipStream_t s) {
   const hess_t h0 = hs[0];
   const int64_t d = h0->d;
   BigWorkspace& W = g_big[h0->device];
   std::lock_guard<std::mutex> lock(W.mu);
-  // the gather buffer: grown (never shrunk) to this call's rows, up to 4 GiB
+  const bool direct = g_group_direct && nrows >= 0 && nrows * ld * 2 < ((int64_t)1 << 31);
+  // the gather buffer (or row table): grown (never shrunk) to this call's
+  // rows, up to 4 GiB
   int64_t need = 0;
-  for (int e = 0; e < n_groups; ++e) need += (offsets[e + 1] - offsets[e] + 7) / 8 * 8 * d * 2;
-  need = std::min(need, kGroupScratchMax) + kGroupSchedBytes;
+  if (direct) {
+    // each fill's table starts at the buffer's start; all groups' entries
+    // bound any fill's
+    for (int e = 0; e < n_groups; ++e) need += (offsets[e + 1] - offsets[e] + kBigKI - 1) / kBigKI * kBigKI;
+    need = (need + kRowTableSlack) * 4 + kGroupSchedBytes;
+  } else {
+    for (int e = 0; e < n_groups; ++e) need += (offsets[e + 1] - offsets[e] + 7) / 8 * 8 * d * 2;
+    need = std::min(need, kGroupScratchMax) + kGroupSchedBytes;
+  }
   if (W.gbytes < need) {
     hipError_t e = hipSuccess;
     if (W.gptr) {
@@ -588,7 +603,8 @@ int grouped_big(hess_t* hs, int n_groups, const void* X, int64_t ld, const int32
   }
   int64_t cap_bytes = W.gbytes - kGroupSchedBytes;
   if (g_group_chunk > 0) cap_bytes = std::min(cap_bytes, g_group_chunk);
-  const int64_t cap_blocks = cap_bytes / (d * 16);  // 8-token blocks per fill
+  // 8-token blocks per fill (direct: whole groups, never split)
+  const int64_t cap_blocks = direct ? ((int64_t)1 << 40) : cap_bytes / (d * 16);
   if (cap_blocks < 1) return fail(HESS_EINVAL, "grouped scratch smaller than one 8-row block");
   // pieces (group, first row, rows), largest groups first
   struct Piece { int e; int64_t beg, cnt; };
@@ -608,13 +624,13 @@ int grouped_big(hess_t* hs, int n_groups, const void* X, int64_t ld, const int32
   }
   BigParams P;
   std::memset(&P, 0, sizeof(P));
-  P.ld = d;
+  P.ld = direct ? ld : d;
   P.lds = d;
   P.order = h0->order256;
   P.d = (int)d;
   P.nb = h0->nb256;
   P.ntiles = h0->ntiles256;
-  P.t8 = 1;
+  P.t8 = direct ? 0 : 1;
   size_t next = 0;
   while (next < pieces.size()) {
     // one fill: as many pieces as fit (at most kBigMaxGroups)
@@ -626,29 +642,50 @@ int grouped_big(hess_t* hs, int n_groups, const void* X, int64_t ld, const int32
     int k = 0;
     while (next < pieces.size() && k < kBigMaxGroups) {
       const Piece& pc = pieces[next];
-      const int64_t nblk = (pc.cnt + 7) / 8;
+      // 8-token blocks: gathered rows, or (direct) the table's entries in 8s,
+      // a multiple of 32 entries per group
+      const int64_t nblk = direct ? (pc.cnt + kBigKI - 1) / kBigKI * (kBigKI / 8) : (pc.cnt + 7) / 8;
       if (blocks + nblk > cap_blocks) break;
       Gp.beg[k] = pc.beg;
       Gp.cnt[k] = pc.cnt;
       Gp.blk[k] = blocks;
       Gp.blk_prefix[k] = blocks;
-      Gb.blk[k] = blocks;
+      Gb.blk[k] = direct ? blocks * 8 : blocks;
       Gb.n[k] = pc.cnt;
       Gb.S[k] = hs[pc.e]->S;
       blocks += nblk;
       ++k;
       ++next;
     }
-    Gp.blk_prefix[k] = blocks;
-    Gp.X = X;
-    Gp.rows = row_idx;
-    Gp.dst = W.gptr;
-    Gp.ld = ld;
-    Gp.d = (int)d;
-    Gp.fq = (int)((d + 255) / 256);
-    Gp.ngroups = k;
-    err = launch_gather_rows_t8(Gp, s);
-    if (err != hipSuccess) return hip_fail(err, "grouped gather launch");
+    if (direct) {
+      RowTableParams Tp;
+      std::memset(&Tp, 0, sizeof(Tp));
+      Tp.rows = row_idx;
+      Tp.tbl = static_cast<int32_t*>(W.gptr);
+      Tp.nrows = nrows;
+      Tp.row_bytes = ld * 2;
+      Tp.ngroups = k;
+      for (int g = 0; g < k; ++g) {
+        Tp.beg[g] = Gp.beg[g];
+        Tp.cnt[g] = Gp.cnt[g];
+        Tp.tstart[g] = Gp.blk[g] * 8;
+      }
+      Tp.tstart[k] = blocks * 8;
+      Tp.total = blocks * 8 + kRowTableSlack;
+      err = launch_row_table(Tp, s);
+      if (err != hipSuccess) return hip_fail(err, "grouped row table launch");
+    } else {
+      Gp.blk_prefix[k] = blocks;
+      Gp.X = X;
+      Gp.rows = row_idx;
+      Gp.dst = W.gptr;
+      Gp.ld = ld;
+      Gp.d = (int)d;
+      Gp.fq = (int)((d + 255) / 256);
+      Gp.ngroups = k;
+      err = launch_gather_rows_t8(Gp, s);
+      if (err != hipSuccess) return hip_fail(err, "grouped gather launch");
+    }
     // the schedule: items longest first, each to the least-loaded workgroup
     // (cost: 32-token iterations plus a fixed cost for the tile's prologue
     // and output); workgroup w's items are kept in the order dealt
@@ -696,7 +733,9 @@ int grouped_big(hess_t* hs, int n_groups, const void* X, int64_t ld, const int32
     err = hipEventRecord(W.sched_ev, s);
     if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     W.sched_pending = true;
-    Gb.X = W.gptr;
+    Gb.X = direct ? X : W.gptr;
+    Gb.tbl = direct ? static_cast<const int32_t*>(W.gptr) : nullptr;
+    Gb.xbytes = direct ? nrows * ld * 2 : 0;
     Gb.sched = dsched;
     Gb.ngroups = k;
     Gb.nitems = nitems;
@@ -977,6 +1016,11 @@ int hess_add_batch_cast(hess_t h, const void* X, int x_dtype, int64_t n_tokens, 
 
 int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld, const int32_t* row_idx,
                            const int64_t* offsets, hess_stream_t stream) {
+  return hess_add_batch_grouped_ex(hs, n_groups, X, -1, ld, row_idx, offsets, stream);
+}
+
+int hess_add_batch_grouped_ex(hess_t* hs, int n_groups, const void* X, int64_t n_rows, int64_t ld,
+                              const int32_t* row_idx, const int64_t* offsets, hess_stream_t stream) {
   if (!hs || n_groups < 1) return fail(HESS_EINVAL, "need at least one handle");
   GroupLock lock(hs, n_groups);
   if (!offsets) return fail(HESS_EINVAL, "offsets is NULL");
@@ -995,6 +1039,10 @@ int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld, 
     if (offsets[e + 1] < offsets[e]) return fail(HESS_EINVAL, "offsets decrease at %d", e);
   if (ld < h0->d) return fail(HESS_EINVAL, "ld < d");
   const int64_t total = offsets[n_groups];
+  if (n_rows < -1) return fail(HESS_EINVAL, "n_rows = %lld < 0", (long long)n_rows);
+  if (n_rows >= 0 && !row_idx && total > n_rows)
+    return fail(HESS_EINVAL, "without row_idx the groups' %lld rows exceed n_rows = %lld", (long long)total,
+                (long long)n_rows);
   if (total == 0) return HESS_OK;
   if (!X) return fail(HESS_EINVAL, "X is NULL");
   if (reinterpret_cast<uintptr_t>(X) % esize(h0->dtype) != 0) return fail(HESS_EALIGN, "X not element-aligned");
@@ -1006,7 +1054,7 @@ int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld, 
   }
   const bool vec = vec_ok(X, ld, h0->d, esize(h0->dtype));
   if (vec && h0->order256 && h0->d >= kBigMinD && g_tile_override != kTile) {
-    const int rc = grouped_big(hs, n_groups, X, ld, row_idx, offsets, s);
+    const int rc = grouped_big(hs, n_groups, X, n_rows, ld, row_idx, offsets, s);
     if (rc != HESS_OK) return rc;
     for (int e = 0; e < n_groups; ++e) hs[e]->N += offsets[e + 1] - offsets[e];
     return HESS_OK;
@@ -1312,6 +1360,11 @@ int hess_gptq_quantize(const float* W, int64_t rows, int64_t cols, int64_t ldw, 
 int hess_set_group_chunk(int64_t bytes) {
   if (bytes < 0) return fail(HESS_EINVAL, "group chunk must be >= 0");
   g_group_chunk = bytes;
+  return HESS_OK;
+}
+
+int hess_set_group_direct(int enable) {
+  g_group_direct = enable != 0;
   return HESS_OK;
 }
 

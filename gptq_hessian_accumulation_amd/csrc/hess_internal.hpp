@@ -94,6 +94,13 @@ constexpr int kBigMaxGroups = 64;
 struct BigGroupParams {
   const void* X;
   const int32_t* sched;   // workgroup w's items: sched[sched[w] .. sched[w + 1]) (257 offsets first)
+  // Rows read in place (tbl non-null): X is the row-major activations (row
+  // stride P.ld), group g's token t is at byte offset tbl[blk[g] + t]
+  // (blk[g] a multiple of 32; 0x80000000 past the group's rows and for
+  // rows outside X; at least 256 entries after the last group's), and
+  // xbytes (< 2^31) bounds every read
+  const int32_t* tbl;
+  int64_t xbytes;
   int nitems;             // ngroups * ntiles (item = group * ntiles + tile)
   int ngroups;
   int64_t blk[kBigMaxGroups];
@@ -121,6 +128,27 @@ struct GatherParams {
   int64_t blk_prefix[kBigMaxGroups + 1];
 };
 hipError_t launch_gather_rows_t8(const GatherParams& P, hipStream_t stream);
+
+// Row table of a grouped update that reads the routed rows where they are:
+// entry tstart[g] + t (t < cnt[g]) is the byte offset in X of group g's
+// token t, the row rows[beg[g] + t] (or beg[g] + t if rows is null) times
+// row_bytes; kRowAbsent for the padding of each group to a multiple of 32
+// entries, for the entries from tstart[ngroups] up to total, and for a row
+// outside [0, nrows).  nrows * row_bytes < 2^31.
+constexpr int32_t kRowAbsent = (int32_t)0x80000000u;
+constexpr int64_t kRowTableSlack = 256;   // entries after the last group's (read ahead by the SYRK)
+struct RowTableParams {
+  const int32_t* rows;
+  int32_t* tbl;
+  int64_t nrows;
+  int64_t row_bytes;
+  int64_t total;
+  int ngroups;
+  int64_t beg[kBigMaxGroups];
+  int64_t cnt[kBigMaxGroups];
+  int64_t tstart[kBigMaxGroups + 1];
+};
+hipError_t launch_row_table(const RowTableParams& P, hipStream_t stream);
 
 // acc[j] += sum_t X[t][j]^2 (float32), j < d; part holds (max_splits + 32) x d
 // floats: split partial sums, then sums of runs of 32 splits.  vec: X 16-byte aligned, ld * esize % 16 == 0

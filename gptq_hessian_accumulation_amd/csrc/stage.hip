@@ -265,7 +265,38 @@ __global__ void __launch_bounds__(256) gather_rows_t8(GatherParams P) {
   }
 }
 
+// The row table of a grouped update read in place (RowTableParams): one
+// entry per thread, its group found by binary search over tstart.
+__global__ void __launch_bounds__(256) row_table(RowTableParams P) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= P.total) return;
+  int32_t v = kRowAbsent;
+  if (i < P.tstart[P.ngroups]) {
+    int lo = 0, hi = P.ngroups;  // last group g with tstart[g] <= i
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (P.tstart[mid] <= i) lo = mid;
+      else hi = mid;
+    }
+    const int64_t t = i - P.tstart[lo];
+    if (t < P.cnt[lo]) {
+      const int64_t pos = P.beg[lo] + t;
+      const int64_t row = P.rows ? (int64_t)P.rows[pos] : pos;
+      if (row >= 0 && row < P.nrows) v = (int32_t)(row * P.row_bytes);
+    }
+  }
+  P.tbl[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_row_table(const RowTableParams& P, hipStream_t stream) {
+  if (P.total <= 0) return hipSuccess;
+  const int64_t wgs = (P.total + 255) / 256;
+  if (wgs >= ((int64_t)1 << 31) || P.nrows * P.row_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(row_table, dim3((unsigned)wgs), dim3(256), 0, stream, P);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather_rows_t8(const GatherParams& P, hipStream_t stream) {
   const int64_t wgs = P.blk_prefix[P.ngroups] * ((P.fq + kGQ - 1) / kGQ);

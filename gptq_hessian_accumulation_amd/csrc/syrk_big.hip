@@ -146,7 +146,12 @@ __device__ __forceinline__ int64_t excess_start(const BigParams& P, int w) {
   return (int64_t)w * P.excess_total / P.grid_sk;
 }
 
-template <bool T8, bool Grouped>
+// Row offsets through the constant address space: uniform loads of the row
+// table become scalar loads, which the DMA pipeline's vector-memory count
+// does not see.
+typedef __attribute__((address_space(4))) const uint32_t cu32;
+
+template <bool T8, bool Grouped, bool Idx = false>
 __device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParams* G) {
   __shared__ __attribute__((aligned(1024))) char st0[kStageB];
   __shared__ __attribute__((aligned(1024))) char st1[kStageB];
@@ -187,7 +192,10 @@ __device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParam
 
   // one tile's iterations k0..k1-1 of the tokens at X (n of them) into S
   // slot_add: the slot already holds an earlier chunk of this piece; add to it
-  auto segment = [&](int tile, int k0, int k1, int slot, bool slot_add, const void* X, int64_t n, float* S) {
+  // Idx: token t is X's row whose byte offset is tb[t] (a multiple of 32
+  // entries per group, kOOB past the group's rows)
+  auto segment = [&](int tile, int k0, int k1, int slot, bool slot_add, const void* X, int64_t n, float* S,
+                     const int32_t* tb) {
     // accumulator (m, n): tile rows 128 wr + 16 m + (0..15), columns
     // 128 wc + 16 n + (0..15); lane l holds row 16 m + l%16, columns
     // 16 n + 4 (l/16) .. +3 (the column block is the instruction's first
@@ -214,6 +222,11 @@ __device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParam
         const int c = b >> 2;
         const int f = (p ? J : I) * kT + 64 * (b & 3) + lane;
         voff[i] = (f < P.d && !(p && diag)) ? ((uint32_t)c * (uint32_t)P.ld + (uint32_t)f) * 16u : kOOB;
+      } else if constexpr (Idx) {
+        // the feature part only; the token's row offset is added per iteration
+        const int t = 2 * b + (lane >> 5);
+        const int f = (p ? J : I) * kT + 8 * chunk_pos(t, lane & 31);
+        voff[i] = (f < P.d && !(p && diag)) ? (uint32_t)f * 2u : kOOB;
       } else {
         const int t = 2 * b + (lane >> 5);
         const int f = (p ? J : I) * kT + 8 * chunk_pos(t, lane & 31);  // chunk_pos is its own inverse
@@ -223,6 +236,7 @@ __device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParam
     // the iteration's tokens: rows (row-major X) or 8-token blocks of ld
     // chunks (transposed staging, n a multiple of 8)
     auto desc = [&](int j) {
+      if constexpr (Idx) return rsrc_words(reinterpret_cast<uint64_t>(X), G->xbytes);
       const int64_t tok = (int64_t)j * kKI;
       const int64_t valid = j < k1 ? max((int64_t)0, min((int64_t)kKI, n - tok)) : 0;
       if constexpr (T8) {
@@ -234,15 +248,44 @@ __device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParam
         return rsrc_words(base, valid * row_bytes);
       }
     };
-    // load i of this wave's 8 for a stage at LDS address stage_lds
-    auto dma1 = [&](uint32_t stage_lds, const u32x4& r, int i) {
-      lds_dma16(r, voff[i], stage_lds + (uint32_t)(wave * (kDma * 1024) + i * 1024));
+    // load i of this wave's 8 for a stage at LDS address stage_lds, at byte
+    // offsets off (per lane) of the descriptor r
+    auto dma1 = [&](uint32_t stage_lds, const u32x4& r, int i, uint32_t off) {
+      lds_dma16(r, off, stage_lds + (uint32_t)(wave * (kDma * 1024) + i * 1024));
     };
-    auto issue = [&](uint32_t stage_lds, const u32x4& r) {
+    // Idx: the row offsets of this wave's 16 tokens of iteration j (tokens
+    // 16 (wave % 2) .. +15: load i covers tokens 2i and 2i + 1, one per half
+    // wave), by scalar loads
+    auto rows16 = [&](int j, uint32_t (&rw)[16]) {
+      const cu32* q = (const cu32*)(tb + (int64_t)j * kKI + 16 * (wave & 1));
 #pragma unroll
-      for (int i = 0; i < kDma; ++i) dma1(stage_lds, r, i);
+      for (int k = 0; k < 16; ++k) rw[k] = q[k];
     };
-    auto dma = [&](uint32_t stage_lds, int j) { issue(stage_lds, desc(j)); };
+    // ... and the lanes' offsets for iteration j from them (past the segment:
+    // every offset out of range); the saturating add keeps an out-of-range
+    // part out of range
+    auto offs = [&](int j, const uint32_t (&rw)[16], uint32_t (&vo)[kDma]) {
+      const bool live = j < k1;
+#pragma unroll
+      for (int i = 0; i < kDma; ++i) {
+        const uint32_t ra = live ? rw[2 * i] : kOOB, rb = live ? rw[2 * i + 1] : kOOB;
+        vo[i] = __builtin_elementwise_add_sat(lane < 32 ? ra : rb, voff[i]);
+      }
+    };
+    auto issue = [&](uint32_t stage_lds, const u32x4& r, const uint32_t (&vo)[kDma]) {
+#pragma unroll
+      for (int i = 0; i < kDma; ++i) dma1(stage_lds, r, i, vo[i]);
+    };
+    auto dma = [&](uint32_t stage_lds, int j) {
+      if constexpr (Idx) {
+        uint32_t rw[16], vo[kDma];
+        rows16(j, rw);
+        offs(j, rw, vo);
+        issue(stage_lds, desc(j), vo);
+      } else {
+        issue(stage_lds, desc(j), voff);
+      }
+    };
     // operand j of a stage: A block j (j < 8, this wave's rows) or B block
     // j - 8 (its columns)
     const int t8Bd = t8B + (diag ? 0 : kPanelB);
@@ -267,9 +310,19 @@ __device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParam
     // waits at issue until the CU's address unit takes it; spread out this
     // way the wait holds up at most one matrix instruction.  Iterations past
     // the segment multiply the zeros their empty loads wrote.
+    // Idx: rc holds the row offsets of iteration i + kDist (loaded one step
+    // earlier); those of i + kDist + 1 go into rn
     auto step = [&](const char* nxt, uint32_t dtgt, int i, const u32x4 (&xa)[8], const u32x4 (&xb)[8],
-                    u32x4 (&ya)[8], u32x4 (&yb)[8]) {
+                    u32x4 (&ya)[8], u32x4 (&yb)[8], const uint32_t (&rc)[16], uint32_t (&rn)[16]) {
       const u32x4 r = desc(k0 + i + kDist);
+      uint32_t vo[kDma];
+      if constexpr (Idx) {
+        offs(k0 + i + kDist, rc, vo);
+        rows16(k0 + i + kDist + 1, rn);
+      } else {
+#pragma unroll
+        for (int q = 0; q < kDma; ++q) vo[q] = voff[q];
+      }
       __builtin_amdgcn_sched_barrier(0);
       // my loads of iteration i + 1 have landed; those of i + 2 .. i + kDist - 1 stay in flight
       __builtin_amdgcn_s_waitcnt(vm_wait(kDma * (kDist - 2)));
@@ -282,11 +335,11 @@ __device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParam
 #pragma unroll
           for (int u = 0; u < 4; ++u) acc[m][n + u] = mfma16x16x32(xb[n + u], xa[m], acc[m][n + u]);
           rd1(nxt, g, ya, yb);
-          if (g & 1) dma1(dtgt, r, g >> 1);
+          if (g & 1) dma1(dtgt, r, g >> 1, vo[g >> 1]);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        issue(dtgt, r);
+        issue(dtgt, r, vo);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -296,16 +349,38 @@ __device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParam
 #pragma unroll
       for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{};
 
+    // Idx: the row offsets of the first kDist iterations come in one vector
+    // load (lane l: iteration k0 + l / 16, token 16 (wave % 2) + l % 16 of
+    // it), covered by the wait below
+    static_assert(kDist * 16 == 64, "one lane per row offset of the first kDist iterations");
+    uint32_t pro = 0;
+    if constexpr (Idx) {
+      const uint32_t off = (uint32_t)((((k0 + (lane >> 4)) * kKI) + 16 * (wave & 1) + (lane & 15)) * 4);
+      pro = __builtin_amdgcn_raw_buffer_load_b32(
+          make_rsrc(reinterpret_cast<uint64_t>(tb), (int64_t)(k0 + kDist) * kKI * 4), off, 0, 0);
+    }
     // the previous segment's output stores leave the count before these loads
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     const uint32_t Ls[5] = {L0, L1, L2, L3, L4};
     char* const St[5] = {st0, st1, st2, st3, st4};
 #pragma unroll
-    for (int q = 0; q < kDist; ++q) dma(Ls[q], k0 + q);
+    for (int q = 0; q < kDist; ++q) {
+      if constexpr (Idx) {
+        uint32_t rw[16], vo[kDma];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) rw[k] = __builtin_amdgcn_readlane(pro, 16 * q + k);
+        offs(k0 + q, rw, vo);
+        issue(Ls[q], desc(k0 + q), vo);
+      } else {
+        dma(Ls[q], k0 + q);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(vm_wait(kDma * (kDist - 1)));  // iteration k0 has landed
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     u32x4 xa[8], xb[8], ya[8], yb[8];
+    uint32_t ra[16], rb[16];
+    if constexpr (Idx) rows16(k0 + kDist, ra);
     if (active) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) rd1(st0, j, xa, xb);
@@ -315,20 +390,20 @@ __device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParam
     // multiplies zeros)
     const int niter = k1 - k0;
     for (int i = 0;; i += 10) {
-      step(St[1], Ls[kDist % 5], i, xa, xb, ya, yb);
-      step(St[2], Ls[(1 + kDist) % 5], i + 1, ya, yb, xa, xb);
+      step(St[1], Ls[kDist % 5], i, xa, xb, ya, yb, ra, rb);
+      step(St[2], Ls[(1 + kDist) % 5], i + 1, ya, yb, xa, xb, rb, ra);
       if (i + 2 >= niter) break;
-      step(St[3], Ls[(2 + kDist) % 5], i + 2, xa, xb, ya, yb);
-      step(St[4], Ls[(3 + kDist) % 5], i + 3, ya, yb, xa, xb);
+      step(St[3], Ls[(2 + kDist) % 5], i + 2, xa, xb, ya, yb, ra, rb);
+      step(St[4], Ls[(3 + kDist) % 5], i + 3, ya, yb, xa, xb, rb, ra);
       if (i + 4 >= niter) break;
-      step(St[0], Ls[(4 + kDist) % 5], i + 4, xa, xb, ya, yb);
-      step(St[1], Ls[(5 + kDist) % 5], i + 5, ya, yb, xa, xb);
+      step(St[0], Ls[(4 + kDist) % 5], i + 4, xa, xb, ya, yb, ra, rb);
+      step(St[1], Ls[(5 + kDist) % 5], i + 5, ya, yb, xa, xb, rb, ra);
       if (i + 6 >= niter) break;
-      step(St[2], Ls[(6 + kDist) % 5], i + 6, xa, xb, ya, yb);
-      step(St[3], Ls[(7 + kDist) % 5], i + 7, ya, yb, xa, xb);
+      step(St[2], Ls[(6 + kDist) % 5], i + 6, xa, xb, ya, yb, ra, rb);
+      step(St[3], Ls[(7 + kDist) % 5], i + 7, ya, yb, xa, xb, rb, ra);
       if (i + 8 >= niter) break;
-      step(St[4], Ls[(8 + kDist) % 5], i + 8, xa, xb, ya, yb);
-      step(St[0], Ls[(9 + kDist) % 5], i + 9, ya, yb, xa, xb);
+      step(St[4], Ls[(8 + kDist) % 5], i + 8, xa, xb, ya, yb, ra, rb);
+      step(St[0], Ls[(9 + kDist) % 5], i + 9, ya, yb, xa, xb, rb, ra);
       if (i + 10 >= niter) break;
     }
     // drain the trailing loads; every wave is done with the stages
@@ -415,12 +490,16 @@ __device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParam
       const int g = item / P.ntiles, t = item - g * P.ntiles;
       const int64_t ng = G->n[g];
       const int k1 = __builtin_amdgcn_readfirstlane((int)((ng + kKI - 1) / kKI));
-      const char* Xg = static_cast<const char*>(G->X) + G->blk[g] * (int64_t)P.ld * 16;
+      // the group's rows: its 8-token blocks in the gather buffer, or (Idx)
+      // X's rows through its slice of the row table
+      const char* Xg = Idx ? static_cast<const char*>(G->X)
+                           : static_cast<const char*>(G->X) + G->blk[g] * (int64_t)P.ld * 16;
+      const int32_t* tbg = Idx ? G->tbl + G->blk[g] : nullptr;
       // chains of at most kChain iterations, each chunk added into S
       const int nch = (k1 + kChain - 1) / kChain;
       for (int c = 0; c < nch; ++c)
         segment(__builtin_amdgcn_readfirstlane(t), chunk_edge(0, k1, c, nch), chunk_edge(0, k1, c + 1, nch), -1,
-                false, Xg, ng, G->S[g]);
+                false, Xg, ng, G->S[g], tbg);
     }
     return;
   }
@@ -480,7 +559,7 @@ __device__ __forceinline__ void big_body(const BigParams& P, const BigGroupParam
     // chunks, each added into its destination (S, or the slot after the first)
     const int nch = (k1 - k0 + kChain - 1) / kChain;
     for (int c = 0; c < nch; ++c)
-      segment(tile, chunk_edge(k0, k1, c, nch), chunk_edge(k0, k1, c + 1, nch), slot, c > 0, P.X, P.n, P.S);
+      segment(tile, chunk_edge(k0, k1, c, nch), chunk_edge(k0, k1, c + 1, nch), slot, c > 0, P.X, P.n, P.S, nullptr);
   }
 }
 
@@ -491,6 +570,13 @@ __global__ void __launch_bounds__(256, 1) syrk_big_bf16_t8(BigParams P) { big_bo
 // (order, d, nb, ntiles, ld = d, lds = d), the groups from G.
 __global__ void __launch_bounds__(256, 1) syrk_big_t8_grouped(BigParams P, BigGroupParams G) {
   big_body<true, true>(P, &G);
+}
+
+// Grouped launch straight from the routed rows: group g's token t is the row
+// of X at byte offset G.tbl[G.blk[g] + t] (ld = X's row stride), read into
+// LDS as the row-major kernel reads a batch, so no gathered copy is made.
+__global__ void __launch_bounds__(256, 1) syrk_big_rows_grouped(BigParams P, BigGroupParams G) {
+  big_body<false, true, true>(P, &G);
 }
 
 // S_tile += the other parts and the pieces of tile t, in item order (pieces
@@ -571,7 +657,10 @@ hipError_t launch_syrk_big(const BigParams& P, hipStream_t stream) {
 
 hipError_t launch_syrk_big_grouped(const BigParams& P, const BigGroupParams& G, hipStream_t stream) {
   if (G.nitems <= 0) return hipSuccess;
-  hipLaunchKernelGGL(syrk_big_t8_grouped, dim3(256), dim3(256), 0, stream, P, G);
+  if (G.tbl)
+    hipLaunchKernelGGL(syrk_big_rows_grouped, dim3(256), dim3(256), 0, stream, P, G);
+  else
+    hipLaunchKernelGGL(syrk_big_t8_grouped, dim3(256), dim3(256), 0, stream, P, G);
   return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@
  *   Pointers marked (host) are host memory.
  * - Every device operation is enqueued on the given HIP stream
  *   (hipStream_t passed as hess_stream_t; NULL is the null stream).  Apart
- *   from create and destroy calls, hess_timing and hess_add_batch_grouped,
+ *   from create and destroy calls, hess_timing and hess_add_batch_grouped(_ex),
  *   no call synchronizes with the host or allocates device memory, so those
  *   calls (batches, casts, flush, reset, materialize, adopt, imatrix, the
  *   Cholesky factor, the block quantize, and local blocks after the first
@@ -269,6 +269,12 @@ int hess_set_async_flush(int enable);
  * whole buffer.  EINVAL for a negative value. */
 int hess_set_group_chunk(int64_t bytes);
 
+/* Process-wide: 256-tile grouped updates through hess_add_batch_grouped_ex
+ * read each group's rows where they are in X (1, default) or gather them
+ * into the per-device buffer first (0), as hess_add_batch_grouped always
+ * does.  Both give the same bits. */
+int hess_set_group_direct(int enable);
+
 /* S = 0 (its upper triangle, where the sum lives; see hess_state_buffer),
  * N = 0 (enqueued on stream); also re-arms a consumed handle. */
 int hess_reset(hess_t h, hess_stream_t stream);
@@ -416,6 +422,22 @@ int hess_materialize_grouped(hess_t* hs, int n_groups, float damp_percent, unsig
  */
 int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld,
                            const int32_t* row_idx, const int64_t* offsets, hess_stream_t stream);
+
+/*
+ * hess_add_batch_grouped_ex -- hess_add_batch_grouped with X's row count
+ * n_rows (T) given, so that the 256-tile path need not gather: when
+ * n_rows * ld * 2 < 2^31 bytes, the launch reads every group's rows in place
+ * through a table of their offsets in X (1 KiB per 256 routed rows, built by
+ * a small kernel in the per-device buffer, which then holds only the table
+ * and the schedule), with the same operands in the same order as the
+ * gathered path, so the same bits.  Rows outside [0, n_rows) contribute
+ * nothing on that path; every other path requires them in range, as
+ * hess_add_batch_grouped does.  n_rows = -1: unknown (gathered path).
+ * EINVAL also for n_rows < -1, and without row_idx for offsets[n_groups] >
+ * n_rows.  Synchronization and allocation as hess_add_batch_grouped.
+ */
+int hess_add_batch_grouped_ex(hess_t* hs, int n_groups, const void* X, int64_t n_rows, int64_t ld,
+                              const int32_t* row_idx, const int64_t* offsets, hess_stream_t stream);
 
 /*
  * hess_gptq_quantize -- error-propagating 4-bit quantization of a weight

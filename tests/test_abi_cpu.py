@@ -55,6 +55,8 @@ def test_invalid_arguments_rejected_without_gpu():
     assert b"staging_bytes" in lib.hess_last_error()
     offs = (ctypes.c_int64 * 2)(0, 1)
     assert lib.hess_add_batch_grouped(None, 1, None, 16, None, offs, None) == -1
+    assert lib.hess_add_batch_grouped_ex(None, 1, None, 4, 16, None, offs, None) == -1
+    assert lib.hess_set_group_direct(0) == 0 and lib.hess_set_group_direct(1) == 0
     # Cholesky of the inverse: workspace size rule and argument checks (no device work)
     assert lib.hess_chol_inverse_workspace(0) == -1
     assert lib.hess_chol_inverse_workspace(1) == (2 * 64 * 64 + 64 * 64) * 8

@@ -32,9 +32,11 @@ def _say(msg):
 def _defaults():
     hs.set_tile_override(0)
     hs.set_staging(True)
+    hs.set_group_direct(True)
     yield
     hs.set_tile_override(0)
     hs.set_staging(True)
+    hs.set_group_direct(True)
 
 
 def run_lib(wl: W.Workload, damp=0.01, neutralize=True):
@@ -608,8 +610,10 @@ def test_grouped_experts(gather):
         hsx[e].close()
 
 
-def _grouped_check(d, T, E, topk, seed, gather, chunk=0, empty=(), tol=None):
-    """Grouped update of E experts against the oracle's per-expert Gram sums."""
+def _grouped_check(d, T, E, topk, seed, gather, chunk=0, empty=(), tol=None, direct=True):
+    """Grouped update of E experts against the oracle's per-expert Gram sums (direct: the
+    256-tile path reads the routed rows in place; otherwise it gathers them, in fills of at
+    most chunk bytes when chunk > 0)."""
     rng = np.random.default_rng(seed)
     x = W.encode(W.normal_rows(rng, T, d, W.column_scales(rng, d)), W.BF16)
     row_idx, offsets = W.moe_routing(rng, T, experts=E, topk=topk)
@@ -619,6 +623,7 @@ def _grouped_check(d, T, E, topk, seed, gather, chunk=0, empty=(), tol=None):
         offsets[e + 1:] -= n_e
     hsx = [hs.Hessian(d, torch.bfloat16, staging_bytes=0) for _ in range(E)]
     hs.set_group_chunk(chunk)
+    hs.set_group_direct(direct)
     try:
         if gather:
             hs.add_batch_grouped(hsx, to_device(x, W.BF16), offsets, torch.from_numpy(row_idx).cuda())
@@ -629,6 +634,7 @@ def _grouped_check(d, T, E, topk, seed, gather, chunk=0, empty=(), tol=None):
             src, idx = xg, np.arange(xg.shape[0], dtype=np.int32)
     finally:
         hs.set_group_chunk(0)
+        hs.set_group_direct(True)
     ref = O.grouped_grams(src, W.BF16, idx, offsets)
     for e in range(E):
         S_e, N_e = ref[e]
@@ -642,19 +648,95 @@ def _grouped_check(d, T, E, topk, seed, gather, chunk=0, empty=(), tol=None):
         hsx[e].close()
 
 
+@pytest.mark.parametrize("direct", [True, False])
 @pytest.mark.parametrize("gather", [True, False])
-def test_grouped_big_tiles(gather):
+def test_grouped_big_tiles(gather, direct):
     """Width 1,032 (edge tiles) on the 256-tile grouped path: 9 experts, one of them empty,
-    group sizes not multiples of 8 or 32."""
-    _say(f"grouped 256-tile gather={gather}")
-    _grouped_check(1032, 700, 9, 3, seed=52, gather=gather, empty=(4,))
+    group sizes not multiples of 8 or 32; rows read in place or gathered first."""
+    _say(f"grouped 256-tile gather={gather} direct={direct}")
+    _grouped_check(1032, 700, 9, 3, seed=52, gather=gather, empty=(4,), direct=direct)
 
 
 @pytest.mark.parametrize("chunk", [1032 * 16 * 3, 1032 * 16 * 40])
 def test_grouped_big_tiles_refills(chunk):
     """A gather buffer of 3 (or 40) 8-row blocks: groups are split over many fills."""
     _say(f"grouped 256-tile refills chunk={chunk}")
-    _grouped_check(1032, 500, 6, 2, seed=53, gather=True, chunk=chunk)
+    _grouped_check(1032, 500, 6, 2, seed=53, gather=True, chunk=chunk, direct=False)
+
+
+def _grouped_states(d, x, offsets, ridx, direct):
+    """Every expert's raw Gram sum after one grouped update on a given path."""
+    E = len(offsets) - 1
+    hsx = [hs.Hessian(d, torch.bfloat16, staging_bytes=0) for _ in range(E)]
+    hs.set_group_direct(direct)
+    try:
+        hs.add_batch_grouped(hsx, x, offsets, ridx)
+    finally:
+        hs.set_group_direct(True)
+    torch.cuda.synchronize()
+    out = [(h.state_tensor().clone(), h.nsamples) for h in hsx]
+    for h in hsx:
+        h.close()
+    return out
+
+
+@pytest.mark.parametrize("d,T,E,topk", [(1032, 600, 70, 2), (2048, 3000, 16, 4), (2560, 2000, 9, 2)])
+def test_grouped_direct_equals_gathered_bitwise(d, T, E, topk):
+    """The rows read in place through the row table give the gathered path's bits exactly (the
+    same operands in the same order): with row indices and without (rows already grouped),
+    with an empty expert, and with more than 64 experts (two launches)."""
+    _say(f"grouped direct == gathered d={d} T={T} E={E}")
+    rng = np.random.default_rng(70 + d)
+    x = W.encode(W.normal_rows(rng, T, d, W.column_scales(rng, d)), W.BF16)
+    row_idx, offsets = W.moe_routing(rng, T, experts=E, topk=topk)
+    n2 = offsets[3] - offsets[2]                               # expert 2: no tokens
+    row_idx = np.concatenate([row_idx[:offsets[2]], row_idx[offsets[3]:]])
+    offsets[3:] -= n2
+    xt = to_device(x, W.BF16)
+    ridx = torch.from_numpy(row_idx).cuda()
+    a = _grouped_states(d, xt, offsets, ridx, direct=True)
+    b = _grouped_states(d, xt, offsets, ridx, direct=False)
+    for e in range(E):
+        assert a[e][1] == b[e][1] == int(offsets[e + 1] - offsets[e])
+        assert torch.equal(a[e][0], b[e][0]), e
+    # rows already grouped (no row_idx): the table is the identity
+    xg = xt[ridx.long()].contiguous()
+    c = _grouped_states(d, xg, offsets, None, direct=True)
+    for e in range(E):
+        assert torch.equal(c[e][0], b[e][0]), e
+    # and the oracle agrees
+    ref = O.grouped_grams(x, W.BF16, row_idx, offsets)
+    for e in range(E):
+        S_e, N_e = ref[e]
+        if N_e:
+            Sg = np.triu(a[e][0].double().cpu().numpy())
+            assert agreement(Sg * (2.0 / N_e), np.triu(S_e) * (2.0 / N_e)) <= TOL[W.BF16], e
+
+
+def test_grouped_direct_rows_outside_x_read_as_zero():
+    """Given X's row count, the in-place path reads a row index outside [0, n_rows) as a zero
+    row (through the bounds of its buffer descriptor; it still counts toward N_e)."""
+    _say("grouped direct: rows outside X")
+    rng = np.random.default_rng(74)
+    d, T, E = 1032, 400, 3
+    x = W.encode(W.normal_rows(rng, T, d, W.column_scales(rng, d)), W.BF16)
+    rows = [rng.integers(0, T, size=150).astype(np.int32) for _ in range(E)]
+    rows[1][[0, 7, 149]] = [-1, T, 1 << 30]                   # three rows outside X
+    row_idx = np.concatenate(rows)
+    offsets = np.array([0, 150, 300, 450], dtype=np.int64)
+    hsx = [hs.Hessian(d, torch.bfloat16, staging_bytes=0) for _ in range(E)]
+    xt = to_device(x, W.BF16)
+    # the in-place path only: bf16, d % 8 == 0, d >= 1,024, 16-byte aligned rows, X's row count known
+    assert d >= 1024 and d % 8 == 0 and xt.data_ptr() % 16 == 0 and xt.stride(0) * 2 % 16 == 0
+    hs.add_batch_grouped(hsx, xt, offsets, torch.from_numpy(row_idx).cuda())
+    torch.cuda.synchronize()
+    for e in range(E):
+        keep = rows[e][(rows[e] >= 0) & (rows[e] < T)]
+        ref = O.grouped_grams(x, W.BF16, keep, np.array([0, keep.size], dtype=np.int64))[0][0]
+        assert hsx[e].nsamples == 150
+        Sg = np.triu(hsx[e].state_tensor().double().cpu().numpy())
+        assert agreement(Sg, np.triu(ref)) <= TOL[W.BF16], e
+        hsx[e].close()
 
 
 def test_grouped_moe_full_size_sampled():
