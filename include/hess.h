@@ -430,9 +430,10 @@ int hess_add_batch_grouped(hess_t* hs, int n_groups, const void* X, int64_t ld,
  * through a table of their offsets in X (1 KiB per 256 routed rows, built by
  * a small kernel in the per-device buffer, which then holds only the table
  * and the schedule), with the same operands in the same order as the
- * gathered path, so the same bits.  Rows outside [0, n_rows) contribute
- * nothing on that path; every other path requires them in range, as
- * hess_add_batch_grouped does.  n_rows = -1: unknown (gathered path).
+ * gathered path, so the same bits.  On that path a row index outside
+ * [0, n_rows) reads as a zero row (it still counts toward N_e); every other
+ * path requires them in range, as hess_add_batch_grouped does.
+ * n_rows = -1: unknown (gathered path).
  * EINVAL also for n_rows < -1, and without row_idx for offsets[n_groups] >
  * n_rows.  Synchronization and allocation as hess_add_batch_grouped.
  */
