@@ -713,6 +713,30 @@ def test_grouped_direct_equals_gathered_bitwise(d, T, E, topk):
             assert agreement(Sg * (2.0 / N_e), np.triu(S_e) * (2.0 / N_e)) <= TOL[W.BF16], e
 
 
+def test_grouped_direct_long_group_chunks():
+    """An expert with 40,000 routed rows (1,250 iterations: two chains of at most 1,024) beside a
+    small one, read in place: the gathered path's bits, and the oracle's sums."""
+    _say("grouped direct: a 40,000-row expert")
+    rng = np.random.default_rng(75)
+    d, T = 1032, 40000
+    x = W.encode(W.normal_rows(rng, T, d, W.column_scales(rng, d)), W.BF16)
+    big = rng.permutation(T).astype(np.int32)
+    small = rng.integers(0, T, size=3000).astype(np.int32)
+    row_idx = np.concatenate([big, small])
+    offsets = np.array([0, T, T + 3000], dtype=np.int64)
+    xt = to_device(x, W.BF16)
+    ridx = torch.from_numpy(row_idx).cuda()
+    a = _grouped_states(d, xt, offsets, ridx, direct=True)
+    b = _grouped_states(d, xt, offsets, ridx, direct=False)
+    ref = O.grouped_grams(x, W.BF16, row_idx, offsets)
+    for e in range(2):
+        assert torch.equal(a[e][0], b[e][0]), e
+        S_e, N_e = ref[e]
+        assert a[e][1] == N_e
+        Sg = np.triu(a[e][0].double().cpu().numpy())
+        assert agreement(Sg * (2.0 / N_e), np.triu(S_e) * (2.0 / N_e)) <= TOL[W.BF16], e
+
+
 def test_grouped_direct_rows_outside_x_read_as_zero():
     """Given X's row count, the in-place path reads a row index outside [0, n_rows) as a zero
     row (through the bounds of its buffer descriptor; it still counts toward N_e)."""
