@@ -57,6 +57,15 @@
 //    not depend on scheduling).  Workgroups on one XCD take consecutive work
 //    of a blocked tile order, so they share activation panels in that XCD's L2.
 //  * Diagonal tiles load one panel and leave the below-diagonal wave idle.
+//  * Grouped launches (one Hessian per routed expert, Model-Optimizer PR 3002
+//    page, "What does this PR do?") take whole tiles of many Hessians from a
+//    host-built schedule, either on the experts' rows gathered into the
+//    transposed layout or on the routed rows read where they are: the
+//    row-major variant with each load's two row offsets taken from a table
+//    (scalar loads one step ahead, outside the hand-counted load waits) and
+//    the lane's feature offset added with saturation, so that a missing row
+//    stays out of the descriptor's range and reads as zeros.  The operands
+//    and their order are the same either way, so the sums are the same bits.
 //
 // A float32 accumulation chain here is at most kBigChain = 1,024 iterations
 // (32,768 tokens) of one tile, whatever the batch length: each addition
