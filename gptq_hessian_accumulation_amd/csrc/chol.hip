@@ -451,8 +451,15 @@ hipError_t launch_chol_inverse_upper(const float* H, int64_t ldh, int d, float* 
     const int m = nb - k - 1;
     if (m + k > 0) hipLaunchKernelGGL(chol_panel, dim3(4 * m + 2 * k), dim3(256), 0, s, A, X, P, dp, k, nb);
     const int64_t tiles = (int64_t)m * (m + 1) / 2 + (int64_t)m * (k + 1);
+    // A trailing update of at most 5 rounds of one workgroup per CU reserves
+    // 64 KiB of LDS more than it uses, so that no two of its workgroups share
+    // a CU: workgroup 0's diagonal step, the serial chain, then has its CU's
+    // float64 units to itself (measured on MI355X: d=2560 1.40 -> 1.31 ms,
+    // d=4096 2.56 -> 2.51 ms; reserving it for every update made d=4096
+    // slower, 2.72 ms, as its first, largest updates lose residency).
+    const size_t excl = tiles <= 5 * 256 ? (size_t)64 << 10 : 0;
     if (tiles > 0)
-      hipLaunchKernelGGL(chol_update, dim3((unsigned)tiles), dim3(kCB * kTPR), 0, s, A, X, P, dp, k, nb, d, info);
+      hipLaunchKernelGGL(chol_update, dim3((unsigned)tiles), dim3(kCB * kTPR), excl, s, A, X, P, dp, k, nb, d, info);
   }
   hipLaunchKernelGGL(chol_store, dim3(d), dim3(256), 0, s, X, dp, d, U, ldu);
   return hipGetLastError();
