@@ -737,6 +737,38 @@ def test_grouped_direct_long_group_chunks():
         assert agreement(Sg * (2.0 / N_e), np.triu(S_e) * (2.0 / N_e)) <= TOL[W.BF16], e
 
 
+@pytest.mark.parametrize("rows", [(1 << 19) - 1, 1 << 19])
+def test_grouped_rows_near_two_gib(rows):
+    """X of 2,048 bf16 features and 2^19 - 1 rows (just under 2 GiB: read in place, row offsets up
+    to 2^31 - 8 KiB) or 2^19 rows (2 GiB: gathered first), with the routed rows taken from both
+    ends of X: the oracle's sums either way."""
+    _say(f"grouped rows near 2 GiB: {rows} rows")
+    d = 2048
+    g = torch.Generator(device="cuda").manual_seed(76)
+    x = torch.empty((rows, d), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, rows, 1 << 16):
+        r1 = min(rows, r0 + (1 << 16))
+        x[r0:r1] = torch.randn((r1 - r0, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    rng = np.random.default_rng(76)
+    ends = np.concatenate([np.arange(rows - 300, rows), np.arange(0, 200)]).astype(np.int32)
+    rows_e = [rng.permutation(ends)[:350], rng.permutation(ends)[:90]]
+    row_idx = np.concatenate(rows_e).astype(np.int32)
+    offsets = np.array([0, 350, 440], dtype=np.int64)
+    hsx = [hs.Hessian(d, torch.bfloat16, staging_bytes=0) for _ in range(2)]
+    hs.add_batch_grouped(hsx, x, offsets, torch.from_numpy(row_idx).cuda())
+    torch.cuda.synchronize()
+    for e in range(2):
+        xe = W.host_copy(x[torch.from_numpy(rows_e[e].astype(np.int64)).cuda()], W.BF16)
+        ref = O.grouped_grams(xe, W.BF16, np.arange(xe.shape[0], dtype=np.int32),
+                              np.array([0, xe.shape[0]], dtype=np.int64))[0][0]
+        Sg = np.triu(hsx[e].state_tensor().double().cpu().numpy())
+        assert hsx[e].nsamples == len(rows_e[e])
+        assert agreement(Sg, np.triu(ref)) <= TOL[W.BF16], e
+        hsx[e].close()
+    del x
+    torch.cuda.empty_cache()
+
+
 def test_grouped_direct_rows_outside_x_read_as_zero():
     """Given X's row count, the in-place path reads a row index outside [0, n_rows) as a zero
     row (through the bounds of its buffer descriptor; it still counts toward N_e)."""
