@@ -264,6 +264,48 @@ def test_thin_tiles_widest_sampled(dtype):
     torch.cuda.empty_cache()
 
 
+def test_widest_handle_sampled():
+    """The widest handle the API accepts (d = 65,536: a 16 GiB sum, 524,800 tiles of 64) with 1%
+    zeroed columns: 1- and 64-token bf16 batches straight into S (64-tile kernel) and a 600-token
+    one (128-tile kernel), on sampled entries and the whole diagonal; then the materialize: dead
+    mask bitwise, the damping, and sampled H entries, from the oracle's exact sums through the
+    oracle's materialize rule (2/N, neutralized dead columns, p * mean(diag H) on the diagonal)."""
+    _say("widest handle d=65536")
+    hs.set_staging(False)
+    d = 65536
+    wl = W.ragged_case(d, [1, 64, 600], seed=6553, dtype=W.BF16, dead_frac=0.01)
+    h = hs.Hessian(d, torch.bfloat16, staging_bytes=0)
+    for b in wl.batches:
+        h.add_batch(to_device(b, W.BF16))
+    err = _sampled_gram_check(h, wl, n_samples=300, seed=65)
+    assert h.nsamples == 665
+    assert err <= TOL[W.BF16], err
+    H, dead, damp = h.materialize(0.01)
+    torch.cuda.synchronize()
+    diag = np.arange(d)
+    sdiag = O.gram_entries(wl.batches, W.BF16, diag, diag)
+    N = wl.total_tokens
+    dead_r = sdiag == 0.0
+    assert np.array_equal(dead.cpu().numpy(), dead_r)
+    assert np.array_equal(np.flatnonzero(dead_r), wl.dead_cols)
+    hdiag = np.where(dead_r, 1.0, sdiag * (2.0 / N))
+    damp_r = 0.01 * float(np.mean(hdiag))
+    assert abs(float(damp.cpu()[0]) - damp_r) <= 1e-6 * damp_r
+    rng = np.random.default_rng(66)
+    r = rng.integers(0, d, 300)
+    c = rng.integers(0, d, 300)
+    r = np.concatenate([r, wl.dead_cols[:3], diag[:3]])
+    c = np.concatenate([c, rng.integers(0, d, 3), diag[:3]])
+    sv = O.gram_entries(wl.batches, W.BF16, np.minimum(r, c), np.maximum(r, c)) * (2.0 / N)
+    sv = np.where(dead_r[r] | dead_r[c], 0.0, sv)
+    sv = np.where(r == c, np.where(dead_r[r], 1.0, sv) + damp_r, sv)
+    got = H[torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda()].double().cpu().numpy()
+    assert np.max(np.abs(got - sv)) / float(np.mean(hdiag)) <= TOL[W.BF16]
+    del H
+    h.close()
+    torch.cuda.empty_cache()
+
+
 def test_transposed_staging_full_flush_sampled():
     """One full default staging buffer at width 2,560 (209,664 tokens in 2,000-token batches,
     the longest staged flush at this width) against the oracle's exact sums."""
