@@ -551,7 +551,7 @@ def test_nan_propagates():
 # ----------------------------------------------------------- local blocks --
 
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
-@pytest.mark.parametrize("n,d", [(1000, 512), (77, 48), (4096, 272)])
+@pytest.mark.parametrize("n,d", [(1000, 512), (77, 48), (4096, 272), (300, 65536)])
 def test_local_blocks(dtype, n, d):
     _say(f"local blocks n={n} d={d} {dtype}")
     rng = np.random.default_rng(40 + n)
@@ -1040,6 +1040,14 @@ def test_imatrix_parity(d, dtype):
     ragged batches including empty and 1-token ones."""
     _say(f"imatrix d={d} {dtype}")
     _imatrix_check(d, [1, 0, 700, 33, 4000], dtype, seed=600 + d)
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_imatrix_widest(dtype):
+    """Width 65,536 (128 column groups of 512 bf16 or 256 of 256 float32 features), batches of
+    1, 300 and 65 tokens."""
+    _say(f"imatrix d=65536 {dtype}")
+    _imatrix_check(65536, [1, 300, 65], dtype, seed=640)
 
 
 def test_imatrix_strided_rows_and_reset():
